@@ -1,0 +1,300 @@
+"""Benchmark: one Llama-8B-shaped decode step of quantised matvecs on one MI355X.
+
+A step is the whole single-token hot path over one synthetic token:
+32 layers x {fused QKV 6144x4096, O 4096x4096, fused gate+up 28672x4096,
+down 4096x14336} in Q4_K, then the 128000x4096 Q6_K output projection with the
+fused greedy argmax -- 129 library calls, every weight byte streamed once.
+Weights are N(0, 0.02^2) drawn on the GPU and quantised by the library;
+activations N(0, 1).  The 4.36 GB weight set is far larger than the 256 MiB
+last-level cache, so every step reads HBM.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+
+Prints one JSON line.  `value` is achieved HBM GB/s over the step
+(algorithmic bytes: packed weights + x reads + y writes, per step / step time).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0    # MI355X HBM3E peak, 8 TB/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--seed", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+class DecodeStep:
+    """Device-resident weights, activations and outputs of the decode step."""
+
+    def __init__(self, torch, q, synth, seed):
+        self.torch, self.q = torch, q
+        cfg = synth.CONFIG4
+        H, L = cfg["hidden"], cfg["layers"]
+        self.H, self.L = H, L
+        self.qkv_rows = list(cfg["qkv"])
+        self.gu_rows = list(cfg["gate_up"])
+        self.o_shape = cfg["o"]
+        self.down_shape = cfg["down"]
+        self.vocab = cfg["vocab"]
+        dev = "cuda"
+        I = self.down_shape[1]
+        self.I = I
+
+        def make(t, M, K, tensor, layer):
+            blocks = torch.empty(M * q.row_bytes(t, K), dtype=torch.uint8, device=dev)
+            step = max(1, (1 << 28) // K)           # quantise in ~1 GiB f32 slabs
+            rb = q.row_bytes(t, K)
+            for r0 in range(0, M, step):
+                m = min(step, M - r0)
+                w = synth.normal_device(seed, tensor, (m, K), synth.W_STD, dev,
+                                        layer=layer * 100003 + r0)
+                q.qmv_quantize(t, w, m, K, blocks[r0 * rb:(r0 + m) * rb])
+                del w
+            return blocks
+
+        self.layers = []
+        for l in range(L):
+            self.layers.append(dict(
+                qkv=make("q4_k", sum(self.qkv_rows), H, 1, l),
+                o=make("q4_k", self.o_shape[0], self.o_shape[1], 2, l),
+                gu=make("q4_k", sum(self.gu_rows), H, 3, l),
+                down=make("q4_k", self.down_shape[0], I, 4, l),
+            ))
+        self.out = make(cfg["out_type"], self.vocab, H, 5, 0)
+        self.x_h = synth.normal_device(seed, 10, (H,), 1.0, dev)
+        self.x_i = synth.normal_device(seed, 11, (I,), 1.0, dev)
+        self.y_qkv = [torch.empty(m, device=dev) for m in self.qkv_rows]
+        self.y_o = torch.empty(self.o_shape[0], device=dev)
+        self.y_gu = [torch.empty(m, device=dev) for m in self.gu_rows]
+        self.y_down = torch.empty(self.down_shape[0], device=dev)
+        self.idx = torch.empty(1, dtype=torch.int32, device=dev)
+        self.mx = torch.empty(1, device=dev)
+        ws = q.qmv_workspace_bytes(q.OP_ARGMAX, self.vocab, H)
+        self.ws = torch.empty(ws, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+    # launches of one step, as (kind, format, K, algorithmic bytes, callable)
+    def launches(self):
+        q, H, I = self.q, self.H, self.I
+        rbh = q.row_bytes("q4_k", H)
+        out = []
+        for lay in self.layers:
+            M = sum(self.qkv_rows)
+            out.append(("qkv", "q4_k", H, M * rbh + 4 * H + 4 * M,
+                        lambda lay=lay: q.qmv_fused_rows("q4_k", lay["qkv"], H, self.x_h,
+                                                         self.qkv_rows, self.y_qkv)))
+            M = self.o_shape[0]
+            out.append(("o", "q4_k", H, M * rbh + 4 * H + 4 * M,
+                        lambda lay=lay: q.qmv_q4_k(lay["o"], self.o_shape[0], H, self.x_h,
+                                                   self.y_o)))
+            M = sum(self.gu_rows)
+            out.append(("gate_up", "q4_k", H, M * rbh + 4 * H + 4 * M,
+                        lambda lay=lay: q.qmv_fused_rows("q4_k", lay["gu"], H, self.x_h,
+                                                         self.gu_rows, self.y_gu)))
+            M = self.down_shape[0]
+            out.append(("down", "q4_k", I, M * q.row_bytes("q4_k", I) + 4 * I + 4 * M,
+                        lambda lay=lay: q.qmv_q4_k(lay["down"], self.down_shape[0], I, self.x_i,
+                                                   self.y_down)))
+        V = self.vocab
+        out.append(("out_argmax", "q6_k", H, V * q.row_bytes("q6_k", H) + 4 * H + 8,
+                    lambda: q.qmv_argmax("q6_k", self.out, V, H, self.x_h, self.idx, self.mx,
+                                         self.ws)))
+        return out
+
+
+def cpu_baseline(seconds: float):
+    """The oracle (single thread, as written) on one layer of the step, timed
+    repeatedly for about `seconds`; scaled to GB/s and to decode steps/s."""
+    import oracle
+    import synth
+    cfg = synth.CONFIG4
+    H, I = cfg["hidden"], cfg["down"][1]
+    mats = [("q4_k", sum(cfg["qkv"]), H), ("q4_k", cfg["o"][0], H),
+            ("q4_k", sum(cfg["gate_up"]), H), ("q4_k", cfg["down"][0], I)]
+    prepared = []
+    for i, (t, M, K) in enumerate(mats):
+        w = synth.weights(99, M, K, synth.T_W, i)
+        prepared.append((t, oracle.quantize(t, w), M, K, synth.activations(98, K, layer=i)))
+        del w
+    layer_bytes = sum(b.nbytes + 4 * K + 4 * M for t, b, M, K, x in prepared)
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        for t, b, M, K, x in prepared:
+            oracle.qmv(t, b, M, K, x)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    gbs = layer_bytes * passes / el / 1e9
+    return dict(value=round(gbs, 4), unit="GB/s", cores=1, kind="oracle",
+                sample=f"one decode-step layer of the same workload (q4_k QKV 6144x4096, O "
+                       f"4096x4096, gate+up 28672x4096, down 4096x14336; {layer_bytes} B), "
+                       f"{passes} passes in {el:.1f} s",
+                seconds=round(el, 2))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the matvec shards by output rows; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import gguf_dequant_matvec_amd as q
+    import synth
+
+    torch.cuda.set_device(0)
+    step = DecodeStep(torch, q, synth, args.seed)
+    launches = step.launches()
+    step_bytes = sum(b for _, _, _, b, _ in launches)
+    stream = torch.cuda.current_stream()
+
+    def run_step():
+        for *_, fn in launches:
+            fn()
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+
+    # eager step time (one library call per launch from Python), for context
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(max(1, args.steps // 5)):
+        run_step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step_eager = e0.elapsed_time(e1) / max(1, args.steps // 5)
+
+    # headline: the step captured once as a HIP graph, replayed K times
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run_step()
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # per-launch kernel durations: each main kernel carries its own dispatch
+    # start/end timestamps into an event pair (the library's timing hook)
+    pairs = []
+    for _ in launches:
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        z.record(stream)
+        pairs.append((a, z))
+    torch.cuda.synchronize()
+    per = {}
+    for _ in range(args.steps):
+        for (kind, t, K, b, fn), (a, z) in zip(launches, pairs):
+            q.qmv_time_next_launch(a, z)
+            fn()
+        torch.cuda.synchronize()
+        for (kind, t, K, b, fn), (a, z) in zip(launches, pairs):
+            d = per.setdefault(kind, dict(fmt=t, K=K, ms=0.0, n=0, bytes=0))
+            d["ms"] += a.elapsed_time(z)
+            d["n"] += 1
+            d["bytes"] += b
+    kernel_ms_step = sum(d["ms"] for d in per.values()) / args.steps
+
+    breakdown = {}
+    for kind, d in per.items():
+        avg_ms = d["ms"] / d["n"]
+        breakdown[kind] = dict(fmt=d["fmt"], K=d["K"], us_per_launch=round(avg_ms * 1e3, 2),
+                               bytes_per_launch=d["bytes"] // d["n"],
+                               gbs=round(d["bytes"] / d["n"] / (avg_ms * 1e-3) / 1e9, 1))
+    # dominant kernel: the Q4_K row kernel at K = 4096 (QKV, O and gate+up launches)
+    dom = [per[k] for k in ("qkv", "o", "gate_up")]
+    dom_bytes = sum(d["bytes"] for d in dom) / sum(d["n"] for d in dom)
+    dom_ms = sum(d["ms"] for d in dom) / sum(d["n"] for d in dom)
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+
+    # achievable streaming-read ceiling on this device (same 128-bit loads)
+    probe_gbs = None
+    try:
+        nbytes = 4 << 30
+        buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        sink = torch.empty(2048, dtype=torch.int32, device="cuda")
+        for _ in range(2):
+            q.qmv_probe_stream_read(buf, nbytes, sink)
+        torch.cuda.synchronize()
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(5):
+            q.qmv_probe_stream_read(buf, nbytes, sink)
+        z.record(stream)
+        torch.cuda.synchronize()
+        probe_gbs = round(5 * nbytes / (a.elapsed_time(z) * 1e-3) / 1e9, 1)
+        del buf
+    except Exception as exc:  # the probe is context only
+        print(f"probe skipped: {exc}", file=sys.stderr)
+
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    rec = {
+        "metric": "achieved HBM GB/s (% of peak) and weight-stream tok/s per quantized matvec",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "llama-8b-shaped decode step: 32 x (q4_k QKV 6144x4096 fused, O "
+                        "4096x4096, gate+up 28672x4096 fused, down 4096x14336) + q6_k output "
+                        "128000x4096 with fused argmax; 1 token",
+            "bytes_per_step": step_bytes,
+            "launches_per_step": len(launches),
+            "weights": "N(0,0.02) quantised on device; x N(0,1)",
+        },
+        "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "tok_per_s": round(1000.0 / ms_step, 1),
+        "ms_per_step_eager": round(ms_step_eager, 4),
+        "kernel_ms_per_step": round(kernel_ms_step, 4),
+        "kernel_only_gbs": round(step_bytes / (kernel_ms_step * 1e-3) / 1e9, 1),
+        "probe_read_gbs": probe_gbs,
+        "breakdown": breakdown,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "rows_kernel<Q4K,64,2,store> (q4_k, K=4096: QKV, O, gate+up)",
+        },
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

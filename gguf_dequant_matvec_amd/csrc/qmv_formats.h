@@ -1,0 +1,297 @@
+// Per-format "unit" decoders for the gfx950 matvec kernels.
+//
+// A unit is the slice of one row that one lane handles per step: 64 weights
+// (32 for Q8_0 rows with an odd number of blocks).  Lanes keep the same unit
+// position modulo 4 for a whole launch, so the sub-block they touch inside a
+// 256-weight super-block is lane-constant.  Each decoder
+//   - loads its unit's bytes straight from HBM with 128-bit loads (load),
+//   - reads the unit's 64 activations from LDS (load_x),
+//   - multiplies and adds into a per-lane f32 accumulator (dot), using the
+//     factored form  d*sc_j*sum(q*x) - dmin*m_j*sum(x)  so that the scales are
+//     applied once per 16 or 32 weights, never per weight.
+//
+// Block layouts (bytes, little-endian), standard GGUF bit order:
+//   Q8_0 34 B / 32 w:  fp16 d | int8 q[32]
+//   Q4_K 144 B / 256 w: fp16 d | fp16 dmin | S[12] (6-bit sc/m of 8 sub-blocks)
+//                      | Q[128]: byte 32c+l holds weight 64c+l (low nibble)
+//                        and weight 64c+32+l (high nibble)
+//   Q6_K 210 B / 256 w: QL[128] | QH[64] | int8 sc[16] | fp16 d; weight
+//                      128n+32g+l takes its low 4 bits from QL[64n+l+32(g&1)]
+//                      (nibble g>>1) and its high 2 bits from bits 2g..2g+1 of
+//                      QH[32n+l]; q - 32 is the signed code, sub-block = i/16.
+// BebeLM page ("BebeLM：纯Rust实现的端侧大模型推理引擎"), section "量化格式支持"
+// (Q4_K: 256 weights in 144 bytes; Q6_K for sensitive tensors; f32
+// activations); Wick page, section "量化支持" (Q8_0).
+#pragma once
+
+#include "qmv_device.h"
+
+namespace qmv {
+
+// ---------------------------------------------------------------------------
+// Q4_K: unit u of a row = block u/4, 64-weight chunk c = u%4, i.e. nibble
+// bytes Q[32c .. 32c+32): low nibbles are sub-block 2c, high nibbles 2c+1.
+// Activation sums per 32-weight sub-block come from LDS (`sums`).
+// ---------------------------------------------------------------------------
+struct Q4K {
+    static constexpr int kBlockWeights = 256;
+    static constexpr int kBlockBytes = 144;
+    static constexpr int kUnitWeights = 64;
+    static constexpr int kSumGroup = 32;  // activation sums per sub-block of 32
+    static constexpr int kPadEvery = 64;  // LDS copy of x: 4 pad floats per 64
+    struct Regs {
+        uint4 hdr, q0, q1;
+    };
+    __device__ static __forceinline__ Regs load(const uint8_t *row, int u) {
+        const uint8_t *blk = row + (size_t)(u >> 2) * kBlockBytes;
+        const int c = u & 3;
+        Regs r;
+        r.hdr = load16(blk);
+        r.q0 = load16(blk + 16 + 32 * c);
+        r.q1 = load16(blk + 32 + 32 * c);
+        return r;
+    }
+    // The unit's 64 activations: x[64u .. 64u+64), stored at 68u in the padded
+    // LDS copy, so lane u's i-th 16-byte read falls in bank group (u + i) mod 16
+    // and consecutive lanes never collide.
+    __device__ static __forceinline__ void load_x(const float *xs, int u, float *xv) {
+        const float4 *p = reinterpret_cast<const float4 *>(xs + 68 * u);
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            float4 v = p[i];
+            xv[4 * i] = v.x;
+            xv[4 * i + 1] = v.y;
+            xv[4 * i + 2] = v.z;
+            xv[4 * i + 3] = v.w;
+        }
+    }
+    // acc += sum over the unit's 64 weights of w * x.
+    __device__ static __forceinline__ void dot(const Regs &r, const float *xv, const float *sums,
+                                               int u, float inv_unit, float &acc) {
+        const uint32_t qw[8] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w};
+        float lo0 = 0.f, lo1 = 0.f, hi0 = 0.f, hi1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            float a0, a1, a2, a3, b0, b1, b2, b3;
+            nib4_to_f32_x512(qw[i] & 0x0F0F0F0Fu, a0, a1, a2, a3);
+            nib4_to_f32_x512((qw[i] >> 4) & 0x0F0F0F0Fu, b0, b1, b2, b3);
+            lo0 = fmaf(a0, xv[4 * i + 0], lo0);
+            lo1 = fmaf(a1, xv[4 * i + 1], lo1);
+            lo0 = fmaf(a2, xv[4 * i + 2], lo0);
+            lo1 = fmaf(a3, xv[4 * i + 3], lo1);
+            hi0 = fmaf(b0, xv[32 + 4 * i + 0], hi0);
+            hi1 = fmaf(b1, xv[32 + 4 * i + 1], hi1);
+            hi0 = fmaf(b2, xv[32 + 4 * i + 2], hi0);
+            hi1 = fmaf(b3, xv[32 + 4 * i + 3], hi1);
+        }
+        const float alo = lo0 + lo1, ahi = hi0 + hi1;
+        // 6-bit scale and min of sub-blocks 2c and 2c+1, as two bytes each
+        // (both decodings are formed and one is selected: no branch).
+        const int c = u & 3;
+        const int sh = (c & 1) * 16;
+        const uint32_t s0 = r.hdr.y >> sh, s1 = r.hdr.z >> sh, s2 = r.hdr.w >> sh;
+        const uint32_t sc_lo = s0 & 0x3F3Fu, m_lo = s1 & 0x3F3Fu;
+        const uint32_t sc_hi = (s2 & 0x0F0Fu) | ((s0 >> 2) & 0x3030u);
+        const uint32_t m_hi = ((s2 >> 4) & 0x0F0Fu) | ((s1 >> 2) & 0x3030u);
+        const uint32_t sc = c < 2 ? sc_lo : sc_hi;
+        const uint32_t m = c < 2 ? m_lo : m_hi;
+        const float d = half_bits_to_float(r.hdr.x) * inv_unit;
+        const float dmin = half_bits_to_float(r.hdr.x >> 16);
+        const float t = fmaf(ubyte<1>(sc), ahi, ubyte<0>(sc) * alo);
+        const float mm = fmaf(ubyte<1>(m), sums[2 * u + 1], ubyte<0>(m) * sums[2 * u]);
+        acc = fmaf(d, t, acc);
+        acc = fmaf(-dmin, mm, acc);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Q6_K: unit u of a row = block u/4, half n = (u>>1)&1, h = u&1: weights
+// 128n + 32g + 16h + t for g, t in 0..3 x 0..15 (sub-blocks 8n+2g+h).
+// Activation sums per 16-weight sub-block come from LDS; the -32 offset of
+// the codes is applied through them.
+// ---------------------------------------------------------------------------
+struct Q6K {
+    static constexpr int kBlockWeights = 256;
+    static constexpr int kBlockBytes = 210;
+    static constexpr int kUnitWeights = 64;
+    static constexpr int kSumGroup = 16;
+    static constexpr int kPadEvery = 128;  // LDS copy of x: 4 pad floats per 128
+    struct Regs {
+        uint4 qa, qb, qh;
+        uint2 sc;
+        uint32_t d;
+    };
+    __device__ static __forceinline__ Regs load(const uint8_t *row, int u) {
+        const uint8_t *blk = row + (size_t)(u >> 2) * kBlockBytes;
+        const int n = (u >> 1) & 1, h = u & 1;
+        Regs r;
+        r.qa = load16(blk + 64 * n + 16 * h);
+        r.qb = load16(blk + 64 * n + 32 + 16 * h);
+        r.qh = load16(blk + 128 + 32 * n + 16 * h);
+        r.sc = load8(blk + 192 + 8 * n);
+        r.d = load2(blk + 208);
+        return r;
+    }
+    // Runs x[256b + 128n + 32g + 16h .. +16) for g = 0..3; in the padded LDS
+    // copy (4 pad floats per 128) the 8 units of two blocks start in 8
+    // distinct bank groups.
+    __device__ static __forceinline__ void load_x(const float *xs, int u, float *xv) {
+        const int b = u >> 2, n = (u >> 1) & 1, h = u & 1;
+        const float *base = xs + 264 * b + 132 * n + 16 * h;
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+            const float4 *p = reinterpret_cast<const float4 *>(base + 32 * g);
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                float4 v = p[i];
+                xv[16 * g + 4 * i] = v.x;
+                xv[16 * g + 4 * i + 1] = v.y;
+                xv[16 * g + 4 * i + 2] = v.z;
+                xv[16 * g + 4 * i + 3] = v.w;
+            }
+        }
+    }
+    __device__ static __forceinline__ void dot(const Regs &r, const float *xv, const float *sums,
+                                               int u, float /*inv_unit*/, float &acc) {
+        const uint32_t qa[4] = {r.qa.x, r.qa.y, r.qa.z, r.qa.w};
+        const uint32_t qb[4] = {r.qb.x, r.qb.y, r.qb.z, r.qb.w};
+        const uint32_t qh[4] = {r.qh.x, r.qh.y, r.qh.z, r.qh.w};
+        float A[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const uint32_t a = qa[i], b = qb[i], hh = qh[i];
+            const uint32_t q[4] = {
+                (a & 0x0F0F0F0Fu) | ((hh & 0x03030303u) << 4),
+                (b & 0x0F0F0F0Fu) | ((hh & 0x0C0C0C0Cu) << 2),
+                ((a >> 4) & 0x0F0F0F0Fu) | (hh & 0x30303030u),
+                ((b >> 4) & 0x0F0F0F0Fu) | ((hh >> 2) & 0x30303030u),
+            };
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+                A[g] = fmaf(ubyte<0>(q[g]), xv[16 * g + 4 * i + 0], A[g]);
+                A[g] = fmaf(ubyte<1>(q[g]), xv[16 * g + 4 * i + 1], A[g]);
+                A[g] = fmaf(ubyte<2>(q[g]), xv[16 * g + 4 * i + 2], A[g]);
+                A[g] = fmaf(ubyte<3>(q[g]), xv[16 * g + 4 * i + 3], A[g]);
+            }
+        }
+        // sub-block of group g is 8n + 2g + h: its scale is byte 2g + h of the
+        // 8 scale bytes loaded from 192 + 8n; its activation sum is entry
+        // 16*b + 8n + 2g + h of `sums`.
+        const int h = u & 1;
+        const int sbase = 16 * (u >> 2) + 8 * ((u >> 1) & 1) + h;
+        const uint32_t w0 = r.sc.x >> (8 * h), w1 = r.sc.y >> (8 * h);
+        float t = 0.f;
+        t = fmaf(sbyte<0>(w0), fmaf(-32.f, sums[sbase + 0], A[0]), t);
+        t = fmaf(sbyte<2>(w0), fmaf(-32.f, sums[sbase + 2], A[1]), t);
+        t = fmaf(sbyte<0>(w1), fmaf(-32.f, sums[sbase + 4], A[2]), t);
+        t = fmaf(sbyte<2>(w1), fmaf(-32.f, sums[sbase + 6], A[3]), t);
+        acc = fmaf(half_bits_to_float(r.d), t, acc);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Q8_0, two blocks per unit (rows with an even number of blocks): unit u =
+// blocks 2u and 2u+1 = 68 bytes starting 68u into the row (4-byte aligned).
+// ---------------------------------------------------------------------------
+struct Q80x2 {
+    static constexpr int kBlockWeights = 32;
+    static constexpr int kBlockBytes = 34;
+    static constexpr int kUnitWeights = 64;
+    static constexpr int kSumGroup = 0;
+    static constexpr int kPadEvery = 64;
+    struct Regs {
+        uint4 a, b, c, d;
+        uint32_t e;
+    };
+    __device__ static __forceinline__ Regs load(const uint8_t *row, int u) {
+        const uint8_t *p = row + (size_t)u * 68;
+        Regs r;
+        r.a = load16(p);
+        r.b = load16(p + 16);
+        r.c = load16(p + 32);
+        r.d = load16(p + 48);
+        r.e = load4(p + 64);
+        return r;
+    }
+    __device__ static __forceinline__ void load_x(const float *xs, int u, float *xv) {
+        Q4K::load_x(xs, u, xv);
+    }
+    __device__ static __forceinline__ void dot(const Regs &r, const float *xv, const float *,
+                                               int, float, float &acc) {
+        const uint32_t D[17] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w,
+                                r.c.x, r.c.y, r.c.z, r.c.w, r.d.x, r.d.y, r.d.z, r.d.w, r.e};
+        // block 0: d in D0 bytes 0-1, q[0..1] in D0 bytes 2-3, q[2..29] in
+        // D1..D7, q[30..31] in D8 bytes 0-1.  Block 1: d in D8 bytes 2-3,
+        // q[0..31] in D9..D16.
+        float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
+        a0 = fmaf(sbyte<2>(D[0]), xv[0], a0);
+        a1 = fmaf(sbyte<3>(D[0]), xv[1], a1);
+#pragma unroll
+        for (int i = 1; i < 8; i++) {
+            a0 = fmaf(sbyte<0>(D[i]), xv[4 * i - 2], a0);
+            a1 = fmaf(sbyte<1>(D[i]), xv[4 * i - 1], a1);
+            a0 = fmaf(sbyte<2>(D[i]), xv[4 * i + 0], a0);
+            a1 = fmaf(sbyte<3>(D[i]), xv[4 * i + 1], a1);
+        }
+        a0 = fmaf(sbyte<0>(D[8]), xv[30], a0);
+        a1 = fmaf(sbyte<1>(D[8]), xv[31], a1);
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            b0 = fmaf(sbyte<0>(D[9 + i]), xv[32 + 4 * i + 0], b0);
+            b1 = fmaf(sbyte<1>(D[9 + i]), xv[32 + 4 * i + 1], b1);
+            b0 = fmaf(sbyte<2>(D[9 + i]), xv[32 + 4 * i + 2], b0);
+            b1 = fmaf(sbyte<3>(D[9 + i]), xv[32 + 4 * i + 3], b1);
+        }
+        acc = fmaf(half_bits_to_float(D[0]), a0 + a1, acc);
+        acc = fmaf(half_bits_to_float(D[8] >> 16), b0 + b1, acc);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Q8_0, one block per unit (any row length): 34 bytes at 34u, 2-byte aligned.
+// ---------------------------------------------------------------------------
+struct Q80x1 {
+    static constexpr int kBlockWeights = 32;
+    static constexpr int kBlockBytes = 34;
+    static constexpr int kUnitWeights = 32;
+    static constexpr int kSumGroup = 0;
+    static constexpr int kPadEvery = 32;
+    struct Regs {
+        uint4 a, b;
+        uint32_t c;
+    };
+    __device__ static __forceinline__ Regs load(const uint8_t *row, int u) {
+        const uint8_t *p = row + (size_t)u * 34;
+        Regs r;
+        r.c = load2(p);
+        r.a = load16(p + 2);
+        r.b = load16(p + 18);
+        return r;
+    }
+    __device__ static __forceinline__ void load_x(const float *xs, int u, float *xv) {
+        const float4 *p = reinterpret_cast<const float4 *>(xs + 36 * u);
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            float4 v = p[i];
+            xv[4 * i] = v.x;
+            xv[4 * i + 1] = v.y;
+            xv[4 * i + 2] = v.z;
+            xv[4 * i + 3] = v.w;
+        }
+    }
+    __device__ static __forceinline__ void dot(const Regs &r, const float *xv, const float *,
+                                               int, float, float &acc) {
+        const uint32_t D[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
+        float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            a0 = fmaf(sbyte<0>(D[i]), xv[4 * i + 0], a0);
+            a1 = fmaf(sbyte<1>(D[i]), xv[4 * i + 1], a1);
+            a0 = fmaf(sbyte<2>(D[i]), xv[4 * i + 2], a0);
+            a1 = fmaf(sbyte<3>(D[i]), xv[4 * i + 3], a1);
+        }
+        acc = fmaf(half_bits_to_float(r.c), a0 + a1, acc);
+    }
+};
+
+}  // namespace qmv

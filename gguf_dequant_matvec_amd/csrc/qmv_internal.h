@@ -1,0 +1,73 @@
+// Host-side declarations shared by the C ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qmv {
+
+struct SegTable;
+
+enum { kQ80 = 8, kQ4K = 12, kQ6K = 14 };
+
+constexpr int kMaxGrid = 2048;  // largest persistent grid (argmax partial slots)
+
+inline int block_weights_of(int type) {
+    return type == kQ80 ? 32 : (type == kQ4K || type == kQ6K) ? 256 : 0;
+}
+inline int block_bytes_of(int type) {
+    return type == kQ80 ? 34 : type == kQ4K ? 144 : type == kQ6K ? 210 : 0;
+}
+inline size_t row_bytes_of(int type, int64_t K) {
+    const int bw = block_weights_of(type);
+    return bw ? (size_t)(K / bw) * (size_t)block_bytes_of(type) : 0;
+}
+
+// One-shot kernel timing hook of the calling thread (see qmv_time_next_launch).
+struct TimingHook {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+void set_timing_hook(hipEvent_t start, hipEvent_t stop);
+TimingHook take_timing_hook();
+
+// Launch `kernel`, through hipExtLaunchKernelGGL with the thread's timing
+// events when the hook is armed (the hook is consumed).
+template <typename Kernel, typename... Args>
+hipError_t launch_main(Kernel kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                       Args... args) {
+    TimingHook h = take_timing_hook();
+    if (h.start && h.stop)
+        hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, h.start, h.stop, 0, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+    return hipGetLastError();
+}
+
+// Compute units of the current device (cached per device).
+int device_cu_count();
+// Workgroups of `kernel` that can be resident on one compute unit at once
+// (occupancy query, cached per kernel and LDS size; at least 1).
+int resident_blocks(const void *kernel, int threads, size_t lds);
+// Raise a kernel's dynamic-LDS limit when it needs more than the default.
+hipError_t ensure_lds(const void *kernel, size_t bytes);
+
+hipError_t launch_rows_store(int type, const uint8_t *W, int64_t M, int64_t K, const float *x,
+                             const SegTable &seg, hipStream_t s);
+hipError_t launch_rows_argmax(int type, const uint8_t *W, int64_t M, int64_t K, const float *x,
+                              uint64_t *partials, int32_t *idx_out, float *max_out,
+                              hipStream_t s);
+hipError_t launch_dequant(int type, const uint8_t *W, int64_t M, int64_t K, float *out,
+                          hipStream_t s);
+hipError_t launch_quantize(int type, const float *w, int64_t M, int64_t K, uint8_t *out,
+                           hipStream_t s);
+hipError_t launch_probe(const void *buf, size_t bytes, uint32_t *sink, hipStream_t s);
+hipError_t launch_moe(const float *x, int64_t H, const float *router, const float *bias,
+                      int32_t E, int32_t k, int gu_t, const uint8_t *gate_up, int dn_t,
+                      const uint8_t *down, int64_t I, float *y, int32_t *topk_idx,
+                      float *topk_w, uint8_t *ws, hipStream_t s);
+hipError_t launch_gemm_n(int type, const uint8_t *W, int64_t M, int64_t K, int32_t n,
+                         const float *X, float *Y, hipStream_t s);
+
+}  // namespace qmv

@@ -1,0 +1,266 @@
+// The row-streaming matvec kernel shared by the single-token, fused-row and
+// argmax entry points.
+//
+// Work split: a wave owns tiles of rows; inside a tile, groups of G lanes
+// cooperate on one row (64/G rows side by side) and each lane also carries R
+// independent row slots, so one step issues R x (64/G) rows of 128-bit loads.
+// The activation vector x is staged once per workgroup in LDS together with
+// its per-sub-block sums; every lane keeps the same unit position modulo G,
+// so its 64 activations are read from LDS once per step and reused by all R
+// rows.  The grid is persistent (a few workgroups per compute unit) so that
+// the LDS staging is paid once per workgroup, not once per row.
+//
+// The per-row result is a fixed butterfly over the G lanes of fixed partial
+// sums, so it depends only on (format, K, G, R) -- never on M, the grid or
+// which rows share a tile.  That makes fused-row outputs and argmax values
+// bit-identical to the plain matvec of the same rows.
+#pragma once
+
+#include <stdint.h>
+
+#include "qmv_formats.h"
+
+namespace qmv {
+
+constexpr int kMaxSegments = 8;
+
+// Row counts are below 2^31 (checked on the host), so every row and tile
+// index is 32-bit and wave-uniform bookkeeping stays in scalar registers.
+struct SegTable {
+    int32_t n;
+    int32_t start[kMaxSegments + 1];  // prefix sums of the segment row counts
+    float *y[kMaxSegments];
+};
+
+struct RowsParams {
+    const uint8_t *W;
+    int32_t M;
+    int32_t K;
+    int64_t row_bytes;
+    const float *x;
+    SegTable seg;
+    uint64_t *partials;  // argmax mode: one packed (value, index) key per workgroup
+};
+
+enum { kModeStore = 0, kModeArgmax = 1 };
+
+// Packed argmax key: larger value first, then lower index.
+__device__ __forceinline__ uint64_t argmax_key(float v, int32_t idx) {
+    v = v + 0.0f;  // -0 -> +0 so equal values compare equal
+    return ((uint64_t)float_key(v) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)idx);
+}
+
+// Stage x[0..K) in LDS, plus the sums of its consecutive groups of
+// F::kSumGroup values.  x is stored padded (4 floats after every
+// F::kPadEvery) so that the lanes' 16-byte reads spread over the LDS banks.
+// Loads are issued eight at a time; each group's sum is formed by the
+// kSumGroup/4 consecutive lanes that loaded it (a shuffle butterfly), so the
+// sums need no extra pass over LDS.  K is a multiple of 32,
+// so a lane group is either wholly inside [0, K) or wholly outside.
+template <class F>
+__device__ __forceinline__ void stage_x(const float *__restrict__ x, int K, float *xs,
+                                        float *sums) {
+    constexpr int kLanes = F::kSumGroup > 0 ? F::kSumGroup / 4 : 1;
+    const int nt = blockDim.x;
+    for (int base = threadIdx.x * 4; base < K; base += nt * 4 * 8) {
+        float4 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const int i = base + j * nt * 4;
+            v[j] = i < K ? *reinterpret_cast<const float4 *>(x + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const int i = base + j * nt * 4;
+            if (i < K) *reinterpret_cast<float4 *>(xs + i + (i / F::kPadEvery) * 4) = v[j];
+            if (F::kSumGroup > 0) {
+                float sum = (v[j].x + v[j].y) + (v[j].z + v[j].w);
+#pragma unroll
+                for (int o = 1; o < kLanes; o <<= 1) sum += __shfl_xor(sum, o, kWave);
+                if (i < K && (threadIdx.x % kLanes) == 0) sums[i / (F::kSumGroup > 0 ? F::kSumGroup : 1)] = sum;
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// Floats of the padded LDS copy of x.
+template <class F>
+__host__ __device__ constexpr int lds_x_floats(int K) {
+    return K + (K / F::kPadEvery) * 4;
+}
+
+__device__ __forceinline__ float fp8_unit_inverse() {
+    // value of fp8 code 0x01 is the smallest subnormal step (2^-9 for OCP
+    // e4m3); nibble products are scaled back by its exact inverse.
+    f32x2 v = __builtin_amdgcn_cvt_pk_f32_fp8(1u, false);
+    return 1.0f / v.x;
+}
+
+template <class F, int G, int R, int MODE>
+__global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
+    extern __shared__ float smem[];
+    float *xs = smem;
+    float *sums = smem + lds_x_floats<F>(p.K);
+    stage_x<F>(p.x, p.K, xs, sums);
+
+    const float inv_unit = fp8_unit_inverse();
+    const int lane = threadIdx.x & (kWave - 1);
+    // wave-uniform values are forced into scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int waves_per_block = blockDim.x / kWave;
+    constexpr int P = kWave / G;  // rows side by side in one wave
+    const int sub = lane / G, g = lane % G;
+    const int U = p.K / F::kUnitWeights;
+    const int iters = (U + G - 1) / G;  // unit steps per row
+    constexpr int kRowsPerTile = R * P;
+    const int ntiles = (p.M + kRowsPerTile - 1) / kRowsPerTile;
+    const int tile_stride = (int)gridDim.x * waves_per_block;
+
+    // row of slot r inside a tile, relative to the tile's first row
+    int rel[R];
+#pragma unroll
+    for (int r = 0; r < R; r++) rel[r] = r * P + sub;
+
+    float best_v = -__builtin_inff();
+    int best_i = 0x7FFFFFFF;
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; r++) acc[r] = 0.f;
+
+    // One work item = (tile, unit step).  Items are software-pipelined: the
+    // next item's weight loads are in flight while the current one is
+    // multiplied, with two register sets used in turn (no copies, so no wait).
+    // Tile bookkeeping is wave-uniform (scalar); a lane only adds its own row
+    // offset, clamped to the last row so the ragged tail stays in bounds.
+    auto issue = [&](typename F::Regs(&dst)[R], int t, int it) {
+        t = __builtin_amdgcn_readfirstlane(t);
+        it = __builtin_amdgcn_readfirstlane(it);
+        int u = g + G * it;
+        u = u < U ? u : U - 1;
+        const int r0 = t * kRowsPerTile;
+        const int last = (p.M - 1 - r0) < kRowsPerTile ? (p.M - 1 - r0) : kRowsPerTile;
+        const uint8_t *tile_base = p.W + (int64_t)r0 * p.row_bytes;
+#pragma unroll
+        for (int r = 0; r < R; r++) {
+            const int rr = rel[r] < last ? rel[r] : last;
+            dst[r] = F::load(tile_base + (int64_t)rr * p.row_bytes, u);
+        }
+    };
+    auto finish_tile = [&](int t) {
+        t = __builtin_amdgcn_readfirstlane(t);
+        float tot[R];
+#pragma unroll
+        for (int r = 0; r < R; r++) {
+            tot[r] = group_sum<G>(acc[r]);
+            acc[r] = 0.f;
+        }
+        const int r0 = t * kRowsPerTile;
+        if (MODE == kModeStore) {
+            // segment of the tile's first row and the start of the next one:
+            // compile-time indices over the table, all in scalar registers
+            float *yb = p.seg.y[0];
+            int sb = 0, next = INT32_MAX;
+#pragma unroll
+            for (int k = 1; k < kMaxSegments; k++) {
+                if (k < p.seg.n) {
+                    if (r0 >= p.seg.start[k]) {
+                        sb = p.seg.start[k];
+                        yb = p.seg.y[k];
+                    } else if (next == INT32_MAX) {
+                        next = p.seg.start[k];
+                    }
+                }
+            }
+            if (g == 0) {
+#pragma unroll
+                for (int r = 0; r < R; r++) {
+                    const int row = r0 + rel[r];
+                    if (row >= p.M) continue;
+                    if (row < next) {
+                        yb[row - sb] = tot[r];
+                    } else {  // the tile straddles a segment boundary
+                        int s = 0;
+                        while (s + 1 < p.seg.n && row >= p.seg.start[s + 1]) s++;
+                        p.seg.y[s][row - p.seg.start[s]] = tot[r];
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < R; r++) {
+                const int row = r0 + rel[r];
+                const float v = tot[r] + 0.0f;
+                if (row < p.M && (v > best_v || (v == best_v && row < best_i))) {
+                    best_v = v;
+                    best_i = row;
+                }
+            }
+        }
+    };
+    auto consume = [&](typename F::Regs(&src)[R], int t, int it) {
+        t = __builtin_amdgcn_readfirstlane(t);
+        it = __builtin_amdgcn_readfirstlane(it);
+        const int u = g + G * it;
+        if (u < U) {
+            float xv[F::kUnitWeights];
+            F::load_x(xs, u, xv);
+#pragma unroll
+            for (int r = 0; r < R; r++) F::dot(src[r], xv, sums, u, inv_unit, acc[r]);
+        }
+        if (it == iters - 1) finish_tile(t);
+    };
+
+    // Items of this wave: tiles t_first, t_first + stride, ..., each with
+    // `iters` unit steps.  Both issues of an iteration are unconditional (past
+    // the end they repeat the last item's addresses, which hit in L2), so the
+    // compiler's wait counters never have to merge "maybe issued" states and
+    // each consume waits only for its own loads.
+    const int t_first = __builtin_amdgcn_readfirstlane((int)blockIdx.x * waves_per_block + wave);
+    const int my_tiles = t_first < ntiles ? (ntiles - 1 - t_first) / tile_stride + 1 : 0;
+    const int n_items = my_tiles * iters;
+    if (n_items > 0) {
+        typename F::Regs bufA[R], bufB[R];
+        int tA = t_first;
+        int itA = 0;
+        issue(bufA, tA, itA);
+        for (int k = 0; k < n_items; k += 2) {
+            int tB = tA;
+            int itB = itA;
+            if (k + 1 < n_items && ++itB == iters) {
+                itB = 0;
+                tB += tile_stride;
+            }
+            issue(bufB, tB, itB);
+            consume(bufA, tA, itA);
+            int tC = tB;
+            int itC = itB;
+            if (k + 2 < n_items && ++itC == iters) {
+                itC = 0;
+                tC += tile_stride;
+            }
+            issue(bufA, tC, itC);
+            if (k + 1 < n_items) consume(bufB, tB, itB);
+            tA = tC;
+            itA = itC;
+        }
+    }
+
+    if (MODE == kModeArgmax) {
+        __shared__ uint64_t wave_best[kBlockThreads / kWave];
+        uint64_t key = best_i < p.M ? argmax_key(best_v, best_i) : 0ull;
+        for (int o = kWave / 2; o > 0; o >>= 1) {
+            const uint64_t other = __shfl_xor(key, o, kWave);
+            key = other > key ? other : key;
+        }
+        if (lane == 0) wave_best[wave] = key;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint64_t k = wave_best[0];
+            for (int w = 1; w < waves_per_block; w++) k = wave_best[w] > k ? wave_best[w] : k;
+            p.partials[blockIdx.x] = k;
+        }
+    }
+}
+
+}  // namespace qmv

@@ -1,0 +1,188 @@
+/*
+ * qmv.h -- C ABI of libqmv.so: dequantize-fused matrix-vector products over
+ * GGUF block-quantised weights on AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (the pages are prior art written for CPUs and
+ * WebGPU; the operations below are what they describe):
+ *  - Weights stay in their GGUF block formats and are dequantised on the fly;
+ *    activations and results are f32.  BebeLM page ("BebeLM：纯Rust实现的端侧
+ *    大模型推理引擎"), section "量化格式支持": Q4_K super-blocks of 256 weights
+ *    in 144 bytes, Q6_K for sensitive tensors, run-time dequantisation with f32
+ *    activations.  Wick page, section "量化支持": Q4_K_M and Q8_0.
+ *  - Fused QKV and gate/up row stacks, greedy fused argmax, small-batch verify
+ *    for n-gram speculative decoding and preallocated buffers with no
+ *    allocation during inference: FlareLLM page, section "推理层面的深度优化".
+ *  - Sigmoid-routed top-k MoE FFN: BebeLM page, section "核心算子".
+ *  - Decode is memory-bandwidth bound: BebeLM page, section "性能表现".
+ *
+ * Block layouts (bytes, little-endian; rows are consecutive blocks, matrices
+ * consecutive rows; B = weights per block):
+ *   Q8_0 (B = 32, 34 bytes):  fp16 d | int8 q[32];           w = d*q
+ *   Q4_K (B = 256, 144 bytes): fp16 d | fp16 dmin | 12 bytes of packed 6-bit
+ *        sub-block scales/mins | 128 bytes of nibbles;    w = d*sc*q - dmin*m
+ *   Q6_K (B = 256, 210 bytes): 128 bytes low nibbles | 64 bytes high 2-bit
+ *        pairs | int8 sc[16] | fp16 d;                    w = d*sc*(q - 32)
+ *   (the bit order inside the fields is the standard GGUF one.)
+ *
+ * Conventions shared by every entry point:
+ *  - Ownership: the caller allocates and owns every buffer (device memory,
+ *    unless a parameter says "host").  The library never allocates, frees,
+ *    copies between host and device or synchronises, and keeps no pointer
+ *    after it returns.
+ *  - Asynchrony: all work is enqueued on `stream` (0 = the null stream) of the
+ *    current device and the call returns at once; results are valid after the
+ *    stream is synchronised.
+ *  - Outputs are overwritten, never accumulated into.  Outputs must not alias
+ *    inputs or the workspace.
+ *  - Alignment: `x`/`X` must be 16-byte aligned, outputs 4-byte, `blocks`
+ *    2-byte (so row slices of any matrix are valid; 16-byte-aligned block
+ *    buffers stream fastest).
+ *  - Errors: every check runs on the host before anything is enqueued; a call
+ *    that returns anything but QMV_OK has enqueued nothing.  QMV_EHIP means a
+ *    launch failed; qmv_last_hip_error() returns the raw HIP code.  No
+ *    exception crosses the ABI.  The library is re-entrant: its only state is
+ *    a per-device cache of the compute-unit count and a thread-local error.
+ *  - Shapes: M >= 1, K >= 1, K a multiple of B, K <= QMV_MAX_K.
+ */
+#ifndef QMV_H
+#define QMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Block formats, numbered with their GGUF tensor type ids. */
+typedef enum { QMV_Q8_0 = 8, QMV_Q4_K = 12, QMV_Q6_K = 14 } qmv_type;
+
+typedef enum {
+    QMV_OK = 0,
+    QMV_EINVAL = 1,      /* null pointer, unknown type, bad count */
+    QMV_ESHAPE = 2,      /* M, K, n, E, k or a segment size out of range */
+    QMV_EALIGN = 3,      /* pointer not aligned as required */
+    QMV_EWORKSPACE = 4,  /* workspace missing or smaller than required */
+    QMV_EHIP = 5         /* a HIP call failed; see qmv_last_hip_error() */
+} qmv_status;
+
+/* Operations that need a workspace, for qmv_workspace_bytes(). */
+typedef enum { QMV_OP_ARGMAX = 1, QMV_OP_MOE = 2 } qmv_op;
+
+/* Largest K (columns) any entry point accepts: x is staged whole in LDS. */
+#define QMV_MAX_K 32768
+/* Most segments in one qmv_fused_rows call. */
+#define QMV_MAX_SEGMENTS 8
+/* Most columns in one qmv_gemm_n call. */
+#define QMV_MAX_N 16
+
+/* ---- single token: y[M] = dequant(W)[M x K] . x[K] ----------------------
+ * blocks: M*K/B blocks, row-major (row i is K/B consecutive blocks).
+ * x: f32[K].  y: f32[M].  Wick page, section "量化支持" (Q8_0, Q4_K_M);
+ * BebeLM page, section "量化格式支持" (Q4_K, Q6_K, f32 activations). */
+qmv_status qmv_q8_0(const void *blocks, int64_t M, int64_t K, const float *x, float *y,
+                    hipStream_t stream);
+qmv_status qmv_q4_k(const void *blocks, int64_t M, int64_t K, const float *x, float *y,
+                    hipStream_t stream);
+qmv_status qmv_q6_k(const void *blocks, int64_t M, int64_t K, const float *x, float *y,
+                    hipStream_t stream);
+
+/* ---- fused row stack: one launch over nseg row segments sharing x --------
+ * FlareLLM page, section "推理层面的深度优化" (fused QKV and gate/up
+ * projections cut the matvec calls per layer).  The stack holds
+ * sum(seg_rows) rows of K columns in format t; segment s is rows
+ * [sum_{r<s} seg_rows[r], sum_{r<=s} seg_rows[r]) and its result goes to the
+ * device buffer y_seg[s] (f32[seg_rows[s]]).  seg_rows and y_seg are HOST
+ * arrays of nseg entries, 1 <= nseg <= QMV_MAX_SEGMENTS, each seg_rows >= 1.
+ * Each output equals, bit for bit, what the single-token call returns for
+ * the same rows. */
+qmv_status qmv_fused_rows(qmv_type t, const void *blocks, int64_t K, const float *x,
+                          int32_t nseg, const int64_t *seg_rows, float *const *y_seg,
+                          hipStream_t stream);
+
+/* ---- fused greedy argmax: the index and value of max_i (dequant(W) x)_i ---
+ * FlareLLM page, section "推理层面的深度优化": at temperature 0 the next
+ * token is found during the output projection, without a logits buffer.
+ * Ties go to the lowest index.  idx_out: int32[1], max_out: f32[1] (device).
+ * workspace: device, >= qmv_workspace_bytes(QMV_OP_ARGMAX, M, K, 0, 0) bytes,
+ * 8-byte aligned, no initial contents needed.  The per-row values are the
+ * ones qmv_q*_* returns for the same (t, M, K). */
+qmv_status qmv_argmax(qmv_type t, const void *blocks, int64_t M, int64_t K, const float *x,
+                      int32_t *idx_out, float *max_out, void *workspace, size_t ws_bytes,
+                      hipStream_t stream);
+
+/* ---- sigmoid-routed top-k MoE FFN for one token ---------------------------
+ * BebeLM page, section "核心算子" (MoE FFN): router scores are sigmoids
+ * (not a softmax); the k experts with the largest score + bias are chosen
+ * (the bias only ranks; ties go to the lower expert index); their weights are
+ * the unbiased scores renormalised to sum 1; section "量化格式支持" keeps the
+ * router and the expert bias in f32.  For each chosen expert e:
+ *   g = Gate_e x, u = Up_e x, h = silu(g) * u, y_e = Down_e h;  y = sum w_e y_e.
+ * x: f32[H].  router: f32[E][H] (row e scores expert e).  bias: f32[E].
+ * gate_up: E stacked matrices of 2I rows x H columns in format gu_t (rows
+ *   0..I-1 gate, I..2I-1 up).  down: E stacked matrices of H rows x I columns
+ *   in format dn_t.
+ * y: f32[H].  topk_idx: int32[k] and topk_w: f32[k], in rank order.
+ * workspace: device, >= qmv_workspace_bytes(QMV_OP_MOE, H, I, E, k) bytes,
+ *   16-byte aligned.  Layout after the call (for inspection): f32 logits[E]
+ *   at byte 0, then at byte 256: f32 g[k][I], u[k][I], h[k][I].
+ * Constraints: 1 <= k <= E <= 64; H and I multiples of their formats' B. */
+qmv_status moe_qmv_topk(const float *x, int64_t H, const float *router, const float *bias,
+                        int32_t E, int32_t k, qmv_type gu_t, const void *gate_up,
+                        qmv_type dn_t, const void *down, int64_t I, float *y,
+                        int32_t *topk_idx, float *topk_w, void *workspace, size_t ws_bytes,
+                        hipStream_t stream);
+
+/* ---- small batch (speculative verify): Y[n][M] = X[n][K] . dequant(W)^T ----
+ * FlareLLM page, section "推理层面的深度优化" (n-gram speculative decoding
+ * checks several drafted tokens against the same weights).  X: f32 n x K
+ * row-major, Y: f32 n x M row-major, 1 <= n <= QMV_MAX_N.  Runs on the matrix
+ * cores; see the implementation notes for the accuracy bound. */
+qmv_status qmv_gemm_n(qmv_type t, const void *blocks, int64_t M, int64_t K, int32_t n,
+                      const float *X, float *Y, hipStream_t stream);
+
+/* ---- dequantise to f32 (verification surface): w_out[M][K] --------------
+ * Bit-exact block decoding, the values every matvec above is defined on. */
+qmv_status qmv_dequant(qmv_type t, const void *blocks, int64_t M, int64_t K, float *w_out,
+                       hipStream_t stream);
+
+/* ---- quantise f32 weights to blocks (weight preparation) -----------------
+ * w: f32 M x K row-major; blocks_out: M*K/B blocks.  Plain min/max rules
+ * (the pages give none): Q8_0 d = max|w|/127, q = round(w/d); Q4_K mins
+ * first (dmin = max(-min)/62), then scales (d = max s/62, s = range/15);
+ * Q6_K s = max|w|/31, d = max s/126; codes rounded half away from zero. */
+qmv_status qmv_quantize(qmv_type t, const float *w, int64_t M, int64_t K, void *blocks_out,
+                        hipStream_t stream);
+
+/* ---- helpers -------------------------------------------------------------- */
+/* Bytes of one row of K weights in format t; 0 if K is not a multiple of B. */
+size_t qmv_row_bytes(qmv_type t, int64_t K);
+/* Workspace an operation needs.  ARGMAX: (M, K, -, -); MOE: (H, I, E, k). */
+size_t qmv_workspace_bytes(qmv_op op, int64_t a, int64_t b, int32_t c, int32_t d);
+/* Raw HIP error code of this thread's last QMV_EHIP (0 if none). */
+int qmv_last_hip_error(void);
+/* Static, human-readable name of a status. */
+const char *qmv_status_str(qmv_status s);
+
+/* ---- kernel timing hook (measurement only) --------------------------------
+ * Arms this thread's next call: its main kernel (the matvec, argmax, MoE
+ * expert or small-batch kernel) is launched with hipExtLaunchKernelGGL so that
+ * the caller-created events `start` and `stop` carry that kernel's own
+ * dispatch start and end timestamps -- no marker packets, no gaps counted.
+ * Both events must be valid (created by the caller) or both NULL (disarm).
+ * The hook is consumed by the next launching call on this thread. */
+qmv_status qmv_time_next_launch(hipEvent_t start, hipEvent_t stop);
+
+/* ---- bandwidth probe (measurement only) -----------------------------------
+ * Streams `bytes` (a multiple of 16, buffer 16-byte aligned) with the same
+ * 128-bit loads the matvec kernels use and writes one u32 per workgroup into
+ * sink (>= 2048 entries); gives the achievable HBM read rate on this device. */
+qmv_status qmv_probe_stream_read(const void *buf, size_t bytes, uint32_t *sink,
+                                 hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMV_H */

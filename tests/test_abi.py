@@ -1,0 +1,89 @@
+"""CPU checks of the C ABI: libqmv.so loads, exports every function that
+include/qmv.h declares, and rejects bad arguments on the host with the
+documented status before touching the GPU (no compute call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gguf_dequant_matvec_amd as q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qmv.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(q.LIB_PATH), reason="libqmv.so not built")
+
+
+def declared_functions():
+    src = open(HEADER, encoding="utf-8").read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while")))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(q.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported():
+    lib = q.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_row_bytes_and_workspace():
+    assert q.qmv_row_bytes("q8_0", 576) == 612
+    assert q.qmv_row_bytes("q4_k", 4096) == 2304
+    assert q.qmv_row_bytes("q6_k", 1536) == 1260
+    assert q.qmv_row_bytes("q4_k", 100) == 0
+    assert q.qmv_workspace_bytes(q.OP_ARGMAX, 128000, 4096) >= 8 * 2048
+    assert q.qmv_workspace_bytes(q.OP_MOE, 2048, 1536, 32, 4) == 256 + 3 * 4 * 1536 * 4
+    assert q.load().qmv_status_str(3) == b"pointer misaligned"
+
+
+A16 = 1 << 20      # fake, 16-byte aligned addresses: never dereferenced
+
+
+def status_of(fn, *args):
+    with pytest.raises(q.QmvError) as e:
+        fn(*args, stream=0)
+    return e.value.status_name
+
+
+def test_shape_errors():
+    assert status_of(q.qmv_q4_k, A16, 0, 256, A16, A16) == "QMV_ESHAPE"
+    assert status_of(q.qmv_q4_k, A16, 4, 100, A16, A16) == "QMV_ESHAPE"
+    assert status_of(q.qmv_q6_k, A16, 4, 0, A16, A16) == "QMV_ESHAPE"
+    assert status_of(q.qmv_q8_0, A16, 4, 48, A16, A16) == "QMV_ESHAPE"
+    assert status_of(q.qmv_q8_0, A16, 4, q.MAX_K + 32, A16, A16) == "QMV_ESHAPE"
+    assert status_of(q.qmv_gemm_n, "q4_k", A16, 4, 256, 17, A16, A16) == "QMV_ESHAPE"
+    assert status_of(q.qmv_gemm_n, "q4_k", A16, 4, 256, 0, A16, A16) == "QMV_ESHAPE"
+    assert status_of(q.qmv_fused_rows, "q4_k", A16, 256, A16, [4, 0], [A16, A16]) == "QMV_ESHAPE"
+
+
+def test_pointer_and_type_errors():
+    assert status_of(q.qmv_q4_k, 0, 4, 256, A16, A16) == "QMV_EINVAL"
+    assert status_of(q.qmv_q4_k, A16, 4, 256, 0, A16) == "QMV_EINVAL"
+    assert status_of(q.qmv_dequant, 13, A16, 4, 256, A16) == "QMV_EINVAL"
+    assert status_of(q.qmv_fused_rows, "q4_k", A16, 256, A16, [1] * 9, [A16] * 9) == "QMV_EINVAL"
+    assert status_of(q.qmv_fused_rows, "q4_k", A16, 256, A16, [], []) == "QMV_EINVAL"
+
+
+def test_alignment_errors():
+    assert status_of(q.qmv_q4_k, A16 + 1, 4, 256, A16, A16) == "QMV_EALIGN"
+    assert status_of(q.qmv_q4_k, A16, 4, 256, A16 + 4, A16) == "QMV_EALIGN"
+    assert status_of(q.qmv_q4_k, A16, 4, 256, A16, A16 + 2) == "QMV_EALIGN"
+
+
+def test_workspace_errors():
+    ws = q.qmv_workspace_bytes(q.OP_ARGMAX, 1000, 256)
+    assert status_of(q.qmv_argmax, "q6_k", A16, 1000, 256, A16, A16, A16, A16, ws - 8) == \
+        "QMV_EWORKSPACE"
+    assert status_of(q.qmv_argmax, "q6_k", A16, 1000, 256, A16, A16, A16, 0, ws) == \
+        "QMV_EWORKSPACE"
+    wm = q.qmv_workspace_bytes(q.OP_MOE, 2048, 1536, 32, 4)
+    args = (A16, 2048, A16, A16, 32, 4, "q4_k", A16, "q6_k", A16, 1536, A16, A16, A16, A16)
+    assert status_of(q.moe_qmv_topk, *args, wm - 4) == "QMV_EWORKSPACE"
+    bad_k = (A16, 2048, A16, A16, 32, 33, "q4_k", A16, "q6_k", A16, 1536, A16, A16, A16, A16)
+    assert status_of(q.moe_qmv_topk, *bad_k, wm) == "QMV_ESHAPE"

@@ -1,0 +1,201 @@
+"""GPU parity: dequantisation, single-token matvec, fused rows, argmax and the
+quantiser of libqmv against the CPU oracle, through the C ABI.
+
+Bars: dequantised values and argmax indices bit-exact; matvec outputs within
+1e-5 * sum_k |w_ik x_k| per output; one-hot x bit-exact; fused rows
+bit-identical to the separate calls; quantised bytes bit-exact.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import golden_blocks
+from tests.gpu_util import assert_rel, dev, empty, host, quantized
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import gguf_dequant_matvec_amd as q  # noqa: E402
+
+# (type, M, K): several tiles, ragged tails, every lane-group width, odd Q8_0
+# block counts, the smallest legal shapes.
+SHAPES = [
+    ("q4_k", 1, 256), ("q4_k", 5, 256), ("q4_k", 77, 2048), ("q4_k", 1000, 4096),
+    ("q4_k", 300, 14336), ("q4_k", 129, 8192), ("q4_k", 63, 1536),
+    ("q6_k", 1, 256), ("q6_k", 50, 256), ("q6_k", 333, 1536), ("q6_k", 1000, 4096),
+    ("q6_k", 97, 14336),
+    ("q8_0", 1, 32), ("q8_0", 1536, 576), ("q8_0", 37, 224), ("q8_0", 100, 4096),
+    ("q8_0", 19, 96),
+]
+
+
+def _case(t, M, K, seed):
+    b = quantized(t, M, K, seed)
+    x = synth.activations(seed + 1, K)
+    return b, x
+
+
+@pytest.mark.parametrize("t,M,K", SHAPES)
+def test_dequant_bit_exact(t, M, K):
+    b, _ = _case(t, M, K, 100 + M)
+    ref = oracle.dequant(t, b, M, K)
+    out = empty(M * K)
+    q.qmv_dequant(t, dev(b), M, K, out)
+    got = host(out).reshape(M, K)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_dequant_handbuilt_blocks():
+    for t, name, blk, expected in golden_blocks.load():
+        n = len(expected)
+        out = empty(n)
+        q.qmv_dequant(t, dev(blk), 1, n, out)
+        bad = golden_blocks.matches(host(out), expected)
+        assert not bad, (name, bad[:5])
+
+
+@pytest.mark.parametrize("t,M,K", SHAPES)
+def test_qmv_parity(t, M, K):
+    b, x = _case(t, M, K, 200 + M)
+    y_ref, a_ref = oracle.qmv(t, b, M, K, x)
+    y = empty(M)
+    q.qmv(t, dev(b), M, K, dev(x), y)
+    assert_rel(host(y), y_ref, a_ref, what=f"{t} {M}x{K}")
+
+
+@pytest.mark.parametrize("t,M,K", [("q4_k", 40, 4096), ("q6_k", 40, 1536), ("q8_0", 40, 576),
+                                   ("q8_0", 9, 224), ("q4_k", 33, 14336)])
+def test_qmv_one_hot_is_exact(t, M, K):
+    b, _ = _case(t, M, K, 300)
+    W = oracle.dequant(t, b, M, K)
+    bd = dev(b)
+    for k in sorted({c for c in [0, 1, 17, 31, 32, 63, 64, 127, 128, 200, 255, K - 1] if c < K}):
+        x = np.zeros(K, dtype=np.float32)
+        x[k] = 1.0
+        y = empty(M)
+        q.qmv(t, bd, M, K, dev(x), y)
+        assert np.array_equal(host(y), W[:, k]), (t, k)
+
+
+def test_qmv_scaled_integer_x_is_exact():
+    """Hand-built integer blocks (d = dmin = 1) and x = 2^-3 * small integers:
+    every partial sum is an exactly representable f32, so y is exact."""
+    for t, name, blk, expected in golden_blocks.load():
+        if not all(v.denominator == 1 for v, _ in expected):
+            continue
+        n = len(expected)
+        x = ((np.arange(n) % 7) - 3).astype(np.float32) * np.float32(0.125)
+        y_ref, _ = oracle.qmv(t, blk, 1, n, x)
+        y = empty(1)
+        q.qmv(t, dev(blk), 1, n, dev(x), y)
+        assert float(host(y)[0]) == y_ref[0], name
+
+
+def test_x_extremes():
+    """Large and tiny activations (1e30 .. 1e-30) keep the relative bound."""
+    t, M, K = "q4_k", 64, 4096
+    b = quantized(t, M, K, 310)
+    g = np.random.default_rng(311)
+    x = (g.standard_normal(K) * 10.0 ** g.integers(-30, 30, K)).astype(np.float32)
+    y_ref, a_ref = oracle.qmv(t, b, M, K, x)
+    y = empty(M)
+    q.qmv(t, dev(b), M, K, dev(x), y)
+    assert_rel(host(y), y_ref, a_ref, what="wide-range x")
+
+
+@pytest.mark.parametrize("t,segs,K", [
+    ("q4_k", (2048, 512, 512), 2048),          # Llama-3.2-1B QKV
+    ("q4_k", (8192, 8192), 2048),              # Llama-3.2-1B gate+up
+    ("q6_k", (100, 7, 1, 60), 1536),
+    ("q8_0", (300, 11, 5), 576),
+    ("q4_k", tuple([3] * 8), 4096),            # the most segments
+])
+def test_fused_rows(t, segs, K):
+    M = sum(segs)
+    b, x = _case(t, M, K, 400 + len(segs))
+    bd, xd = dev(b), dev(x)
+    ys = [empty(m) for m in segs]
+    q.qmv_fused_rows(t, bd, K, xd, list(segs), ys)
+    y_ref, a_ref = oracle.qmv(t, b, M, K, x)
+    rb = q.row_bytes(t, K)
+    r0 = 0
+    for m, ys_ in zip(segs, ys):
+        got = host(ys_)
+        assert_rel(got, y_ref[r0:r0 + m], a_ref[r0:r0 + m], what=f"segment at {r0}")
+        # bit-identical to a separate single-token call on the same rows
+        sep = empty(m)
+        q.qmv(t, bd[r0 * rb:(r0 + m) * rb], m, K, xd, sep)
+        assert np.array_equal(host(sep).view(np.uint32), got.view(np.uint32))
+        r0 += m
+
+
+def _argmax_gpu(t, bd, M, K, xd):
+    idx = empty(1, "int32")
+    mx = empty(1)
+    ws = empty(q.qmv_workspace_bytes(q.OP_ARGMAX, M, K), "uint8")
+    q.qmv_argmax(t, bd, M, K, xd, idx, mx, ws)
+    return int(host(idx)[0]), float(host(mx)[0])
+
+
+@pytest.mark.parametrize("t,M,K", [("q6_k", 5000, 4096), ("q4_k", 777, 2048), ("q8_0", 1536, 576),
+                                   ("q6_k", 1, 256), ("q6_k", 3001, 1536)])
+def test_argmax(t, M, K):
+    b, x = _case(t, M, K, 500 + M)
+    y_ref, a_ref = oracle.qmv(t, b, M, K, x)
+    i_ref = int(np.argmax(y_ref))
+    bd, xd = dev(b), dev(x)
+    i, v = _argmax_gpu(t, bd, M, K, xd)
+    if M == 1:
+        assert i == 0
+    elif y_ref[i_ref] - np.sort(y_ref)[-2] > 1e-5 * (a_ref[i_ref] + a_ref[np.argsort(y_ref)[-2]]):
+        assert i == i_ref
+    else:   # near tie: any member of the near-tie set
+        assert y_ref[i_ref] - y_ref[i] <= 1e-5 * (a_ref[i_ref] + a_ref[i])
+    assert abs(v - y_ref[i]) <= 1e-5 * a_ref[i]
+    # same per-row values as the matvec: argmax of its y, bit for bit
+    y = empty(M)
+    q.qmv(t, bd, M, K, xd, y)
+    yh = host(y)
+    assert i == int(np.argmax(yh)) and np.float32(v) == yh[i]
+
+
+def test_argmax_ties_go_low():
+    t, M, K = "q6_k", 4000, 1536
+    b, x = _case(t, M, K, 600)
+    y_ref, _ = oracle.qmv(t, b, M, K, x)
+    win = int(np.argmax(y_ref))
+    rb = q.row_bytes(t, K)
+    b2 = b.copy()
+    for r in (win + 1, M - 1, 3):     # exact copies of the winner, one below it
+        b2[r * rb:(r + 1) * rb] = b[win * rb:(win + 1) * rb]
+    i, _ = _argmax_gpu(t, dev(b2), M, K, dev(x))
+    assert i == min(3, win)
+
+
+@pytest.mark.parametrize("t", ["q8_0", "q4_k", "q6_k"])
+def test_quantize_matches_oracle(t):
+    M, K = 96, 4096
+    w = synth.weights(700, M, K)
+    w[3, :256] = 0.0                       # an all-zero block
+    w[5, :256] = np.abs(w[5, :256])        # a non-negative block (m = 0)
+    ref = oracle.quantize(t, w)
+    out = empty(ref.size, "uint8")
+    q.qmv_quantize(t, dev(w), M, K, out)
+    got = host(out)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, bad[:10]
+
+
+def test_probe_reads_everything():
+    n = 1 << 22
+    g = np.random.default_rng(3)
+    buf = g.integers(0, 2 ** 32, n // 4, dtype=np.uint32)
+    sink = empty(2048, "int32")
+    sink.zero_()
+    q.qmv_probe_stream_read(dev(buf.view(np.uint8)), n, sink)
+    got = np.bitwise_xor.reduce(host(sink).view(np.uint32))
+    assert got == np.bitwise_xor.reduce(buf)
