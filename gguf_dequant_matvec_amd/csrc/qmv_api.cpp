@@ -103,7 +103,7 @@ size_t qmv_workspace_bytes(qmv_op op, int64_t a, int64_t b, int32_t c, int32_t d
     if (op == QMV_OP_ARGMAX) return (size_t)kMaxGrid * sizeof(uint64_t);
     if (op == QMV_OP_MOE) {
         if (b < 1 || c < 1 || d < 1) return 0;
-        // logits[E] padded to 256 B, then g, u, h: k x I f32 each
+        // logits[E] padded to 256 B, then gu[k][2I] and h[k][I] in f32
         return 256 + 3 * (size_t)d * (size_t)b * sizeof(float);
     }
     return 0;
@@ -198,6 +198,9 @@ qmv_status moe_qmv_topk(const float *x, int64_t H, const float *router, const fl
         return QMV_EINVAL;
     if (!valid_type(gu_t) || !valid_type(dn_t)) return QMV_EINVAL;
     if (E < 1 || E > 64 || k < 1 || k > E) return QMV_ESHAPE;
+    if (H < 1 || I < 1 || (int64_t)k * I > QMV_MAX_K || (int64_t)k * 2 * I > 0x7FFFFFFFll)
+        return QMV_ESHAPE;
+    if (dn_t == QMV_Q8_0 && I % 128 != 0) return QMV_ESHAPE;
     qmv_status st = check_matrix(gu_t, gate_up, 2 * I, H);
     if (st != QMV_OK) return st;
     st = check_matrix(dn_t, down, H, I);

@@ -1,79 +1,9 @@
 // Single-token, fused-row and argmax launches of the row-streaming kernel.
-#include "qmv_internal.h"
-#include "qmv_rows.h"
+#include "qmv_launch.h"
 
 namespace qmv {
 
 namespace {
-
-// Fraction of lane-steps that carry work when a row of U units is spread over
-// G lanes; the launcher picks the G (>= 4, a power of two) that maximises it,
-// preferring wider groups on ties (fewer rows per wave, better coalescing).
-int pick_group(int U) {
-    int best = 64;
-    double best_eff = -1.0;
-    for (int G = 64; G >= 4; G >>= 1) {
-        const int steps = (U + G - 1) / G;
-        const double eff = (double)U / ((double)G * steps);
-        if (eff > best_eff + 1e-9) {
-            best_eff = eff;
-            best = G;
-        }
-    }
-    return best;
-}
-
-constexpr int kR = 2;  // row slots per lane
-
-template <class F, int MODE>
-using KernelPtr = void (*)(RowsParams);
-
-template <class F, int MODE>
-KernelPtr<F, MODE> kernel_for(int G) {
-    switch (G) {
-    case 4: return rows_kernel<F, 4, kR, MODE>;
-    case 8: return rows_kernel<F, 8, kR, MODE>;
-    case 16: return rows_kernel<F, 16, kR, MODE>;
-    case 32: return rows_kernel<F, 32, kR, MODE>;
-    default: return rows_kernel<F, 64, kR, MODE>;
-    }
-}
-
-template <class F, int MODE>
-hipError_t launch_typed(const RowsParams &p, hipStream_t s, int *grid_out) {
-    const int U = p.K / F::kUnitWeights;
-    const int G = pick_group(U);
-    const int64_t rows_per_tile = (int64_t)kR * (kWave / G);
-    const int64_t ntiles = ((int64_t)p.M + rows_per_tile - 1) / rows_per_tile;
-    const int waves = kBlockThreads / kWave;
-    const size_t lds =
-        ((size_t)lds_x_floats<F>(p.K) + (F::kSumGroup ? (size_t)p.K / F::kSumGroup : 0)) * 4;
-    KernelPtr<F, MODE> k = kernel_for<F, MODE>(G);
-    hipError_t e = ensure_lds((const void *)k, lds);
-    if (e != hipSuccess) return e;
-    // persistent grid: exactly the workgroups that are resident at once, so
-    // no workgroup waits for a second round while compute units idle
-    const int per_cu = resident_blocks((const void *)k, kBlockThreads, lds);
-    int64_t grid = (ntiles + waves - 1) / waves;
-    const int64_t cap = (int64_t)device_cu_count() * per_cu;
-    if (grid > cap) grid = cap;
-    if (grid > kMaxGrid) grid = kMaxGrid;
-    if (grid < 1) grid = 1;
-    if (grid_out) *grid_out = (int)grid;
-    return launch_main(k, dim3((unsigned)grid), dim3(kBlockThreads), lds, s, p);
-}
-
-template <int MODE>
-hipError_t launch_fmt(int type, const RowsParams &p, hipStream_t s, int *grid_out) {
-    switch (type) {
-    case kQ4K: return launch_typed<Q4K, MODE>(p, s, grid_out);
-    case kQ6K: return launch_typed<Q6K, MODE>(p, s, grid_out);
-    case kQ80:
-        if ((p.K / 32) % 2 == 0) return launch_typed<Q80x2, MODE>(p, s, grid_out);
-        return launch_typed<Q80x1, MODE>(p, s, grid_out);
-    default: return hipErrorInvalidValue;
-    }
-}
 
 __global__ __launch_bounds__(256) void argmax_finalize(const uint64_t *partials, int n,
                                                        int32_t *idx_out, float *max_out) {

@@ -1,5 +1,5 @@
-// The row-streaming matvec kernel shared by the single-token, fused-row and
-// argmax entry points.
+// The row-streaming matvec kernel shared by the single-token, fused-row,
+// argmax and MoE expert entry points.
 //
 // Work split: a wave owns tiles of rows; inside a tile, groups of G lanes
 // cooperate on one row (64/G rows side by side) and each lane also carries R
@@ -7,13 +7,25 @@
 // The activation vector x is staged once per workgroup in LDS together with
 // its per-sub-block sums; every lane keeps the same unit position modulo G,
 // so its 64 activations are read from LDS once per step and reused by all R
-// rows.  The grid is persistent (a few workgroups per compute unit) so that
-// the LDS staging is paid once per workgroup, not once per row.
+// rows.  The grid is persistent (exactly the resident workgroups) so the LDS
+// staging is paid once per workgroup, not once per row.
 //
 // The per-row result is a fixed butterfly over the G lanes of fixed partial
 // sums, so it depends only on (format, K, G, R) -- never on M, the grid or
 // which rows share a tile.  That makes fused-row outputs and argmax values
 // bit-identical to the plain matvec of the same rows.
+//
+// MoE modes (BebeLM page, section "核心算子": sigmoid router, top-k experts,
+// bias used only to select, weights renormalised):
+//  - kModeMoeGateUp: rows are the gate/up rows of the k selected experts,
+//    stacked; every workgroup first derives the selection from the router
+//    logits (so no host round trip and no extra launch), workgroup 0 publishes
+//    it.  Tiles never straddle experts, so the expert of a tile is uniform.
+//  - kModeMoeDown: row i is the concatenation over the k selected experts of
+//    their down-projection row i, and x is the concatenation of
+//    w_s * silu(g_s) * u_s; one row sum is then the weighted expert mixture,
+//    formed in a fixed order.  G divides the units per expert, so the expert
+//    of each unit step is uniform too.
 #pragma once
 
 #include <stdint.h>
@@ -23,6 +35,7 @@
 namespace qmv {
 
 constexpr int kMaxSegments = 8;
+constexpr int kMaxExperts = 64;
 
 // Row counts are below 2^31 (checked on the host), so every row and tile
 // index is 32-bit and wave-uniform bookkeeping stays in scalar registers.
@@ -30,6 +43,20 @@ struct SegTable {
     int32_t n;
     int32_t start[kMaxSegments + 1];  // prefix sums of the segment row counts
     float *y[kMaxSegments];
+};
+
+struct MoeArgs {
+    const float *logits;    // [E] router logits (gate/up launch)
+    const float *bias;      // [E] selection bias (gate/up launch)
+    int32_t E, k;
+    int32_t *topk_idx;      // [k] written by the gate/up launch, read by the down launch
+    float *topk_w;          // [k]
+    const float *gu;        // down launch: [k][2I] gate rows then up rows per slot
+    float *h;               // down launch: [k][I] silu(g) * u, written by workgroup 0
+    int64_t mat_bytes;      // bytes of one expert matrix
+    int32_t rows_per_mat;   // gate/up launch: 2I
+    int32_t units_per_mat;  // down launch: I / unit weights
+    int32_t I;
 };
 
 struct RowsParams {
@@ -40,9 +67,10 @@ struct RowsParams {
     const float *x;
     SegTable seg;
     uint64_t *partials;  // argmax mode: one packed (value, index) key per workgroup
+    MoeArgs moe;
 };
 
-enum { kModeStore = 0, kModeArgmax = 1 };
+enum { kModeStore = 0, kModeArgmax = 1, kModeMoeGateUp = 2, kModeMoeDown = 3 };
 
 // Packed argmax key: larger value first, then lower index.
 __device__ __forceinline__ uint64_t argmax_key(float v, int32_t idx) {
@@ -50,17 +78,36 @@ __device__ __forceinline__ uint64_t argmax_key(float v, int32_t idx) {
     return ((uint64_t)float_key(v) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)idx);
 }
 
+// Floats of the padded LDS copy of x.
+template <class F>
+__host__ __device__ constexpr int lds_x_floats(int K) {
+    return K + (K / F::kPadEvery) * 4;
+}
+
+// Store four consecutive activations (x[i..i+3]) into the padded LDS copy and
+// add their group sum: the kSumGroup/4 consecutive lanes that hold one group
+// combine with a shuffle butterfly, so the sums need no extra pass over LDS.
+// Every lane of the wave must call this (the shuffles span the group).
+template <class F>
+__device__ __forceinline__ void put_x4(float *xs, float *sums, int i, bool valid, float4 v) {
+    constexpr int kLanes = F::kSumGroup > 0 ? F::kSumGroup / 4 : 1;
+    if (valid) *reinterpret_cast<float4 *>(xs + i + (i / F::kPadEvery) * 4) = v;
+    if (F::kSumGroup > 0) {
+        float sum = (v.x + v.y) + (v.z + v.w);
+#pragma unroll
+        for (int o = 1; o < kLanes; o <<= 1) sum += __shfl_xor(sum, o, kWave);
+        if (valid && (threadIdx.x % kLanes) == 0) sums[i / (F::kSumGroup > 0 ? F::kSumGroup : 1)] = sum;
+    }
+}
+
 // Stage x[0..K) in LDS, plus the sums of its consecutive groups of
 // F::kSumGroup values.  x is stored padded (4 floats after every
 // F::kPadEvery) so that the lanes' 16-byte reads spread over the LDS banks.
-// Loads are issued eight at a time; each group's sum is formed by the
-// kSumGroup/4 consecutive lanes that loaded it (a shuffle butterfly), so the
-// sums need no extra pass over LDS.  K is a multiple of 32,
-// so a lane group is either wholly inside [0, K) or wholly outside.
+// Loads are issued eight at a time.  K is a multiple of 32, so a lane group
+// is either wholly inside [0, K) or wholly outside.
 template <class F>
 __device__ __forceinline__ void stage_x(const float *__restrict__ x, int K, float *xs,
                                         float *sums) {
-    constexpr int kLanes = F::kSumGroup > 0 ? F::kSumGroup / 4 : 1;
     const int nt = blockDim.x;
     for (int base = threadIdx.x * 4; base < K; base += nt * 4 * 8) {
         float4 v[8];
@@ -72,22 +119,50 @@ __device__ __forceinline__ void stage_x(const float *__restrict__ x, int K, floa
 #pragma unroll
         for (int j = 0; j < 8; j++) {
             const int i = base + j * nt * 4;
-            if (i < K) *reinterpret_cast<float4 *>(xs + i + (i / F::kPadEvery) * 4) = v[j];
-            if (F::kSumGroup > 0) {
-                float sum = (v[j].x + v[j].y) + (v[j].z + v[j].w);
-#pragma unroll
-                for (int o = 1; o < kLanes; o <<= 1) sum += __shfl_xor(sum, o, kWave);
-                if (i < K && (threadIdx.x % kLanes) == 0) sums[i / (F::kSumGroup > 0 ? F::kSumGroup : 1)] = sum;
-            }
+            put_x4<F>(xs, sums, i, i < K, v[j]);
         }
     }
     __syncthreads();
 }
 
-// Floats of the padded LDS copy of x.
-template <class F>
-__host__ __device__ constexpr int lds_x_floats(int K) {
-    return K + (K / F::kPadEvery) * 4;
+__device__ __forceinline__ float sigmoidf(float v) { return 1.0f / (1.0f + expf(-v)); }
+__device__ __forceinline__ float siluf(float v) { return v / (1.0f + expf(-v)); }
+
+// MoE selection from the router logits, done by wave 0 of every workgroup:
+// scores s_e = sigmoid(r_e); rank by s_e + b_e (ties to the lower expert);
+// weights = selected s_e over their sum.  Results land in LDS (and, from
+// workgroup 0, in topk_idx / topk_w).
+__device__ __forceinline__ void moe_select(const MoeArgs &m, int32_t *sel, float *wsel) {
+    if (threadIdx.x >= kWave) return;
+    const int e = threadIdx.x;
+    const float s = e < m.E ? sigmoidf(m.logits[e]) : 0.f;
+    const float v = e < m.E ? s + m.bias[e] : -__builtin_inff();
+    bool taken = e >= m.E;
+    float ssum = 0.f;
+    for (int t = 0; t < m.k; t++) {
+        // packed key: ordered score, then the lower index wins
+        uint64_t key = taken ? 0ull : (((uint64_t)float_key(v + 0.0f) << 32) | (uint64_t)(63 - e));
+        for (int o = kWave / 2; o > 0; o >>= 1) {
+            const uint64_t other = __shfl_xor(key, o, kWave);
+            key = other > key ? other : key;
+        }
+        const int win = 63 - (int)(key & 0xFFFFFFFFu);
+        const float swin = __shfl(s, win, kWave);
+        if (e == win) taken = true;
+        if (e == 0) {
+            sel[t] = win;
+            wsel[t] = swin;  // normalised below
+        }
+        ssum += swin;
+    }
+    if (e < m.k) {
+        const float w = wsel[e] / ssum;
+        wsel[e] = w;
+        if (blockIdx.x == 0) {
+            m.topk_idx[e] = sel[e];
+            m.topk_w[e] = w;
+        }
+    }
 }
 
 __device__ __forceinline__ float fp8_unit_inverse() {
@@ -99,10 +174,39 @@ __device__ __forceinline__ float fp8_unit_inverse() {
 
 template <class F, int G, int R, int MODE>
 __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
+    constexpr bool kMoe = MODE == kModeMoeGateUp || MODE == kModeMoeDown;
     extern __shared__ float smem[];
     float *xs = smem;
     float *sums = smem + lds_x_floats<F>(p.K);
-    stage_x<F>(p.x, p.K, xs, sums);
+    __shared__ int32_t sel[kMoe ? kMaxExperts : 1];
+    __shared__ float wsel[kMoe ? kMaxExperts : 1];
+
+    if (MODE == kModeMoeGateUp) {
+        moe_select(p.moe, sel, wsel);
+        stage_x<F>(p.x, p.K, xs, sums);  // its barrier also publishes sel
+    } else if (MODE == kModeMoeDown) {
+        if ((int)threadIdx.x < p.moe.k) {
+            sel[threadIdx.x] = p.moe.topk_idx[threadIdx.x];
+            wsel[threadIdx.x] = p.moe.topk_w[threadIdx.x];
+        }
+        __syncthreads();
+        // x[s*I + j] = w_s * silu(g_s[j]) * u_s[j]; workgroup 0 keeps h.
+        // K = k*I is a multiple of 32, so sum groups never straddle slots.
+        const int I = p.moe.I, K = p.K;
+        for (int base = threadIdx.x * 4; base < K; base += blockDim.x * 4) {
+            const int s = base / I, j = base - s * I;
+            const float4 g = *reinterpret_cast<const float4 *>(p.moe.gu + (int64_t)s * 2 * I + j);
+            const float4 u = *reinterpret_cast<const float4 *>(p.moe.gu + (int64_t)s * 2 * I + I + j);
+            const float4 h = make_float4(siluf(g.x) * u.x, siluf(g.y) * u.y, siluf(g.z) * u.z,
+                                         siluf(g.w) * u.w);
+            if (blockIdx.x == 0) *reinterpret_cast<float4 *>(p.moe.h + base) = h;
+            const float w = wsel[s];
+            put_x4<F>(xs, sums, base, true, make_float4(w * h.x, w * h.y, w * h.z, w * h.w));
+        }
+        __syncthreads();
+    } else {
+        stage_x<F>(p.x, p.K, xs, sums);
+    }
 
     const float inv_unit = fp8_unit_inverse();
     const int lane = threadIdx.x & (kWave - 1);
@@ -128,6 +232,12 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
 #pragma unroll
     for (int r = 0; r < R; r++) acc[r] = 0.f;
 
+    // The expert a unit step reads in the down launch (uniform: G divides the
+    // units per expert, so a step never straddles two experts).
+    auto step_slot = [&](int it) {
+        return MODE == kModeMoeDown ? __builtin_amdgcn_readfirstlane((G * it) / p.moe.units_per_mat) : 0;
+    };
+
     // One work item = (tile, unit step).  Items are software-pipelined: the
     // next item's weight loads are in flight while the current one is
     // multiplied, with two register sets used in turn (no copies, so no wait).
@@ -140,7 +250,19 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
         u = u < U ? u : U - 1;
         const int r0 = t * kRowsPerTile;
         const int last = (p.M - 1 - r0) < kRowsPerTile ? (p.M - 1 - r0) : kRowsPerTile;
-        const uint8_t *tile_base = p.W + (int64_t)r0 * p.row_bytes;
+        const uint8_t *tile_base;
+        if (MODE == kModeMoeGateUp) {
+            // the tile's rows belong to one selected expert
+            const int slot = r0 / p.moe.rows_per_mat;
+            tile_base = p.W + (int64_t)sel[slot] * p.moe.mat_bytes +
+                        (int64_t)(r0 - slot * p.moe.rows_per_mat) * p.row_bytes;
+        } else if (MODE == kModeMoeDown) {
+            const int slot = step_slot(it);
+            u -= slot * p.moe.units_per_mat;
+            tile_base = p.W + (int64_t)sel[slot] * p.moe.mat_bytes + (int64_t)r0 * p.row_bytes;
+        } else {
+            tile_base = p.W + (int64_t)r0 * p.row_bytes;
+        }
 #pragma unroll
         for (int r = 0; r < R; r++) {
             const int rr = rel[r] < last ? rel[r] : last;
@@ -156,7 +278,7 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
             acc[r] = 0.f;
         }
         const int r0 = t * kRowsPerTile;
-        if (MODE == kModeStore) {
+        if (MODE != kModeArgmax) {
             // segment of the tile's first row and the start of the next one:
             // compile-time indices over the table, all in scalar registers
             float *yb = p.seg.y[0];
@@ -205,6 +327,8 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
         if (u < U) {
             float xv[F::kUnitWeights];
             F::load_x(xs, u, xv);
+            // u indexes the (concatenated) x and its sums; the block-internal
+            // position only depends on u mod 4, the same inside each expert
 #pragma unroll
             for (int r = 0; r < R; r++) F::dot(src[r], xv, sums, u, inv_unit, acc[r]);
         }

@@ -126,8 +126,10 @@ qmv_status qmv_argmax(qmv_type t, const void *blocks, int64_t M, int64_t K, cons
  * y: f32[H].  topk_idx: int32[k] and topk_w: f32[k], in rank order.
  * workspace: device, >= qmv_workspace_bytes(QMV_OP_MOE, H, I, E, k) bytes,
  *   16-byte aligned.  Layout after the call (for inspection): f32 logits[E]
- *   at byte 0, then at byte 256: f32 g[k][I], u[k][I], h[k][I].
- * Constraints: 1 <= k <= E <= 64; H and I multiples of their formats' B. */
+ *   at byte 0; from byte 256 f32 gu[k][2I] (per slot: the I gate results,
+ *   then the I up results); then f32 h[k][I] = silu(g) * u.
+ * Constraints: 1 <= k <= E <= 64; H and I multiples of their formats' B;
+ *   k * I <= QMV_MAX_K; with a Q8_0 down projection, I a multiple of 128.  Three launches; the selection never leaves the GPU. */
 qmv_status moe_qmv_topk(const float *x, int64_t H, const float *router, const float *bias,
                         int32_t E, int32_t k, qmv_type gu_t, const void *gate_up,
                         qmv_type dn_t, const void *down, int64_t I, float *y,

@@ -87,3 +87,6 @@ def test_workspace_errors():
     assert status_of(q.moe_qmv_topk, *args, wm - 4) == "QMV_EWORKSPACE"
     bad_k = (A16, 2048, A16, A16, 32, 33, "q4_k", A16, "q6_k", A16, 1536, A16, A16, A16, A16)
     assert status_of(q.moe_qmv_topk, *bad_k, wm) == "QMV_ESHAPE"
+    w64 = q.qmv_workspace_bytes(q.OP_MOE, 256, 64, 4, 2)
+    bad_i = (A16, 256, A16, A16, 4, 2, "q8_0", A16, "q8_0", A16, 64, A16, A16, A16, A16)
+    assert status_of(q.moe_qmv_topk, *bad_i, w64) == "QMV_ESHAPE"
