@@ -106,6 +106,10 @@ size_t qmv_workspace_bytes(qmv_op op, int64_t a, int64_t b, int32_t c, int32_t d
         // logits[E] padded to 256 B, then gu[k][2I] and h[k][I] in f32
         return 256 + 3 * (size_t)d * (size_t)b * sizeof(float);
     }
+    if (op == QMV_OP_GEMM_N) {
+        if (a < 1 || b < 1) return 0;
+        return gemm_n_workspace(a, b);
+    }
     return 0;
 }
 
@@ -217,13 +221,17 @@ qmv_status moe_qmv_topk(const float *x, int64_t H, const float *router, const fl
 }
 
 qmv_status qmv_gemm_n(qmv_type t, const void *blocks, int64_t M, int64_t K, int32_t n,
-                      const float *X, float *Y, hipStream_t stream) {
+                      const float *X, float *Y, void *workspace, size_t ws_bytes,
+                      hipStream_t stream) {
     qmv_status st = check_matrix(t, blocks, M, K);
     if (st != QMV_OK) return st;
     if (n < 1 || n > QMV_MAX_N) return QMV_ESHAPE;
     if (!X || !Y) return QMV_EINVAL;
     if (!aligned(X, 16) || !aligned(Y, 4)) return QMV_EALIGN;
-    return from_hip(launch_gemm_n(t, (const uint8_t *)blocks, M, K, n, X, Y, stream));
+    const size_t need = gemm_n_workspace(M, K);
+    if (need > 0 && (!workspace || ws_bytes < need)) return QMV_EWORKSPACE;
+    if (need > 0 && !aligned(workspace, 16)) return QMV_EALIGN;
+    return from_hip(launch_gemm_n(t, (const uint8_t *)blocks, M, K, n, X, Y, workspace, stream));
 }
 
 qmv_status qmv_dequant(qmv_type t, const void *blocks, int64_t M, int64_t K, float *w_out,

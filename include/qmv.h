@@ -68,7 +68,7 @@ typedef enum {
 } qmv_status;
 
 /* Operations that need a workspace, for qmv_workspace_bytes(). */
-typedef enum { QMV_OP_ARGMAX = 1, QMV_OP_MOE = 2 } qmv_op;
+typedef enum { QMV_OP_ARGMAX = 1, QMV_OP_MOE = 2, QMV_OP_GEMM_N = 3 } qmv_op;
 
 /* Largest K (columns) any entry point accepts: x is staged whole in LDS. */
 #define QMV_MAX_K 32768
@@ -140,9 +140,15 @@ qmv_status moe_qmv_topk(const float *x, int64_t H, const float *router, const fl
  * FlareLLM page, section "推理层面的深度优化" (n-gram speculative decoding
  * checks several drafted tokens against the same weights).  X: f32 n x K
  * row-major, Y: f32 n x M row-major, 1 <= n <= QMV_MAX_N.  Runs on the matrix
- * cores; see the implementation notes for the accuracy bound. */
+ * cores (bf16 MFMA on the exact integer codes, X split into bf16 hi + lo, f32
+ * scales), within 1e-5 * sum_k |w_ik x_k| of the exact result like the
+ * matvecs.  workspace: device, >= qmv_workspace_bytes(QMV_OP_GEMM_N, M, K, n,
+ * 0) bytes (may be 0 bytes, then NULL is allowed), 16-byte aligned, no
+ * initial contents needed; K is split into slices whose partial sums are
+ * added in a fixed order, so results are deterministic. */
 qmv_status qmv_gemm_n(qmv_type t, const void *blocks, int64_t M, int64_t K, int32_t n,
-                      const float *X, float *Y, hipStream_t stream);
+                      const float *X, float *Y, void *workspace, size_t ws_bytes,
+                      hipStream_t stream);
 
 /* ---- dequantise to f32 (verification surface): w_out[M][K] --------------
  * Bit-exact block decoding, the values every matvec above is defined on. */
@@ -160,7 +166,8 @@ qmv_status qmv_quantize(qmv_type t, const float *w, int64_t M, int64_t K, void *
 /* ---- helpers -------------------------------------------------------------- */
 /* Bytes of one row of K weights in format t; 0 if K is not a multiple of B. */
 size_t qmv_row_bytes(qmv_type t, int64_t K);
-/* Workspace an operation needs.  ARGMAX: (M, K, -, -); MOE: (H, I, E, k). */
+/* Workspace an operation needs.  ARGMAX: (M, K, -, -); MOE: (H, I, E, k);
+ * GEMM_N: (M, K, n, -). */
 size_t qmv_workspace_bytes(qmv_op op, int64_t a, int64_t b, int32_t c, int32_t d);
 /* Raw HIP error code of this thread's last QMV_EHIP (0 if none). */
 int qmv_last_hip_error(void);

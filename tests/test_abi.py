@@ -57,8 +57,8 @@ def test_shape_errors():
     assert status_of(q.qmv_q6_k, A16, 4, 0, A16, A16) == "QMV_ESHAPE"
     assert status_of(q.qmv_q8_0, A16, 4, 48, A16, A16) == "QMV_ESHAPE"
     assert status_of(q.qmv_q8_0, A16, 4, q.MAX_K + 32, A16, A16) == "QMV_ESHAPE"
-    assert status_of(q.qmv_gemm_n, "q4_k", A16, 4, 256, 17, A16, A16) == "QMV_ESHAPE"
-    assert status_of(q.qmv_gemm_n, "q4_k", A16, 4, 256, 0, A16, A16) == "QMV_ESHAPE"
+    assert status_of(q.qmv_gemm_n, "q4_k", A16, 4, 256, 17, A16, A16, A16, 1 << 20) == "QMV_ESHAPE"
+    assert status_of(q.qmv_gemm_n, "q4_k", A16, 4, 256, 0, A16, A16, A16, 1 << 20) == "QMV_ESHAPE"
     assert status_of(q.qmv_fused_rows, "q4_k", A16, 256, A16, [4, 0], [A16, A16]) == "QMV_ESHAPE"
 
 
@@ -90,3 +90,7 @@ def test_workspace_errors():
     w64 = q.qmv_workspace_bytes(q.OP_MOE, 256, 64, 4, 2)
     bad_i = (A16, 256, A16, A16, 4, 2, "q8_0", A16, "q8_0", A16, 64, A16, A16, A16, A16)
     assert status_of(q.moe_qmv_topk, *bad_i, w64) == "QMV_ESHAPE"
+    wg = q.qmv_workspace_bytes(q.OP_GEMM_N, 4096, 4096, 16)
+    assert wg > 0
+    assert status_of(q.qmv_gemm_n, "q4_k", A16, 4096, 4096, 16, A16, A16, A16, wg - 4) == \
+        "QMV_EWORKSPACE"
