@@ -42,6 +42,45 @@ __device__ __forceinline__ uint32_t load2(const uint8_t *p) {
     return v;
 }
 
+// A raw buffer view of `bytes` bytes at `base` (base and size wave-uniform).
+// Loads take a per-lane byte offset and, past the end, return zeros without
+// touching memory (the hardware range check), so ragged tails need no clamps.
+// Every weight stream goes through these: one 32-bit offset per lane instead
+// of 64-bit address arithmetic per load.
+struct BufSrc {
+    __amdgpu_buffer_rsrc_t rsrc;
+    __device__ __forceinline__ BufSrc(const uint8_t *base, uint64_t bytes) {
+        const uint32_t n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)bytes;
+        rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), (short)0, (int)n,
+                                                 0x00020000);  // 32-bit data format (gfx9)
+    }
+    __device__ __forceinline__ uint4 ld16(uint32_t off) const {
+        return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0));
+    }
+    __device__ __forceinline__ uint2 ld8(uint32_t off) const {
+        return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rsrc, off, 0, 0));
+    }
+    __device__ __forceinline__ uint32_t ld4(uint32_t off) const {
+        return __builtin_amdgcn_raw_buffer_load_b32(rsrc, off, 0, 0);
+    }
+    __device__ __forceinline__ uint32_t ld2(uint32_t off) const {
+        return __builtin_amdgcn_raw_buffer_load_b16(rsrc, off, 0, 0);
+    }
+};
+
+// v with its lanes permuted by a DPP control (row-local patterns; VALU only).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;          // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;          // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;   // lane 7 - i within each 8
+constexpr int kDppMirror = 0x140;       // lane 15 - i within each 16
+constexpr int kDppBcast15 = 0x142;      // lane 15 of row r to row r + 1
+constexpr int kDppBcast31 = 0x143;      // lane 31 to rows 2 and 3
+
 // Byte b of a dword as an f32 integer value (v_cvt_f32_ubyteN).
 template <int B>
 __device__ __forceinline__ float ubyte(uint32_t v) {
@@ -67,13 +106,28 @@ __device__ __forceinline__ void nib4_to_f32_x512(uint32_t v, float &a, float &b,
     d = hi.y;
 }
 
-// Sum over groups of G consecutive lanes (G a power of two <= 64); every lane
-// of the group ends with the group total.  Butterfly order is fixed, so the
-// result does not depend on which rows the wave processes.
+// Sum over groups of G consecutive lanes (G a power of two, 4..64), with DPP
+// moves only (no LDS round trips).  The total is exact in lane G - 1 of each
+// group (the group's "owner"); for G <= 16 every lane of the group has it.
+// The order of the additions is fixed, so the result depends only on the
+// lane values.
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-    for (int o = G / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    static_assert(G == 4 || G == 8 || G == 16 || G == 32 || G == 64, "lane group");
+    v += dpp_f32<kDppXor1>(v);
+    v += dpp_f32<kDppXor2>(v);
+    if (G >= 8) v += dpp_f32<kDppHalfMirror>(v);
+    if (G >= 16) v += dpp_f32<kDppMirror>(v);
+    if (G >= 32) {
+        // rows 1 and 3 add the total of rows 0 and 2
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                           0, __builtin_bit_cast(int, v), kDppBcast15, 0xA, 0xF, false));
+    }
+    if (G == 64) {
+        // row 3 adds lane 31 (rows 0 + 1)
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                           0, __builtin_bit_cast(int, v), kDppBcast31, 0x8, 0xF, false));
+    }
     return v;
 }
 

@@ -4,7 +4,8 @@
 // (32 for Q8_0 rows with an odd number of blocks).  Lanes keep the same unit
 // position modulo 4 for a whole launch, so the sub-block they touch inside a
 // 256-weight super-block is lane-constant.  Each decoder
-//   - loads its unit's bytes straight from HBM with 128-bit loads (load),
+//   - loads its unit's bytes straight from HBM with 128-bit buffer loads
+//     (load; `off` is the byte offset of the unit's region, unit_offset),
 //   - reads the unit's 64 activations from LDS (load_x),
 //   - multiplies and adds into a per-lane f32 accumulator (dot), using the
 //     factored form  d*sc_j*sum(q*x) - dmin*m_j*sum(x)  so that the scales are
@@ -42,13 +43,15 @@ struct Q4K {
     struct Regs {
         uint4 hdr, q0, q1;
     };
-    __device__ static __forceinline__ Regs load(const uint8_t *row, int u) {
-        const uint8_t *blk = row + (size_t)(u >> 2) * kBlockBytes;
-        const int c = u & 3;
+    __device__ static __forceinline__ uint32_t unit_offset(int u) {
+        return (uint32_t)(u >> 2) * kBlockBytes;
+    }
+    __device__ static __forceinline__ Regs load(const BufSrc &src, uint32_t off, int u) {
+        const uint32_t c = u & 3;
         Regs r;
-        r.hdr = load16(blk);
-        r.q0 = load16(blk + 16 + 32 * c);
-        r.q1 = load16(blk + 32 + 32 * c);
+        r.hdr = src.ld16(off);
+        r.q0 = src.ld16(off + 16 + 32 * c);
+        r.q1 = src.ld16(off + 32 + 32 * c);
         return r;
     }
     // The unit's 64 activations: x[64u .. 64u+64), stored at 68u in the padded
@@ -121,15 +124,17 @@ struct Q6K {
         uint2 sc;
         uint32_t d;
     };
-    __device__ static __forceinline__ Regs load(const uint8_t *row, int u) {
-        const uint8_t *blk = row + (size_t)(u >> 2) * kBlockBytes;
-        const int n = (u >> 1) & 1, h = u & 1;
+    __device__ static __forceinline__ uint32_t unit_offset(int u) {
+        return (uint32_t)(u >> 2) * kBlockBytes;
+    }
+    __device__ static __forceinline__ Regs load(const BufSrc &src, uint32_t off, int u) {
+        const uint32_t n = (u >> 1) & 1, h = u & 1;
         Regs r;
-        r.qa = load16(blk + 64 * n + 16 * h);
-        r.qb = load16(blk + 64 * n + 32 + 16 * h);
-        r.qh = load16(blk + 128 + 32 * n + 16 * h);
-        r.sc = load8(blk + 192 + 8 * n);
-        r.d = load2(blk + 208);
+        r.qa = src.ld16(off + 64 * n + 16 * h);
+        r.qb = src.ld16(off + 64 * n + 32 + 16 * h);
+        r.qh = src.ld16(off + 128 + 32 * n + 16 * h);
+        r.sc = src.ld8(off + 192 + 8 * n);
+        r.d = src.ld2(off + 208);
         return r;
     }
     // Runs x[256b + 128n + 32g + 16h .. +16) for g = 0..3; in the padded LDS
@@ -203,14 +208,14 @@ struct Q80x2 {
         uint4 a, b, c, d;
         uint32_t e;
     };
-    __device__ static __forceinline__ Regs load(const uint8_t *row, int u) {
-        const uint8_t *p = row + (size_t)u * 68;
+    __device__ static __forceinline__ uint32_t unit_offset(int u) { return (uint32_t)u * 68; }
+    __device__ static __forceinline__ Regs load(const BufSrc &src, uint32_t off, int) {
         Regs r;
-        r.a = load16(p);
-        r.b = load16(p + 16);
-        r.c = load16(p + 32);
-        r.d = load16(p + 48);
-        r.e = load4(p + 64);
+        r.a = src.ld16(off);
+        r.b = src.ld16(off + 16);
+        r.c = src.ld16(off + 32);
+        r.d = src.ld16(off + 48);
+        r.e = src.ld4(off + 64);
         return r;
     }
     __device__ static __forceinline__ void load_x(const float *xs, int u, float *xv) {
@@ -260,12 +265,12 @@ struct Q80x1 {
         uint4 a, b;
         uint32_t c;
     };
-    __device__ static __forceinline__ Regs load(const uint8_t *row, int u) {
-        const uint8_t *p = row + (size_t)u * 34;
+    __device__ static __forceinline__ uint32_t unit_offset(int u) { return (uint32_t)u * 34; }
+    __device__ static __forceinline__ Regs load(const BufSrc &src, uint32_t off, int) {
         Regs r;
-        r.c = load2(p);
-        r.a = load16(p + 2);
-        r.b = load16(p + 18);
+        r.c = src.ld2(off);
+        r.a = src.ld16(off + 2);
+        r.b = src.ld16(off + 18);
         return r;
     }
     __device__ static __forceinline__ void load_x(const float *xs, int u, float *xv) {

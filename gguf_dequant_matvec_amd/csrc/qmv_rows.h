@@ -86,17 +86,19 @@ __host__ __device__ constexpr int lds_x_floats(int K) {
 
 // Store four consecutive activations (x[i..i+3]) into the padded LDS copy and
 // add their group sum: the kSumGroup/4 consecutive lanes that hold one group
-// combine with a shuffle butterfly, so the sums need no extra pass over LDS.
-// Every lane of the wave must call this (the shuffles span the group).
+// combine with DPP moves (VALU only, no LDS round trip), so the sums need no
+// extra pass over LDS.  Every lane of the wave must call this.
 template <class F>
 __device__ __forceinline__ void put_x4(float *xs, float *sums, int i, bool valid, float4 v) {
-    constexpr int kLanes = F::kSumGroup > 0 ? F::kSumGroup / 4 : 1;
     if (valid) *reinterpret_cast<float4 *>(xs + i + (i / F::kPadEvery) * 4) = v;
-    if (F::kSumGroup > 0) {
+    if constexpr (F::kSumGroup > 0) {
+        constexpr int kLanes = F::kSumGroup / 4;
+        static_assert(kLanes == 4 || kLanes == 8, "sum groups of 16 or 32 activations");
         float sum = (v.x + v.y) + (v.z + v.w);
-#pragma unroll
-        for (int o = 1; o < kLanes; o <<= 1) sum += __shfl_xor(sum, o, kWave);
-        if (valid && (threadIdx.x % kLanes) == 0) sums[i / (F::kSumGroup > 0 ? F::kSumGroup : 1)] = sum;
+        sum += dpp_f32<kDppXor1>(sum);
+        sum += dpp_f32<kDppXor2>(sum);
+        if (kLanes == 8) sum += dpp_f32<kDppHalfMirror>(sum);
+        if (valid && (threadIdx.x % kLanes) == 0) sums[i / F::kSumGroup] = sum;
     }
 }
 
@@ -181,34 +183,6 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
     __shared__ int32_t sel[kMoe ? kMaxExperts : 1];
     __shared__ float wsel[kMoe ? kMaxExperts : 1];
 
-    if (MODE == kModeMoeGateUp) {
-        moe_select(p.moe, sel, wsel);
-        stage_x<F>(p.x, p.K, xs, sums);  // its barrier also publishes sel
-    } else if (MODE == kModeMoeDown) {
-        if ((int)threadIdx.x < p.moe.k) {
-            sel[threadIdx.x] = p.moe.topk_idx[threadIdx.x];
-            wsel[threadIdx.x] = p.moe.topk_w[threadIdx.x];
-        }
-        __syncthreads();
-        // x[s*I + j] = w_s * silu(g_s[j]) * u_s[j]; workgroup 0 keeps h.
-        // K = k*I is a multiple of 32, so sum groups never straddle slots.
-        const int I = p.moe.I, K = p.K;
-        for (int base = threadIdx.x * 4; base < K; base += blockDim.x * 4) {
-            const int s = base / I, j = base - s * I;
-            const float4 g = *reinterpret_cast<const float4 *>(p.moe.gu + (int64_t)s * 2 * I + j);
-            const float4 u = *reinterpret_cast<const float4 *>(p.moe.gu + (int64_t)s * 2 * I + I + j);
-            const float4 h = make_float4(siluf(g.x) * u.x, siluf(g.y) * u.y, siluf(g.z) * u.z,
-                                         siluf(g.w) * u.w);
-            if (blockIdx.x == 0) *reinterpret_cast<float4 *>(p.moe.h + base) = h;
-            const float w = wsel[s];
-            put_x4<F>(xs, sums, base, true, make_float4(w * h.x, w * h.y, w * h.z, w * h.w));
-        }
-        __syncthreads();
-    } else {
-        stage_x<F>(p.x, p.K, xs, sums);
-    }
-
-    const float inv_unit = fp8_unit_inverse();
     const int lane = threadIdx.x & (kWave - 1);
     // wave-uniform values are forced into scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -220,11 +194,13 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
     constexpr int kRowsPerTile = R * P;
     const int ntiles = (p.M + kRowsPerTile - 1) / kRowsPerTile;
     const int tile_stride = (int)gridDim.x * waves_per_block;
+    const uint32_t rb = (uint32_t)p.row_bytes;
 
-    // row of slot r inside a tile, relative to the tile's first row
-    int rel[R];
+    // byte offset of row slot r inside a tile (rows of a tile are consecutive)
+    uint32_t row_off[R];
 #pragma unroll
-    for (int r = 0; r < R; r++) rel[r] = r * P + sub;
+    for (int r = 0; r < R; r++) row_off[r] = (uint32_t)(r * P + sub) * rb;
+    const uint32_t lane_uoff = F::unit_offset(g);
 
     float best_v = -__builtin_inff();
     int best_i = 0x7FFFFFFF;
@@ -241,42 +217,50 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
     // One work item = (tile, unit step).  Items are software-pipelined: the
     // next item's weight loads are in flight while the current one is
     // multiplied, with two register sets used in turn (no copies, so no wait).
-    // Tile bookkeeping is wave-uniform (scalar); a lane only adds its own row
-    // offset, clamped to the last row so the ragged tail stays in bounds.
+    // Tile bookkeeping is wave-uniform (scalar): each item reads through a
+    // buffer view that starts at the tile's first row and ends at the end of
+    // its matrix, so a lane only adds its own 32-bit offset, and rows past
+    // the end (the ragged tail) or units past the last row's end read zeros
+    // without touching memory.  Lanes whose unit lies past the row's end are
+    // skipped by the multiply.
     auto issue = [&](typename F::Regs(&dst)[R], int t, int it) {
         t = __builtin_amdgcn_readfirstlane(t);
         it = __builtin_amdgcn_readfirstlane(it);
-        int u = g + G * it;
-        u = u < U ? u : U - 1;
+        int ustep = G * it;
         const int r0 = t * kRowsPerTile;
-        const int last = (p.M - 1 - r0) < kRowsPerTile ? (p.M - 1 - r0) : kRowsPerTile;
-        const uint8_t *tile_base;
+        const uint8_t *base;
+        uint64_t avail;
         if (MODE == kModeMoeGateUp) {
             // the tile's rows belong to one selected expert
             const int slot = r0 / p.moe.rows_per_mat;
-            tile_base = p.W + (int64_t)sel[slot] * p.moe.mat_bytes +
-                        (int64_t)(r0 - slot * p.moe.rows_per_mat) * p.row_bytes;
+            const int rin = r0 - slot * p.moe.rows_per_mat;
+            base = p.W + (int64_t)sel[slot] * p.moe.mat_bytes + (int64_t)rin * rb;
+            avail = (uint64_t)(p.moe.rows_per_mat - rin) * rb;
         } else if (MODE == kModeMoeDown) {
             const int slot = step_slot(it);
-            u -= slot * p.moe.units_per_mat;
-            tile_base = p.W + (int64_t)sel[slot] * p.moe.mat_bytes + (int64_t)r0 * p.row_bytes;
+            ustep -= slot * p.moe.units_per_mat;
+            base = p.W + (int64_t)sel[slot] * p.moe.mat_bytes + (int64_t)r0 * rb;
+            avail = (uint64_t)(p.M - r0) * rb;
         } else {
-            tile_base = p.W + (int64_t)r0 * p.row_bytes;
+            base = p.W + (int64_t)r0 * rb;
+            avail = (uint64_t)(p.M - r0) * rb;
         }
+        const BufSrc src(base, avail);
+        // unit g + ustep: ustep is a multiple of 4, so the position inside a
+        // block only depends on g
+        const uint32_t uoff = lane_uoff + F::unit_offset(ustep);
 #pragma unroll
-        for (int r = 0; r < R; r++) {
-            const int rr = rel[r] < last ? rel[r] : last;
-            dst[r] = F::load(tile_base + (int64_t)rr * p.row_bytes, u);
-        }
+        for (int r = 0; r < R; r++) dst[r] = F::load(src, row_off[r] + uoff, g);
     };
     auto finish_tile = [&](int t) {
         t = __builtin_amdgcn_readfirstlane(t);
         float tot[R];
 #pragma unroll
         for (int r = 0; r < R; r++) {
-            tot[r] = group_sum<G>(acc[r]);
+            tot[r] = group_sum<G>(acc[r]);  // exact in the group's last lane
             acc[r] = 0.f;
         }
+        const bool owner = g == G - 1;
         const int r0 = t * kRowsPerTile;
         if (MODE != kModeArgmax) {
             // segment of the tile's first row and the start of the next one:
@@ -294,10 +278,10 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
                     }
                 }
             }
-            if (g == 0) {
+            if (owner) {
 #pragma unroll
                 for (int r = 0; r < R; r++) {
-                    const int row = r0 + rel[r];
+                    const int row = r0 + r * P + sub;
                     if (row >= p.M) continue;
                     if (row < next) {
                         yb[row - sb] = tot[r];
@@ -311,16 +295,16 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
         } else {
 #pragma unroll
             for (int r = 0; r < R; r++) {
-                const int row = r0 + rel[r];
+                const int row = r0 + r * P + sub;
                 const float v = tot[r] + 0.0f;
-                if (row < p.M && (v > best_v || (v == best_v && row < best_i))) {
+                if (owner && row < p.M && (v > best_v || (v == best_v && row < best_i))) {
                     best_v = v;
                     best_i = row;
                 }
             }
         }
     };
-    auto consume = [&](typename F::Regs(&src)[R], int t, int it) {
+    auto consume = [&](typename F::Regs(&src)[R], const float inv_unit, int t, int it) {
         t = __builtin_amdgcn_readfirstlane(t);
         it = __builtin_amdgcn_readfirstlane(it);
         const int u = g + G * it;
@@ -336,18 +320,51 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
     };
 
     // Items of this wave: tiles t_first, t_first + stride, ..., each with
-    // `iters` unit steps.  Both issues of an iteration are unconditional (past
-    // the end they repeat the last item's addresses, which hit in L2), so the
-    // compiler's wait counters never have to merge "maybe issued" states and
-    // each consume waits only for its own loads.
+    // `iters` unit steps.
     const int t_first = __builtin_amdgcn_readfirstlane((int)blockIdx.x * waves_per_block + wave);
     const int my_tiles = t_first < ntiles ? (ntiles - 1 - t_first) / tile_stride + 1 : 0;
     const int n_items = my_tiles * iters;
+    typename F::Regs bufA[R], bufB[R];
+    int tA = t_first;
+    int itA = 0;
+
+    if (MODE == kModeMoeGateUp) {
+        moe_select(p.moe, sel, wsel);
+        stage_x<F>(p.x, p.K, xs, sums);  // its barrier also publishes sel
+    } else if (MODE == kModeMoeDown) {
+        if ((int)threadIdx.x < p.moe.k) {
+            sel[threadIdx.x] = p.moe.topk_idx[threadIdx.x];
+            wsel[threadIdx.x] = p.moe.topk_w[threadIdx.x];
+        }
+        __syncthreads();
+        // x[s*I + j] = w_s * silu(g_s[j]) * u_s[j]; workgroup 0 keeps h.
+        // K = k*I is a multiple of 32, so sum groups never straddle slots.
+        const int I = p.moe.I, K = p.K;
+        for (int base = threadIdx.x * 4; base < K; base += blockDim.x * 4) {
+            const int s = base / I, j = base - s * I;
+            const float4 gg = *reinterpret_cast<const float4 *>(p.moe.gu + (int64_t)s * 2 * I + j);
+            const float4 uu = *reinterpret_cast<const float4 *>(p.moe.gu + (int64_t)s * 2 * I + I + j);
+            const float4 h = make_float4(siluf(gg.x) * uu.x, siluf(gg.y) * uu.y,
+                                         siluf(gg.z) * uu.z, siluf(gg.w) * uu.w);
+            if (blockIdx.x == 0) *reinterpret_cast<float4 *>(p.moe.h + base) = h;
+            const float w = wsel[s];
+            put_x4<F>(xs, sums, base, true, make_float4(w * h.x, w * h.y, w * h.z, w * h.w));
+        }
+        __syncthreads();
+    } else {
+        // the first item's weights are requested before x is staged, so the
+        // two latencies overlap
+        if (n_items > 0) issue(bufA, tA, itA);
+        stage_x<F>(p.x, p.K, xs, sums);
+    }
+    const float inv_unit = fp8_unit_inverse();
+
+    // Both issues of an iteration are unconditional (past the end they repeat
+    // the last item's addresses, which hit in L2), so the compiler's wait
+    // counters never have to merge "maybe issued" states and each consume
+    // waits only for its own loads.
     if (n_items > 0) {
-        typename F::Regs bufA[R], bufB[R];
-        int tA = t_first;
-        int itA = 0;
-        issue(bufA, tA, itA);
+        if (kMoe) issue(bufA, tA, itA);
         for (int k = 0; k < n_items; k += 2) {
             int tB = tA;
             int itB = itA;
@@ -356,7 +373,7 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
                 tB += tile_stride;
             }
             issue(bufB, tB, itB);
-            consume(bufA, tA, itA);
+            consume(bufA, inv_unit, tA, itA);
             int tC = tB;
             int itC = itB;
             if (k + 2 < n_items && ++itC == iters) {
@@ -364,7 +381,7 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
                 tC += tile_stride;
             }
             issue(bufA, tC, itC);
-            if (k + 1 < n_items) consume(bufB, tB, itB);
+            if (k + 1 < n_items) consume(bufB, inv_unit, tB, itB);
             tA = tC;
             itA = itC;
         }
