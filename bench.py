@@ -28,6 +28,48 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0    # MI355X HBM3E peak, 8 TB/s
 
+# The dominant kernel: the Q4_K row kernel instantiated for K = 4096 (64-lane
+# row groups, 2 row slots, store mode) -- the QKV, O and gate+up launches.
+DOMINANT = "rows_kernel<qmv::Q4K, 64, 2, 0>"
+DOMINANT_KINDS = ("qkv", "o", "gate_up")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "rows_kernel_q4k_k4096_decode_step_traffic.txt")
+PROBE_KERNEL = "probe_read"          # streaming-read probe: known bytes read
+CAL_WRITE_KERNEL = "dequant_q4_k"    # dequantisation of one 4096x4096 matrix: known bytes written
+PROBE_BYTES = 4 << 30
+
+
+def kernel_source_hash():
+    """SHA-256 over the HIP sources and the C header: a stored counter
+    measurement is only reported while the kernels it measured are unchanged."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gguf_dequant_matvec_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".h", ".hip", ".cpp")):
+            h.update(name.encode())
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(f.read())
+    with open(os.path.join(ROOT, "include", "qmv.h"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()
+
+
+def stored_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None when it is missing or was taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith(" "))
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -37,6 +79,10 @@ def parse():
     ap.add_argument("--seed", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--summarize", nargs="+", metavar="DIR",
+                    help="print a text summary of rocprofv3 output directories of this "
+                         "bench (kernel trace and/or FETCH_SIZE / WRITE_SIZE counter runs) "
+                         "and exit")
     return ap.parse_args()
 
 
@@ -71,6 +117,8 @@ class DecodeStep:
 
         self.layers = []
         for l in range(L):
+            if l % 8 == 0:
+                print(f"[bench] quantising layer {l}/{L}", file=sys.stderr, flush=True)
             self.layers.append(dict(
                 qkv=make("q4_k", sum(self.qkv_rows), H, 1, l),
                 o=make("q4_k", self.o_shape[0], self.o_shape[1], 2, l),
@@ -150,8 +198,65 @@ def cpu_baseline(seconds: float):
                 seconds=round(el, 2))
 
 
+def summarize(dirs):
+    """Text summary of rocprofv3 csv output of this bench: per-kernel durations
+    from a kernel trace, per-dispatch FETCH_SIZE / WRITE_SIZE from counter
+    runs, and the calibrated HBM traffic of the dominant kernel."""
+    import csv
+    import glob
+    trace, counters = [], []
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+            trace += list(csv.DictReader(open(f)))
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            counters += list(csv.DictReader(open(f)))
+
+    def short(name):
+        name = name.replace("void ", "").replace("qmv::", "").replace("(anonymous namespace)::", "")
+        return name.split("(")[0]
+
+    if trace:
+        per = {}
+        for r in trace:
+            per.setdefault(short(r["Kernel_Name"]), []).append(
+                int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        print("kernel trace: calls, mean / median / min / max duration (us), total (ms)")
+        for k, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+            v = sorted(v)
+            print(f"  {k[:72]:72s} {len(v):6d} {sum(v) / len(v) / 1e3:9.2f} {v[len(v) // 2] / 1e3:9.2f} "
+                  f"{v[0] / 1e3:9.2f} {v[-1] / 1e3:9.2f} {sum(v) / 1e6:9.3f}")
+        dom = sorted(per.get(short("void qmv::" + DOMINANT + "(qmv::RowsParams)"), []))
+        if dom:
+            print(f"dominant kernel {DOMINANT}: {len(dom)} dispatches, mean {sum(dom) / len(dom) / 1e3:.3f} us")
+    if counters:
+        vals = {}
+        for r in counters:
+            key = (short(r["Kernel_Name"]), r["Counter_Name"])
+            vals.setdefault(key, []).append(float(r["Counter_Value"]))
+        mean = {k: sum(v) / len(v) for k, v in vals.items()}
+        print("counters: kernel, counter, dispatches, mean per dispatch")
+        for (k, c), v in sorted(vals.items()):
+            print(f"  {k[:60]:60s} {c:12s} {len(v):6d} {sum(v) / len(v):14.1f}")
+        dom_name = short("void qmv::" + DOMINANT + "(qmv::RowsParams)")
+        probe = mean.get((PROBE_KERNEL, "FETCH_SIZE"))
+        wcal = mean.get((CAL_WRITE_KERNEL, "WRITE_SIZE"))
+        fd, wd = mean.get((dom_name, "FETCH_SIZE")), mean.get((dom_name, "WRITE_SIZE"))
+        if probe and wcal and fd is not None and wd is not None:
+            ff = PROBE_BYTES / probe
+            wf = 4096 * 4096 * 4 / wcal
+            print(f"fetch calibration: {PROBE_BYTES} B read by {PROBE_KERNEL} / {probe:.1f} = {ff:.2f} B per unit")
+            print(f"write calibration: {4096 * 4096 * 4} B written by {CAL_WRITE_KERNEL} / {wcal:.1f} = {wf:.2f} B per unit")
+            print(f"traffic_bytes_per_launch: {fd * ff + wd * wf:.0f}")
+            print(f"fetch_bytes_per_launch: {fd * ff:.0f}")
+            print(f"write_bytes_per_launch: {wd * wf:.0f}")
+            print(f"source_sha256: {kernel_source_hash()}")
+
+
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args.summarize)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the matvec shards by output rows; see the design notes)", file=sys.stderr)
@@ -160,8 +265,13 @@ def main():
     import gguf_dequant_matvec_amd as q
     import synth
 
+    def progress(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
     torch.cuda.set_device(0)
+    progress("building the decode-step weights on the GPU")
     step = DecodeStep(torch, q, synth, args.seed)
+    progress("weights ready")
     launches = step.launches()
     step_bytes = sum(b for _, _, _, b, _ in launches)
     stream = torch.cuda.current_stream()
@@ -183,6 +293,7 @@ def main():
     torch.cuda.synchronize()
     ms_step_eager = e0.elapsed_time(e1) / max(1, args.steps // 5)
 
+    progress("eager pass done; timing the graph-captured step")
     # headline: the step captured once as a HIP graph, replayed K times
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
@@ -198,6 +309,7 @@ def main():
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
 
+    progress(f"graph step {ms_step:.4f} ms; timing each launch")
     # per-launch kernel durations: each main kernel carries its own dispatch
     # start/end timestamps into an event pair (the library's timing hook)
     pairs = []
@@ -232,6 +344,7 @@ def main():
     dom_ms = sum(d["ms"] for d in dom) / sum(d["n"] for d in dom)
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
 
+    progress("per-launch timing done; streaming-read probe")
     # achievable streaming-read ceiling on this device (same 128-bit loads)
     probe_gbs = None
     try:
@@ -251,6 +364,14 @@ def main():
         del buf
     except Exception as exc:  # the probe is context only
         print(f"probe skipped: {exc}", file=sys.stderr)
+
+    # counter calibration for writes: one dequantisation of a 4096x4096 Q4_K
+    # matrix writes exactly 4096 * 4096 * 4 bytes (profiled runs divide the
+    # WRITE_SIZE counter by this)
+    cal = torch.empty(step.o_shape[0] * step.o_shape[1], device="cuda")
+    q.qmv_dequant("q4_k", step.layers[0]["o"], step.o_shape[0], step.o_shape[1], cal)
+    torch.cuda.synchronize()
+    del cal
 
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
     rec = {
@@ -287,11 +408,14 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "kernel": "rows_kernel<Q4K,64,2,store> (q4_k, K=4096: QKV, O, gate+up)",
+            "traffic": stored_traffic(),
+            "kernel": DOMINANT + " (q4_k, K=4096: QKV, O, gate+up launches)",
+            "algorithmic_bytes_per_launch": round(dom_bytes),
+            "us_per_launch": round(dom_ms * 1e3, 3),
         },
     }
     if not args.no_cpu_baseline:
+        progress("timing the CPU oracle")
         rec["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(rec))
 
