@@ -79,6 +79,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the per-configuration measurements beside the headline step")
     ap.add_argument("--summarize", nargs="+", metavar="DIR",
                     help="print a text summary of rocprofv3 output directories of this "
                          "bench (kernel trace and/or FETCH_SIZE / WRITE_SIZE counter runs) "
@@ -165,6 +167,166 @@ class DecodeStep:
                     lambda: q.qmv_argmax("q6_k", self.out, V, H, self.x_h, self.idx, self.mx,
                                          self.ws)))
         return out
+
+
+def graph_time_us(torch, fn_list, reps=10):
+    """Per-call average (us) of a list of library calls captured once as a HIP
+    graph and replayed `reps` times (warm-up replays first)."""
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        for fn in fn_list[:2]:
+            fn()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for fn in fn_list:
+            fn()
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        g.replay()
+    z.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(z) * 1e3 / (reps * len(fn_list))
+    del g
+    return us
+
+
+def extras(torch, q, synth, step, progress):
+    """The other configurations of the path, each cold in HBM: every timed
+    loop cycles through >= 1 GiB of distinct weight addresses (replicas), so
+    the 256 MiB last-level cache cannot serve them.  Rates are algorithmic
+    bytes (weights + x + y, only the selected experts for the MoE) over the
+    per-call time of a HIP graph of the calls."""
+    dev = "cuda"
+    out = {}
+    GiB = 1 << 30
+
+    def replicas(blocks, n):
+        return [blocks.clone() for _ in range(n)]
+
+    def make(t, M, K, tensor, seed):
+        w = synth.normal_device(seed, tensor, (M, K), synth.W_STD, dev)
+        b = torch.empty(M * q.row_bytes(t, K), dtype=torch.uint8, device=dev)
+        q.qmv_quantize(t, w, M, K, b)
+        del w
+        return b
+
+    def rec(us, nbytes, per="call", **kw):
+        return dict(per=per, us=round(us, 3), bytes=int(nbytes),
+                    gbs=round(nbytes / (us * 1e-6) / 1e9, 1),
+                    pct_of_peak=round(100 * nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1), **kw)
+
+    # single Q8_0 matvec, 1536 x 576
+    c = synth.CONFIG1
+    M, K = c["M"], c["K"]
+    b = make("q8_0", M, K, synth.T_W, 1)
+    n = GiB // b.numel() + 1
+    reps = replicas(b, n)
+    x = synth.normal_device(1, synth.T_X, (K,), 1.0, dev)
+    y = torch.empty(M, device=dev)
+    us = graph_time_us(torch, [lambda r=r: q.qmv_q8_0(r, M, K, x, y) for r in reps], reps=3)
+    out["q8_0_1536x576"] = rec(us, b.numel() + 4 * K + 4 * M, replicas=n)
+    del reps
+    progress("extras: q8_0 1536x576 done")
+
+    # Llama-3.2-1B-shaped layer: fused QKV, fused gate+up, down (Q4_K)
+    c = synth.CONFIG2
+    H, I = c["hidden"], c["down"][1]
+    qkv_rows, gu_rows = list(c["qkv"]), list(c["gate_up"])
+    mats = dict(qkv=make("q4_k", sum(qkv_rows), H, 1, 2), gu=make("q4_k", sum(gu_rows), H, 3, 2),
+                down=make("q4_k", c["down"][0], I, 4, 2))
+    layer_bytes = sum(v.numel() for v in mats.values())
+    n = GiB // layer_bytes + 1
+    layers = [{k: v.clone() for k, v in mats.items()} for _ in range(n)]
+    xh = synth.normal_device(2, synth.T_X, (H,), 1.0, dev)
+    xi = synth.normal_device(2, synth.T_XN, (I,), 1.0, dev)
+    yq = [torch.empty(m, device=dev) for m in qkv_rows]
+    yg = [torch.empty(m, device=dev) for m in gu_rows]
+    yd = torch.empty(c["down"][0], device=dev)
+    calls = []
+    for L in layers:
+        calls.append(lambda L=L: q.qmv_fused_rows("q4_k", L["qkv"], H, xh, qkv_rows, yq))
+        calls.append(lambda L=L: q.qmv_fused_rows("q4_k", L["gu"], H, xh, gu_rows, yg))
+        calls.append(lambda L=L: q.qmv_q4_k(L["down"], c["down"][0], I, xi, yd))
+    us = graph_time_us(torch, calls, reps=5) * 3      # per layer
+    io = 4 * (H + sum(qkv_rows)) + 4 * (H + sum(gu_rows)) + 4 * (I + c["down"][0])
+    out["llama1b_layer_q4_k"] = rec(us, layer_bytes + io, per="layer (3 calls)", replicas=n)
+    del layers, mats
+    progress("extras: 1B layer done")
+
+    # LFM2-style MoE FFN: 32 experts, top-4, Q4_K gate/up, Q6_K down
+    c = synth.CONFIG3
+    H, E, I, k = c["H"], c["E"], c["I"], c["k"]
+    gu = make(c["gu_type"], E * 2 * I, H, synth.T_GU, 3)
+    dn = make(c["dn_type"], E * H, I, synth.T_DOWN, 3)
+    n = GiB // (gu.numel() + dn.numel()) + 1
+    sets = [(gu.clone(), dn.clone()) for _ in range(n)]
+    R = synth.normal_device(3, synth.T_ROUTER, (E, H), 0.02, dev)
+    bias = synth.normal_device(3, synth.T_BIAS, (E,), synth.BIAS_STD, dev)
+    xs = [synth.normal_device(3, synth.T_X, (H,), 1.0, dev, layer=i) for i in range(n)]
+    y = torch.empty(H, device=dev)
+    idx = torch.empty(k, dtype=torch.int32, device=dev)
+    wk = torch.empty(k, device=dev)
+    ws = torch.empty(q.qmv_workspace_bytes(q.OP_MOE, H, I, E, k), dtype=torch.uint8, device=dev)
+    calls = [lambda i=i, S=S: q.moe_qmv_topk(xs[i], H, R, bias, E, k, c["gu_type"], S[0],
+                                             c["dn_type"], S[1], I, y, idx, wk, ws)
+             for i, S in enumerate(sets)]
+    us = graph_time_us(torch, calls, reps=5)
+    per_expert = (gu.numel() + dn.numel()) // E
+    nbytes = R.numel() * 4 + E * 4 + 4 * H + k * per_expert + 4 * H + 8 * k
+    out["moe_lfm2_top4"] = rec(us, nbytes, per="call (3 launches)", replicas=n)
+    del sets, gu, dn
+    progress("extras: MoE done")
+
+    # small-batch verify (n = 8, 16) over the decode-step weights
+    Hs, Is = step.H, step.I
+    mats = []
+    for lay in step.layers:
+        mats += [(lay["qkv"], sum(step.qkv_rows), Hs), (lay["o"], step.o_shape[0], Hs),
+                 (lay["gu"], sum(step.gu_rows), Hs), (lay["down"], step.down_shape[0], Is)]
+    wbytes = sum(m.numel() for m, _, _ in mats)
+    for nn in (8, 16):
+        Xh = synth.normal_device(5, synth.T_X, (nn, Hs), 1.0, dev)
+        Xi = synth.normal_device(5, synth.T_XN, (nn, Is), 1.0, dev)
+        Y = torch.empty(nn * sum(step.gu_rows), device=dev)
+        wsb = max(q.qmv_workspace_bytes(q.OP_GEMM_N, M_, K_, nn) for _, M_, K_ in mats)
+        wsn = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+        calls = [lambda m=m, M_=M_, K_=K_: q.qmv_gemm_n("q4_k", m, M_, K_, nn,
+                                                       Xh if K_ == Hs else Xi, Y, wsn)
+                 for m, M_, K_ in mats]
+        us = graph_time_us(torch, calls, reps=3) * len(calls)   # per 32-layer pass
+        io = sum(4 * nn * (K_ + M_) for _, M_, K_ in mats)
+        flops = sum(2 * nn * M_ * K_ for _, M_, K_ in mats)
+        r = rec(us, wbytes + io, per=f"32-layer pass ({len(calls)} calls)", n=nn)
+        r["tflops"] = round(flops / (us * 1e-6) / 1e12, 2)
+        r["tok_per_s"] = round(nn / (us * 1e-6), 1)
+        out[f"verify_n{nn}_32_layers_q4_k"] = r
+        del Y, wsn
+    progress("extras: verify done")
+
+    # Q6_K output projection as a plain matvec (logits written), and a
+    # supplementary cold Q8_0 stream at the decode-step scale
+    V = step.vocab
+    yv = torch.empty(V, device=dev)
+    us = graph_time_us(torch, [lambda: q.qmv_q6_k(step.out, V, Hs, step.x_h, yv)], reps=10)
+    out["q6_k_128000x4096_logits"] = rec(us, step.out.numel() + 4 * Hs + 4 * V)
+    M, K = 28672, 4096
+    b = make("q8_0", M, K, synth.T_W, 6)
+    n = GiB // b.numel() + 1
+    reps = replicas(b, n)
+    y = torch.empty(M, device=dev)
+    us = graph_time_us(torch, [lambda r=r: q.qmv_q8_0(r, M, K, step.x_h, y) for r in reps], reps=5)
+    out["q8_0_28672x4096_cold"] = rec(us, b.numel() + 4 * K + 4 * M, replicas=n)
+    del reps, b
+    progress("extras: cold streams done")
+    return out
 
 
 def cpu_baseline(seconds: float):
@@ -414,6 +576,8 @@ def main():
             "us_per_launch": round(dom_ms * 1e3, 3),
         },
     }
+    if not args.no_extras:
+        rec["extras"] = extras(torch, q, synth, step, progress)
     if not args.no_cpu_baseline:
         progress("timing the CPU oracle")
         rec["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

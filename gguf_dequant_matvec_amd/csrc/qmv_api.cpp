@@ -107,8 +107,8 @@ size_t qmv_workspace_bytes(qmv_op op, int64_t a, int64_t b, int32_t c, int32_t d
         return 256 + 3 * (size_t)d * (size_t)b * sizeof(float);
     }
     if (op == QMV_OP_GEMM_N) {
-        if (a < 1 || b < 1) return 0;
-        return gemm_n_workspace(a, b);
+        if (a < 1 || b < 1 || c < 1 || c > QMV_MAX_N) return 0;
+        return gemm_n_workspace(a, b, c);
     }
     return 0;
 }
@@ -228,7 +228,7 @@ qmv_status qmv_gemm_n(qmv_type t, const void *blocks, int64_t M, int64_t K, int3
     if (n < 1 || n > QMV_MAX_N) return QMV_ESHAPE;
     if (!X || !Y) return QMV_EINVAL;
     if (!aligned(X, 16) || !aligned(Y, 4)) return QMV_EALIGN;
-    const size_t need = gemm_n_workspace(M, K);
+    const size_t need = gemm_n_workspace(M, K, n);
     if (need > 0 && (!workspace || ws_bytes < need)) return QMV_EWORKSPACE;
     if (need > 0 && !aligned(workspace, 16)) return QMV_EALIGN;
     return from_hip(launch_gemm_n(t, (const uint8_t *)blocks, M, K, n, X, Y, workspace, stream));

@@ -16,44 +16,56 @@
 //   v_mfma_f32_16x16x16_bf16 (Q6_K: one 16-weight sub-block); lane l of wave
 //   supplies A[l%16][kpl*(l/16) + t], B[kpl*(l/16) + t][l%16] and holds
 //   C[4*(l/16) + i][l%16].
-// Work split: a workgroup = 4 waves x 16 rows and a K-slice of KS
-// super-blocks (256 weights); X for the slice is staged once in LDS in the
-// operand layout.  Slices > 1 write partial sums to the workspace and a second
-// kernel adds them in slice order (deterministic, no atomics).
+//
+// Work split: a workgroup of 8 waves owns 128 rows (16 per wave, one MFMA
+// tile) and one K-slice of KW windows of 256 weights (KW = 1, 2 or 4, chosen
+// so that there are enough workgroups).  Each wave issues the loads of all
+// its windows at once, then the workgroup stages X for the slice once in LDS
+// (bf16 hi/lo in the MFMA operand layout plus per-sub-block sums), so the
+// staging is shared by 128 rows.  With more than one slice, each writes its
+// partial sums to the workspace and a second kernel adds them in slice order
+// (deterministic, no atomics).
 #include "qmv_device.h"
 #include "qmv_internal.h"
+
+#include <type_traits>
 
 namespace qmv {
 
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kTok = 16;          // MFMA M side: tokens, n padded to 16
-constexpr int kMaxSlicesSB = 4;   // super-blocks per K-slice at most (LDS budget)
+constexpr int kTok = 16;                 // MFMA M side: tokens, n padded to 16
+constexpr int kWin = 256;                // weights per window (one super-block)
 constexpr uint32_t kB16 = 0x43004300u;  // bf16 128.0 in both halves
 
 struct GemmParams {
     const uint8_t *W;
     int32_t M, K, n;
-    int64_t row_bytes;
+    int32_t row_bytes;
     const float *X;
-    float *Y;         // final output (one slice) ...
-    float *partial;   // ... or [slices][kTok][M] partial sums
-    int32_t ks;       // super-blocks per slice
+    float *Y;          // final output (one slice) ...
+    float *partial;    // ... or [slices][n][M] partial sums
+    int32_t row_groups;
     int32_t slices;
 };
 
+constexpr int kThreads = 512;  // 8 waves
+constexpr int kRowsPerWG = 128;
+
 // ---------------------------------------------------------------------------
 // Format policies.  kSub: weights per MFMA sub-block (= MFMA K); kNSub:
-// sub-blocks per 256-weight super-block; kKpl: operand values per lane.
-// slot(i): where weight i (0..255) of a super-block sits in the operand
-// layout, as (sub-block j, lane group q, slot t).
+// sub-blocks per 256-weight window; kKpl: operand values per lane.
+// slot(i): where weight i (0..255) of a window sits in the operand layout, as
+// (sub-block j, lane group q, slot t).  load(src, off, q, nvalid): the bytes
+// lane group q needs from the window starting `off` bytes into the view.
 // ---------------------------------------------------------------------------
 struct GQ4K {
-    static constexpr int kSub = 32, kNSub = 8, kKpl = 8, kBlockBytes = 144;
+    static constexpr int kSub = 32, kNSub = 8, kKpl = 8, kWinBytes = 144;
     struct Regs {
         uint4 hdr;
         uint2 piece[4];  // nibble bytes 32c + 8q .. +8, c = 0..3
@@ -61,18 +73,17 @@ struct GQ4K {
     // k-slot t of lane group q in sub-block 2c + h is nibble h of byte
     // 8q + pi(t) of chunk c, pi = (0 2 1 3 4 6 5 7): the order in which two
     // and-or operations pull nibble pairs out of a dword.
-    __device__ static void slot(int i, int &j, int &q, int &t) {
+    __device__ static constexpr int perm(int b) { return (b & 4) | ((b & 1) << 1) | ((b & 2) >> 1); }
+    __device__ static void slot(int i, int &j, int &q) {
         const int c = i / 64, h = (i % 64) / 32, l = i % 32;
         j = 2 * c + h;
         q = l / 8;
-        const int b = l % 8;
-        t = (b & 4) | ((b & 1) << 1) | ((b & 2) >> 1);
     }
-    __device__ static Regs load(const uint8_t *blk, int q) {
+    __device__ static Regs load(const BufSrc &src, uint32_t off, int q, int) {
         Regs r;
-        r.hdr = load16(blk);
+        r.hdr = src.ld16(off);
 #pragma unroll
-        for (int c = 0; c < 4; c++) r.piece[c] = load8(blk + 16 + 32 * c + 8 * q);
+        for (int c = 0; c < 4; c++) r.piece[c] = src.ld8(off + 16 + 32 * c + 8 * q);
         return r;
     }
     __device__ static bf16x8 codes(const Regs &r, int j) {
@@ -85,16 +96,20 @@ struct GQ4K {
         d[3] = ((p.y >> (sh + 8)) & 0x000F000Fu) | kB16;
         return __builtin_bit_cast(bf16x8, d);
     }
-    // y += scale * C - corr * sum(x): w = d*sc*q - dmin*m and the codes are q + 128
+    // y += scale * C - corr * sum(x): w = d*sc*q - dmin*m and the codes are q + 128.
+    // Scale bytes: sub-blocks 0-3 take the low 6 bits of bytes 4-7 (scale)
+    // and 8-11 (min); 4-7 the low / high nibble of bytes 12-15 plus the top
+    // two bits of bytes 4-7 / 8-11.
     __device__ static void scales(const Regs &r, int j, float &scale, float &corr) {
-        const uint8_t *S = reinterpret_cast<const uint8_t *>(&r.hdr) + 4;
+        const uint32_t s0 = r.hdr.y, s1 = r.hdr.z, s2 = r.hdr.w;
+        const int sh = 8 * (j & 3);
         int sc, m;
         if (j < 4) {
-            sc = S[j] & 63;
-            m = S[j + 4] & 63;
+            sc = (s0 >> sh) & 63;
+            m = (s1 >> sh) & 63;
         } else {
-            sc = (S[j + 4] & 15) | ((S[j - 4] >> 6) << 4);
-            m = (S[j + 4] >> 4) | ((S[j] >> 6) << 4);
+            sc = ((s2 >> sh) & 15) | ((((s0 >> sh) >> 6) & 3) << 4);
+            m = (((s2 >> sh) >> 4) & 15) | ((((s1 >> sh) >> 6) & 3) << 4);
         }
         const float d = half_bits_to_float(r.hdr.x), dmin = half_bits_to_float(r.hdr.x >> 16);
         scale = d * (float)sc;
@@ -103,7 +118,7 @@ struct GQ4K {
 };
 
 struct GQ6K {
-    static constexpr int kSub = 16, kNSub = 16, kKpl = 4, kBlockBytes = 210;
+    static constexpr int kSub = 16, kNSub = 16, kKpl = 4, kWinBytes = 210;
     struct Regs {
         uint32_t ql[2][2][2];  // [n][g&1][hh]: QL bytes 64n + 32(g&1) + 16hh + 4q .. +4
         uint32_t qh[2][2];     // [n][hh]: QH bytes 32n + 16hh + 4q .. +4
@@ -111,26 +126,27 @@ struct GQ6K {
         uint32_t d;
     };
     // weight i = 128n + 32g + 16hh + 4q + t, sub-block j = 8n + 2g + hh
-    __device__ static void slot(int i, int &j, int &q, int &t) {
+    __device__ static constexpr int perm(int b) { return b; }
+    __device__ static void slot(int i, int &j, int &q) {
         const int n = i / 128, g = (i % 128) / 32, l = i % 32, hh = l / 16;
         j = 8 * n + 2 * g + hh;
         q = (l % 16) / 4;
-        t = l % 4;
     }
-    __device__ static Regs load(const uint8_t *blk, int q) {
+    __device__ static Regs load(const BufSrc &src, uint32_t off, int q, int) {
         Regs r;
 #pragma unroll
         for (int n = 0; n < 2; n++)
 #pragma unroll
             for (int a = 0; a < 2; a++)
 #pragma unroll
-                for (int hh = 0; hh < 2; hh++) r.ql[n][a][hh] = load4(blk + 64 * n + 32 * a + 16 * hh + 4 * q);
+                for (int hh = 0; hh < 2; hh++)
+                    r.ql[n][a][hh] = src.ld4(off + 64 * n + 32 * a + 16 * hh + 4 * q);
 #pragma unroll
         for (int n = 0; n < 2; n++)
 #pragma unroll
-            for (int hh = 0; hh < 2; hh++) r.qh[n][hh] = load4(blk + 128 + 32 * n + 16 * hh + 4 * q);
-        r.sc = load16(blk + 192);
-        r.d = load2(blk + 208);
+            for (int hh = 0; hh < 2; hh++) r.qh[n][hh] = src.ld4(off + 128 + 32 * n + 16 * hh + 4 * q);
+        r.sc = src.ld16(off + 192);
+        r.d = src.ld2(off + 208);
         return r;
     }
     __device__ static s16x4 codes(const Regs &r, int j) {
@@ -145,32 +161,32 @@ struct GQ6K {
     }
     // w = d*sc*(u - 32) and the codes are u + 128: y += d*sc*C - 160*d*sc*sum(x)
     __device__ static void scales(const Regs &r, int j, float &scale, float &corr) {
-        const int8_t sc = reinterpret_cast<const int8_t *>(&r.sc)[j];
-        scale = half_bits_to_float(r.d) * (float)sc;
+        const uint32_t w = j < 4 ? r.sc.x : j < 8 ? r.sc.y : j < 12 ? r.sc.z : r.sc.w;
+        scale = half_bits_to_float(r.d) * (float)(int32_t)(int8_t)((w >> (8 * (j & 3))) & 0xFFu);
         corr = 160.0f * scale;
     }
 };
 
 struct GQ80 {
-    // a "super-block" is 8 consecutive Q8_0 blocks; block j is sub-block j
-    static constexpr int kSub = 32, kNSub = 8, kKpl = 8, kBlockBytes = 34;
+    // a window is 8 consecutive Q8_0 blocks; block j is sub-block j
+    static constexpr int kSub = 32, kNSub = 8, kKpl = 8, kWinBytes = 272;
     struct Regs {
         uint2 q[8];
         uint32_t d[8];
     };
-    __device__ static void slot(int i, int &j, int &q, int &t) {
+    __device__ static constexpr int perm(int b) { return b; }
+    __device__ static void slot(int i, int &j, int &q) {
         j = i / 32;
         q = (i % 32) / 8;
-        t = i % 8;
     }
-    // blk points at the first of the 8 blocks; nvalid of them exist
-    __device__ static Regs load(const uint8_t *blk, int q, int nvalid) {
+    // nvalid of the window's 8 blocks exist (the rest repeat the last one)
+    __device__ static Regs load(const BufSrc &src, uint32_t off, int q, int nvalid) {
         Regs r;
 #pragma unroll
         for (int b = 0; b < 8; b++) {
-            const uint8_t *p = blk + 34 * (b < nvalid ? b : nvalid - 1);
-            r.d[b] = load2(p);
-            r.q[b] = load8(p + 2 + 8 * q);
+            const uint32_t p = off + 34 * (b < nvalid ? b : nvalid - 1);
+            r.d[b] = src.ld2(p);
+            r.q[b] = src.ld8(p + 2 + 8 * q);
         }
         return r;
     }
@@ -196,166 +212,243 @@ struct GQ80 {
 };
 
 template <class F>
-__device__ __forceinline__ typename F::Regs load_sb(const uint8_t *row, int sb, int q, int nblocks) {
-    if constexpr (std::is_same<F, GQ80>::value) {
-        const int b0 = sb * 8;
-        return F::load(row + (int64_t)b0 * 34, q, nblocks - b0 < 8 ? nblocks - b0 : 8);
-    } else {
-        return F::load(row + (int64_t)sb * F::kBlockBytes, q);
-    }
-}
+using Frag = typename std::conditional<F::kKpl == 8, bf16x8, s16x4>::type;
+template <class F>
+using BFrag = typename std::conditional<F::kKpl == 8, bf16x8, bf16x4>::type;
 
 template <class F>
-__device__ __forceinline__ f32x4 mfma(const typename std::conditional<F::kKpl == 8, bf16x8, s16x4>::type &a,
-                                      const typename std::conditional<F::kKpl == 8, bf16x8, s16x4>::type &b,
-                                      f32x4 c) {
+__device__ __forceinline__ f32x4 mfma(const Frag<F> &a, const Frag<F> &b, f32x4 c) {
     if constexpr (F::kKpl == 8)
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     else
         return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
+// LDS per window buffer and part: hi and lo fragments [j][q][token][kKpl]
+// bf16 (8 KB each), then the per-(j, token) sums of hi + lo.
 template <class F>
-__global__ __launch_bounds__(256) void gemm_n_kernel(GemmParams p) {
-    using Frag = typename std::conditional<F::kKpl == 8, bf16x8, s16x4>::type;
-    // LDS: X fragments for the slice, hi and lo, [sb][j][q][token] x kKpl
-    // bf16, then the per-(sb, j, token) sums of hi + lo.
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    const int frag_vals = p.ks * F::kNSub * 4 * kTok * F::kKpl;
-    __bf16 *xhi = reinterpret_cast<__bf16 *>(smem);
-    __bf16 *xlo = xhi + frag_vals;
-    float *xs = reinterpret_cast<float *>(xlo + frag_vals);
+struct WinLayout {
+    static constexpr int kVals = F::kNSub * 4 * kTok * F::kKpl;  // = 16 * 256
+    static constexpr int kBytes = kVals * 2 * 2 + F::kNSub * kTok * 4;
+};
 
-    const int row_blocks = (p.M + 63) / 64;
-    const int rb = blockIdx.x % row_blocks;
-    const int slice = blockIdx.x / row_blocks;
-    const int k0 = slice * p.ks * 256;  // first weight of the slice
-    const int nw = p.ks * 256;          // weights of the slice (some may lie past K)
+template <class F>
+size_t gemm_lds_bytes(int KW) {
+    return (size_t)KW * WinLayout<F>::kBytes;
+}
 
-    // --- stage X[0..16)[k0 .. k0 + nw) ------------------------------------
-    for (int idx = threadIdx.x; idx < kTok * nw; idx += 256) {
-        const int t = idx / nw, kk = idx - t * nw, k = k0 + kk;
-        const float v = (t < p.n && k < p.K) ? p.X[(int64_t)t * p.K + k] : 0.f;
-        const __bf16 hi = (__bf16)v;
-        const __bf16 lo = (__bf16)(v - (float)hi);
-        const int sb = kk / 256;
-        int j, q, s;
-        F::slot(kk % 256, j, q, s);
-        const int pos = (((sb * F::kNSub + j) * 4 + q) * kTok + t) * F::kKpl + s;
-        xhi[pos] = hi;
-        xlo[pos] = lo;
-        // sum of the represented value over the sub-block: kSub consecutive
-        // indices of one token, i.e. kSub consecutive threads
-        float sum = (float)hi + (float)lo;
+// X staging for the KW windows of a slice, in two halves: load reads the f32
+// activations into registers (unconditional loads through a view of
+// X[0..n): tokens past n read zeros, so no branch waits for the data),
+// store splits them into bf16 hi + lo, writes them in the operand layout and
+// adds the per-sub-block sums.  A lane takes kKpl consecutive activations of
+// one token, so the four groups of a sub-block sit in four consecutive lanes
+// and their sum is a quad DPP reduction.
+template <class F, int KW>
+struct XStage {
+    static constexpr int kPerTok = kWin / F::kKpl;  // groups per token
+    static constexpr int kGroups = kTok * kPerTok;  // per window
+    static constexpr int kIters = KW * kGroups / kThreads;
+    static_assert(KW * kGroups % kThreads == 0, "whole iterations");
+    static_assert(F::kSub / F::kKpl == 4, "four groups per sub-block");
+    float v[kIters][F::kKpl];
+    int kpos[kIters];
+
+    __device__ __forceinline__ void load(const GemmParams &p, const BufSrc &xv, int wfirst) {
 #pragma unroll
-        for (int o = 1; o < F::kSub; o <<= 1) sum += __shfl_xor(sum, o, 64);
-        if ((kk % F::kSub) == 0) xs[(sb * F::kNSub + j) * kTok + t] = sum;
+        for (int it = 0; it < kIters; it++) {
+            const int gi = (int)threadIdx.x + kThreads * it;
+            const int win = gi / kGroups, gg = gi % kGroups;
+            const int t = gg / kPerTok, g = gg % kPerTok;
+            const int k = (wfirst + win) * kWin + g * F::kKpl;
+            const uint32_t off = ((uint32_t)t * (uint32_t)p.K + (uint32_t)k) * 4u;
+#pragma unroll
+            for (int e = 0; e < F::kKpl / 4; e++) {
+                const uint4 a = xv.ld16(off + 16 * e);
+                v[it][4 * e] = __builtin_bit_cast(float, a.x);
+                v[it][4 * e + 1] = __builtin_bit_cast(float, a.y);
+                v[it][4 * e + 2] = __builtin_bit_cast(float, a.z);
+                v[it][4 * e + 3] = __builtin_bit_cast(float, a.w);
+            }
+            kpos[it] = k;
+        }
+    }
+
+    // activations past K (the slice's or a last partial Q8_0 window) are zeroed
+    __device__ __forceinline__ void store(uint8_t *smem, int K) const {
+        using L = WinLayout<F>;
+#pragma unroll
+        for (int it = 0; it < kIters; it++) {
+            const int gi = (int)threadIdx.x + kThreads * it;
+            const int win = gi / kGroups, gg = gi % kGroups;
+            const int t = gg / kPerTok, g = gg % kPerTok;
+            const bool in_k = kpos[it] < K;  // K is a multiple of the group size
+            BFrag<F> hi, lo;
+            float sum = 0.f;
+#pragma unroll
+            for (int e = 0; e < F::kKpl; e++) {
+                const float x = in_k ? v[it][e] : 0.f;
+                const __bf16 h = (__bf16)x;
+                const __bf16 l = (__bf16)(x - (float)h);
+                hi[F::perm(e)] = h;
+                lo[F::perm(e)] = l;
+                sum += (float)h + (float)l;
+            }
+            int j, q;
+            F::slot(g * F::kKpl, j, q);
+            uint8_t *base = smem + (size_t)win * L::kBytes;
+            const int pos = ((j * 4 + q) * kTok + t) * F::kKpl;
+            *reinterpret_cast<BFrag<F> *>(base + 2 * pos) = hi;
+            *reinterpret_cast<BFrag<F> *>(base + 2 * (L::kVals + pos)) = lo;
+            sum += dpp_f32<kDppXor1>(sum);
+            sum += dpp_f32<kDppXor2>(sum);
+            if ((g & 3) == 0) reinterpret_cast<float *>(base + 4 * L::kVals)[j * kTok + t] = sum;
+        }
+    }
+};
+
+template <class F, int KW>
+__global__ __launch_bounds__(kThreads) void gemm_n_kernel(GemmParams p) {
+    using L = WinLayout<F>;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int r = lane & 15, q = lane >> 4;
+    const int rg = (int)blockIdx.x % p.row_groups, slice = (int)blockIdx.x / p.row_groups;
+    const int row0 = __builtin_amdgcn_readfirstlane(rg * kRowsPerWG + wave * 16);
+    const int nblocks = p.K / 32;                // Q8_0 blocks per row (last window)
+    const int wtotal = (p.K + kWin - 1) / kWin;  // windows in a row
+    const int wfirst = slice * KW;
+
+    // view from this wave's first row to the end of the matrix: rows past M
+    // read zeros
+    const int rows_left = p.M - row0 > 0 ? p.M - row0 : 0;
+    const BufSrc src(p.W + (int64_t)row0 * p.row_bytes,
+                     (uint64_t)rows_left * (uint64_t)(uint32_t)p.row_bytes);
+    const uint32_t lane_off = (uint32_t)r * (uint32_t)p.row_bytes;
+
+    auto nvalid_of = [&](int wi) {
+        if constexpr (std::is_same<F, GQ80>::value) {
+            const int left = nblocks - wi * 8;
+            return left < 8 ? left : 8;
+        } else {
+            return F::kNSub;
+        }
+    };
+
+    // every window's weights in flight at once (windows past the row's end
+    // repeat the last one and are skipped below)
+    typename F::Regs wr[KW];
+#pragma unroll
+    for (int i = 0; i < KW; i++) {
+        int wi = wfirst + i < wtotal ? wfirst + i : wtotal - 1;
+        wi = __builtin_amdgcn_readfirstlane(wi);
+        wr[i] = F::load(src, lane_off + (uint32_t)wi * F::kWinBytes, q, nvalid_of(wi));
+    }
+    {
+        const BufSrc xview(reinterpret_cast<const uint8_t *>(p.X),
+                           (uint64_t)p.n * (uint32_t)p.K * 4u);
+        XStage<F, KW> xs;
+        xs.load(p, xview, wfirst);
+        xs.store(smem, p.K);
     }
     __syncthreads();
 
-    // --- stream this wave's 16 rows over the slice -------------------------
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int r = lane & 15, q = lane >> 4;
-    const int row = rb * 64 + wave * 16 + r;
-    const int rowc = row < p.M ? row : p.M - 1;
-    const uint8_t *wrow = p.W + (int64_t)rowc * p.row_bytes;
-    const int nblocks = p.K / (std::is_same<F, GQ80>::value ? 32 : 256);
-    const int sb_total = (p.K + 255) / 256;
-    const int sb0 = slice * p.ks;
-    const int sb1 = (sb0 + p.ks < sb_total) ? sb0 + p.ks : sb_total;
-
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (sb0 < sb1) {
-        typename F::Regs cur = load_sb<F>(wrow, sb0, q, nblocks);
-        for (int sb = sb0; sb < sb1; sb++) {
-            // prefetch the next super-block (repeats the last one at the end)
-            const typename F::Regs nxt = load_sb<F>(wrow, sb + 1 < sb1 ? sb + 1 : sb, q, nblocks);
-            const int lsb = sb - sb0;
-            const int nsub = std::is_same<F, GQ80>::value
-                                 ? ((nblocks - sb * 8) < 8 ? (nblocks - sb * 8) : 8)
-                                 : F::kNSub;
 #pragma unroll
-            for (int j = 0; j < F::kNSub; j++) {
-                if (j >= nsub) break;
-                const int base = ((lsb * F::kNSub + j) * 4 + q) * kTok + r;
-                const Frag ah = *reinterpret_cast<const Frag *>(xhi + base * F::kKpl);
-                const Frag al = *reinterpret_cast<const Frag *>(xlo + base * F::kKpl);
-                const auto b = F::codes(cur, j);
-                f32x4 c = {0.f, 0.f, 0.f, 0.f};
-                c = mfma<F>(ah, b, c);
-                c = mfma<F>(al, b, c);
-                float scale, corr;
-                F::scales(cur, j, scale, corr);
-                const float4 sx = *reinterpret_cast<const float4 *>(xs + (lsb * F::kNSub + j) * kTok + 4 * q);
-                acc[0] = fmaf(scale, c[0], fmaf(-corr, sx.x, acc[0]));
-                acc[1] = fmaf(scale, c[1], fmaf(-corr, sx.y, acc[1]));
-                acc[2] = fmaf(scale, c[2], fmaf(-corr, sx.z, acc[2]));
-                acc[3] = fmaf(scale, c[3], fmaf(-corr, sx.w, acc[3]));
-            }
-            cur = nxt;
+    for (int i = 0; i < KW; i++) {
+        const int wi = wfirst + i;
+        if (wi >= wtotal) break;
+        const uint8_t *base = smem + (size_t)i * L::kBytes;
+        const __bf16 *xhi = reinterpret_cast<const __bf16 *>(base);
+        const __bf16 *xlo = xhi + L::kVals;
+        const float *xs = reinterpret_cast<const float *>(base + 4 * L::kVals);
+        const int nsub = nvalid_of(wi);
+#pragma unroll
+        for (int j = 0; j < F::kNSub; j++) {
+            if (j >= nsub) break;
+            const int fo = ((j * 4 + q) * kTok + r) * F::kKpl;
+            const Frag<F> ah = *reinterpret_cast<const Frag<F> *>(xhi + fo);
+            const Frag<F> al = *reinterpret_cast<const Frag<F> *>(xlo + fo);
+            const Frag<F> b = F::codes(wr[i], j);
+            f32x4 c = {0.f, 0.f, 0.f, 0.f};
+            c = mfma<F>(ah, b, c);
+            c = mfma<F>(al, b, c);
+            float scale, corr;
+            F::scales(wr[i], j, scale, corr);
+            const float4 sx = *reinterpret_cast<const float4 *>(xs + j * kTok + 4 * q);
+            acc[0] = fmaf(scale, c[0], fmaf(-corr, sx.x, acc[0]));
+            acc[1] = fmaf(scale, c[1], fmaf(-corr, sx.y, acc[1]));
+            acc[2] = fmaf(scale, c[2], fmaf(-corr, sx.z, acc[2]));
+            acc[3] = fmaf(scale, c[3], fmaf(-corr, sx.w, acc[3]));
         }
     }
 
-    // --- tokens 4q .. 4q+3 of this lane's row --------------------------------
+    // tokens 4q .. 4q+3 of this lane's row
+    const int row = row0 + r;
     if (row < p.M) {
+        float *out = p.slices == 1 ? p.Y : p.partial + (int64_t)slice * p.n * p.M;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int t = 4 * q + i;
-            if (p.slices == 1) {
-                if (t < p.n) p.Y[(int64_t)t * p.M + row] = acc[i];
-            } else {
-                p.partial[((int64_t)slice * kTok + t) * p.M + row] = acc[i];
-            }
+            if (t < p.n) out[(int64_t)t * p.M + row] = acc[i];
         }
     }
 }
 
-// Y[t][i] = sum over slices, in slice order.
-__global__ __launch_bounds__(256) void gemm_n_reduce(const float *partial, int slices, int M,
-                                                     int n, float *Y) {
+// Y[t][i] = sum over slices of the partial sums, in slice order.
+__global__ __launch_bounds__(256) void gemm_n_reduce(const float *partial, int slices, int64_t nm,
+                                                     float *Y) {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= (int64_t)n * M) return;
-    const int t = (int)(idx / M), i = (int)(idx - (int64_t)t * M);
-    float s = 0.f;
-    for (int sl = 0; sl < slices; sl++) s += partial[((int64_t)sl * kTok + t) * M + i];
+    if (idx >= nm) return;
+    float s = partial[idx];
+    for (int sl = 1; sl < slices; sl++) s += partial[(int64_t)sl * nm + idx];
     Y[idx] = s;
 }
 
-// Slicing of K: enough workgroups for the chip (about 512), at most
-// kMaxSlicesSB super-blocks of X staged per workgroup.
-void plan(int64_t M, int64_t K, int &ks, int &slices) {
-    const int sb_total = (int)((K + 255) / 256);
-    const int row_blocks = (int)((M + 63) / 64);
-    int want = (512 + row_blocks - 1) / row_blocks;
-    if (want < 1) want = 1;
-    if (want > sb_total) want = sb_total;
-    ks = (sb_total + want - 1) / want;
-    if (ks > kMaxSlicesSB) ks = kMaxSlicesSB;
-    slices = (sb_total + ks - 1) / ks;
+// Windows per slice: the largest of 4, 2, 1 that still gives about 1.5
+// workgroups per compute unit of a 256-CU part (the plan depends only on
+// M and K, so the workspace size does too).
+int windows_per_slice(int64_t M, int64_t K) {
+    const int64_t groups = (M + kRowsPerWG - 1) / kRowsPerWG;
+    const int64_t wtotal = (K + kWin - 1) / kWin;
+    for (int kw = 4; kw > 1; kw >>= 1)
+        if (groups * ((wtotal + kw - 1) / kw) >= 384) return kw;
+    return 1;
+}
+
+template <class F, int KW>
+hipError_t launch_kw(GemmParams p, hipStream_t s) {
+    const int wtotal = (p.K + kWin - 1) / kWin;
+    p.row_groups = (p.M + kRowsPerWG - 1) / kRowsPerWG;
+    p.slices = (wtotal + KW - 1) / KW;
+    const size_t lds = gemm_lds_bytes<F>(KW);
+    hipError_t e = ensure_lds((const void *)gemm_n_kernel<F, KW>, lds);
+    if (e != hipSuccess) return e;
+    const int64_t grid = (int64_t)p.row_groups * p.slices;
+    e = launch_main(gemm_n_kernel<F, KW>, dim3((unsigned)grid), dim3(kThreads), lds, s, p);
+    if (e != hipSuccess || p.slices == 1) return e;
+    const int64_t nm = (int64_t)p.n * p.M;
+    hipLaunchKernelGGL(gemm_n_reduce, dim3((unsigned)((nm + 255) / 256)), dim3(256), 0, s,
+                       p.partial, p.slices, nm, p.Y);
+    return hipGetLastError();
 }
 
 template <class F>
 hipError_t launch_typed(const GemmParams &p, hipStream_t s) {
-    const int row_blocks = (p.M + 63) / 64;
-    const size_t frag_vals = (size_t)p.ks * F::kNSub * 4 * kTok * F::kKpl;
-    const size_t lds = frag_vals * 2 * 2 + (size_t)p.ks * F::kNSub * kTok * 4;
-    hipError_t e = ensure_lds((const void *)gemm_n_kernel<F>, lds);
-    if (e != hipSuccess) return e;
-    hipError_t e2 = launch_main(gemm_n_kernel<F>, dim3((unsigned)(row_blocks * p.slices)), dim3(256),
-                                lds, s, p);
-    if (e2 != hipSuccess || p.slices == 1) return e2;
-    const int64_t total = (int64_t)p.n * p.M;
-    hipLaunchKernelGGL(gemm_n_reduce, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
-                       p.partial, p.slices, p.M, p.n, p.Y);
-    return hipGetLastError();
+    switch (windows_per_slice(p.M, p.K)) {
+    case 4: return launch_kw<F, 4>(p, s);
+    case 2: return launch_kw<F, 2>(p, s);
+    default: return launch_kw<F, 1>(p, s);
+    }
 }
 
 }  // namespace
 
-size_t gemm_n_workspace(int64_t M, int64_t K) {
-    int ks, slices;
-    plan(M, K, ks, slices);
-    return slices > 1 ? (size_t)slices * kTok * (size_t)M * sizeof(float) : 0;
+size_t gemm_n_workspace(int64_t M, int64_t K, int32_t n) {
+    const int64_t kw = windows_per_slice(M, K);
+    const int64_t slices = ((K + kWin - 1) / kWin + kw - 1) / kw;
+    return slices > 1 ? (size_t)slices * (size_t)n * (size_t)M * sizeof(float) : 0;
 }
 
 hipError_t launch_gemm_n(int type, const uint8_t *W, int64_t M, int64_t K, int32_t n,
@@ -365,11 +458,10 @@ hipError_t launch_gemm_n(int type, const uint8_t *W, int64_t M, int64_t K, int32
     p.M = (int32_t)M;
     p.K = (int32_t)K;
     p.n = n;
-    p.row_bytes = (int64_t)row_bytes_of(type, K);
+    p.row_bytes = (int32_t)row_bytes_of(type, K);
     p.X = X;
     p.Y = Y;
     p.partial = reinterpret_cast<float *>(ws);
-    plan(M, K, p.ks, p.slices);
     switch (type) {
     case kQ4K: return launch_typed<GQ4K>(p, s);
     case kQ6K: return launch_typed<GQ6K>(p, s);

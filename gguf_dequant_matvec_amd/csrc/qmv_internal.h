@@ -69,6 +69,6 @@ hipError_t launch_moe(const float *x, int64_t H, const float *router, const floa
                       float *topk_w, uint8_t *ws, hipStream_t s);
 hipError_t launch_gemm_n(int type, const uint8_t *W, int64_t M, int64_t K, int32_t n,
                          const float *X, float *Y, void *ws, hipStream_t s);
-size_t gemm_n_workspace(int64_t M, int64_t K);
+size_t gemm_n_workspace(int64_t M, int64_t K, int32_t n);
 
 }  // namespace qmv
