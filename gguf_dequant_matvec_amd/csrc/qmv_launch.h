@@ -36,14 +36,22 @@ inline int pow2_divisor(int n) {
 template <class F, int MODE>
 using KernelPtr = void (*)(RowsParams);
 
-template <class F, int MODE>
-KernelPtr<F, MODE> kernel_for(int G) {
+// Row slots per lane: the MoE down launch has few rows (the hidden size)
+// and long rows (k experts), so it keeps one slot for more tiles.
+template <int MODE>
+constexpr int rows_per_lane() {
+    return MODE == kModeMoeDown ? 1 : kR;
+}
+
+template <class F, int MODE, int KS>
+KernelPtr<F, MODE> kernel_for_ks(int G) {
+    constexpr int R = rows_per_lane<MODE>();
     switch (G) {
-    case 4: return rows_kernel<F, 4, kR, MODE>;
-    case 8: return rows_kernel<F, 8, kR, MODE>;
-    case 16: return rows_kernel<F, 16, kR, MODE>;
-    case 32: return rows_kernel<F, 32, kR, MODE>;
-    default: return rows_kernel<F, 64, kR, MODE>;
+    case 4: return rows_kernel<F, 4, R, MODE, KS>;
+    case 8: return rows_kernel<F, 8, R, MODE, KS>;
+    case 16: return rows_kernel<F, 16, R, MODE, KS>;
+    case 32: return rows_kernel<F, 32, R, MODE, KS>;
+    default: return rows_kernel<F, 64, R, MODE, KS>;
     }
 }
 
@@ -54,18 +62,29 @@ hipError_t launch_typed(const RowsParams &p_in, hipStream_t s, int *grid_out) {
     const int U = p.K / F::kUnitWeights;
     // the MoE down launch needs unit steps that never straddle two experts
     const int G = MODE == kModeMoeDown ? pow2_divisor(p.moe.units_per_mat) : pick_group(U);
-    const int64_t rows_per_tile = (int64_t)kR * (kWave / G);
+    const int iters = (U + G - 1) / G;
+    const int64_t rows_per_tile = (int64_t)rows_per_lane<MODE>() * (kWave / G);
     const int64_t ntiles = ((int64_t)p.M + rows_per_tile - 1) / rows_per_tile;
     const int waves = kBlockThreads / kWave;
     const size_t lds =
         ((size_t)lds_x_floats<F>(p.K) + (F::kSumGroup ? (size_t)p.K / F::kSumGroup : 0)) * 4;
-    KernelPtr<F, MODE> k = kernel_for<F, MODE>(G);
+    // Tiles of one wave each, unless there are fewer than two per compute
+    // unit and a row has at least 4 unit steps: then the 4 waves of a
+    // workgroup split each tile's K (more workgroups, but each stages x).
+    KernelPtr<F, MODE> k = kernel_for_ks<F, MODE, 1>(G);
     hipError_t e = ensure_lds((const void *)k, lds);
     if (e != hipSuccess) return e;
-    // persistent grid: exactly the workgroups that are resident at once, so
+    int per_cu = resident_blocks((const void *)k, kBlockThreads, lds);
+    const bool split = iters >= waves && ntiles < 2 * (int64_t)device_cu_count();
+    if (split) {
+        k = kernel_for_ks<F, MODE, kBlockThreads / kWave>(G);
+        e = ensure_lds((const void *)k, lds);
+        if (e != hipSuccess) return e;
+        per_cu = resident_blocks((const void *)k, kBlockThreads, lds);
+    }
+    // persistent grid: at most the workgroups that are resident at once, so
     // no workgroup waits for a second round while compute units idle
-    const int per_cu = resident_blocks((const void *)k, kBlockThreads, lds);
-    int64_t grid = (ntiles + waves - 1) / waves;
+    int64_t grid = split ? ntiles : (ntiles + waves - 1) / waves;
     const int64_t cap = (int64_t)device_cu_count() * per_cu;
     if (grid > cap) grid = cap;
     if (grid > kMaxGrid) grid = kMaxGrid;

@@ -174,7 +174,11 @@ __device__ __forceinline__ float fp8_unit_inverse() {
     return 1.0f / v.x;
 }
 
-template <class F, int G, int R, int MODE>
+// KS = 1: each wave owns whole tiles.  KS = 4: the four waves of a workgroup
+// share each tile, wave w taking unit steps w, w + 4, ... (needs at least 4
+// steps per row); their per-row partial sums meet in LDS and are added in
+// wave order, so the result is still fixed by (format, K, G, KS).
+template <class F, int G, int R, int MODE, int KS>
 __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
     constexpr bool kMoe = MODE == kModeMoeGateUp || MODE == kModeMoeDown;
     extern __shared__ float smem[];
@@ -193,7 +197,12 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
     const int iters = (U + G - 1) / G;  // unit steps per row
     constexpr int kRowsPerTile = R * P;
     const int ntiles = (p.M + kRowsPerTile - 1) / kRowsPerTile;
-    const int tile_stride = (int)gridDim.x * waves_per_block;
+    const int tile_stride = KS == 1 ? (int)gridDim.x * waves_per_block : (int)gridDim.x;
+    const int it0 = KS == 1 ? 0 : wave;  // this wave's first unit step of a tile
+    static_assert(KS == 1 || KS == kBlockThreads / kWave, "K split over the workgroup's waves");
+    // K-split partial sums: [tile parity][wave][row slot][row in wave]
+    __shared__ float red[KS > 1 ? 2 * KS * R * P : 1];
+    int tile_count = 0;
     const uint32_t rb = (uint32_t)p.row_bytes;
 
     // byte offset of row slot r inside a tile (rows of a tile are consecutive)
@@ -260,7 +269,26 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
             tot[r] = group_sum<G>(acc[r]);  // exact in the group's last lane
             acc[r] = 0.f;
         }
-        const bool owner = g == G - 1;
+        bool owner = g == G - 1;
+        if constexpr (KS > 1) {
+            const int par = tile_count & 1;
+            tile_count++;
+            if (owner) {
+#pragma unroll
+                for (int r = 0; r < R; r++) red[((par * KS + wave) * R + r) * P + sub] = tot[r];
+            }
+            __syncthreads();
+            owner = owner && wave == 0;
+            if (owner) {
+#pragma unroll
+                for (int r = 0; r < R; r++) {
+                    float v = red[((par * KS + 0) * R + r) * P + sub];
+#pragma unroll
+                    for (int w = 1; w < KS; w++) v += red[((par * KS + w) * R + r) * P + sub];
+                    tot[r] = v;
+                }
+            }
+        }
         const int r0 = t * kRowsPerTile;
         if (MODE != kModeArgmax) {
             // segment of the tile's first row and the start of the next one:
@@ -316,17 +344,19 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
 #pragma unroll
             for (int r = 0; r < R; r++) F::dot(src[r], xv, sums, u, inv_unit, acc[r]);
         }
-        if (it == iters - 1) finish_tile(t);
+        if (it + KS >= iters) finish_tile(t);  // this wave's last step of the tile
     };
 
     // Items of this wave: tiles t_first, t_first + stride, ..., each with
     // `iters` unit steps.
-    const int t_first = __builtin_amdgcn_readfirstlane((int)blockIdx.x * waves_per_block + wave);
+    const int t_first = __builtin_amdgcn_readfirstlane(
+        KS == 1 ? (int)blockIdx.x * waves_per_block + wave : (int)blockIdx.x);
     const int my_tiles = t_first < ntiles ? (ntiles - 1 - t_first) / tile_stride + 1 : 0;
-    const int n_items = my_tiles * iters;
+    const int steps = (iters - it0 + KS - 1) / KS;  // this wave's steps per tile
+    const int n_items = my_tiles * steps;
     typename F::Regs bufA[R], bufB[R];
     int tA = t_first;
-    int itA = 0;
+    int itA = it0;
 
     if (MODE == kModeMoeGateUp) {
         moe_select(p.moe, sel, wsel);
@@ -368,16 +398,16 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
         for (int k = 0; k < n_items; k += 2) {
             int tB = tA;
             int itB = itA;
-            if (k + 1 < n_items && ++itB == iters) {
-                itB = 0;
+            if (k + 1 < n_items && (itB += KS) >= iters) {
+                itB = it0;
                 tB += tile_stride;
             }
             issue(bufB, tB, itB);
             consume(bufA, inv_unit, tA, itA);
             int tC = tB;
             int itC = itB;
-            if (k + 2 < n_items && ++itC == iters) {
-                itC = 0;
+            if (k + 2 < n_items && (itC += KS) >= iters) {
+                itC = it0;
                 tC += tile_stride;
             }
             issue(bufA, tC, itC);
