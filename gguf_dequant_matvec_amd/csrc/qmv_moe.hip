@@ -28,9 +28,9 @@ __global__ __launch_bounds__(256) void router_logits(const float *__restrict__ R
         acc = fmaf(r.z, v.z, acc);
         acc = fmaf(r.w, v.w, acc);
     }
-    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    acc = group_sum<64>(acc);  // wave total in lane 63
     __shared__ float red[4];
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+    if ((threadIdx.x & 63) == 63) red[threadIdx.x >> 6] = acc;
     __syncthreads();
     if (threadIdx.x == 0) logits[e] = (red[0] + red[1]) + (red[2] + red[3]);
 }

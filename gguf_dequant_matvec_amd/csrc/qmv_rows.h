@@ -105,19 +105,27 @@ __device__ __forceinline__ void put_x4(float *xs, float *sums, int i, bool valid
 // Stage x[0..K) in LDS, plus the sums of its consecutive groups of
 // F::kSumGroup values.  x is stored padded (4 floats after every
 // F::kPadEvery) so that the lanes' 16-byte reads spread over the LDS banks.
-// Loads are issued eight at a time.  K is a multiple of 32, so a lane group
-// is either wholly inside [0, K) or wholly outside.
-template <class F>
+// Loads are issued eight at a time; `pre` runs after the first eight are
+// issued, so work that is independent of x overlaps their latency.  K is a
+// multiple of 32 (K >= 32), so a lane group is either wholly inside [0, K)
+// or wholly outside.
+struct NoPre {
+    __device__ void operator()() const {}
+};
+template <class F, class Pre = NoPre>
 __device__ __forceinline__ void stage_x(const float *__restrict__ x, int K, float *xs,
-                                        float *sums) {
+                                        float *sums, Pre pre = Pre()) {
     const int nt = blockDim.x;
-    for (int base = threadIdx.x * 4; base < K; base += nt * 4 * 8) {
+    // the loop is uniform over the workgroup, so `pre` runs at one point
+    for (int base0 = 0; base0 < K; base0 += nt * 4 * 8) {
+        const int base = base0 + (int)threadIdx.x * 4;
         float4 v[8];
 #pragma unroll
         for (int j = 0; j < 8; j++) {
             const int i = base + j * nt * 4;
             v[j] = i < K ? *reinterpret_cast<const float4 *>(x + i) : make_float4(0.f, 0.f, 0.f, 0.f);
         }
+        if (base0 == 0) pre();
 #pragma unroll
         for (int j = 0; j < 8; j++) {
             const int i = base + j * nt * 4;
@@ -132,37 +140,33 @@ __device__ __forceinline__ float siluf(float v) { return v / (1.0f + expf(-v)); 
 
 // MoE selection from the router logits, done by wave 0 of every workgroup:
 // scores s_e = sigmoid(r_e); rank by s_e + b_e (ties to the lower expert);
-// weights = selected s_e over their sum.  Results land in LDS (and, from
-// workgroup 0, in topk_idx / topk_w).
+// weights = selected s_e over their sum.  Each lane (one expert) counts the
+// experts that outrank it, reading the others' keys with v_readlane, so the
+// selection is one pass of compares with no LDS round trips.  Results land
+// in LDS (and, from workgroup 0, in topk_idx / topk_w).
 __device__ __forceinline__ void moe_select(const MoeArgs &m, int32_t *sel, float *wsel) {
     if (threadIdx.x >= kWave) return;
     const int e = threadIdx.x;
     const float s = e < m.E ? sigmoidf(m.logits[e]) : 0.f;
-    const float v = e < m.E ? s + m.bias[e] : -__builtin_inff();
-    bool taken = e >= m.E;
-    float ssum = 0.f;
-    for (int t = 0; t < m.k; t++) {
-        // packed key: ordered score, then the lower index wins
-        uint64_t key = taken ? 0ull : (((uint64_t)float_key(v + 0.0f) << 32) | (uint64_t)(63 - e));
-        for (int o = kWave / 2; o > 0; o >>= 1) {
-            const uint64_t other = __shfl_xor(key, o, kWave);
-            key = other > key ? other : key;
-        }
-        const int win = 63 - (int)(key & 0xFFFFFFFFu);
-        const float swin = __shfl(s, win, kWave);
-        if (e == win) taken = true;
-        if (e == 0) {
-            sel[t] = win;
-            wsel[t] = swin;  // normalised below
-        }
-        ssum += swin;
+    const float v = e < m.E ? s + m.bias[e] + 0.0f : -__builtin_inff();  // -0 -> +0
+    int rank = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxExperts; j++) {
+        const float vj = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), j));
+        rank += (vj > v || (vj == v && j < e)) ? 1 : 0;
     }
-    if (e < m.k) {
-        const float w = wsel[e] / ssum;
-        wsel[e] = w;
+    const bool chosen = e < m.E && rank < m.k;
+    // sum of the selected scores (fixed order: DPP tree, total in lane 63)
+    float ssum = group_sum<kWave>(chosen ? s : 0.f);
+    ssum = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ssum), kWave - 1));
+    if (chosen) {
+        const float w = s / ssum;
+        sel[rank] = e;
+        wsel[rank] = w;
         if (blockIdx.x == 0) {
-            m.topk_idx[e] = sel[e];
-            m.topk_w[e] = w;
+            m.topk_idx[rank] = e;
+            m.topk_w[rank] = w;
         }
     }
 }
@@ -359,8 +363,9 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
     int itA = it0;
 
     if (MODE == kModeMoeGateUp) {
-        moe_select(p.moe, sel, wsel);
-        stage_x<F>(p.x, p.K, xs, sums);  // its barrier also publishes sel
+        // the selection overlaps the first activation loads; the staging
+        // barrier also publishes sel
+        stage_x<F>(p.x, p.K, xs, sums, [&]() { moe_select(p.moe, sel, wsel); });
     } else if (MODE == kModeMoeDown) {
         if ((int)threadIdx.x < p.moe.k) {
             sel[threadIdx.x] = p.moe.topk_idx[threadIdx.x];
