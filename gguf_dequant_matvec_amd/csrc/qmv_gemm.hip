@@ -241,26 +241,34 @@ size_t gemm_lds_bytes(int KW) {
 // activations into registers (unconditional loads through a view of
 // X[0..n): tokens past n read zeros, so no branch waits for the data),
 // store splits them into bf16 hi + lo, writes them in the operand layout and
-// adds the per-sub-block sums.  A lane takes kKpl consecutive activations of
-// one token, so the four groups of a sub-block sit in four consecutive lanes
-// and their sum is a quad DPP reduction.
+// adds the per-sub-block sums.  A lane takes the kKpl consecutive
+// activations of one (sub-block j, lane group q, token t), with t fastest:
+// consecutive lanes write consecutive 16-byte operand slots (no LDS bank
+// conflicts), and the four lane groups of a sub-block sit 16 lanes apart in
+// one wave, so their sum is two lane exchanges.
 template <class F, int KW>
 struct XStage {
-    static constexpr int kPerTok = kWin / F::kKpl;  // groups per token
-    static constexpr int kGroups = kTok * kPerTok;  // per window
+    static constexpr int kGroups = kTok * kWin / F::kKpl;  // per window
     static constexpr int kIters = KW * kGroups / kThreads;
     static_assert(KW * kGroups % kThreads == 0, "whole iterations");
-    static_assert(F::kSub / F::kKpl == 4, "four groups per sub-block");
+    static_assert(F::kSub / F::kKpl == 4, "four lane groups per sub-block");
     float v[kIters][F::kKpl];
-    int kpos[kIters];
+
+    __device__ static __forceinline__ void coords(int it, int &win, int &j, int &q, int &t) {
+        const int gi = (int)threadIdx.x + kThreads * it;
+        win = gi / kGroups;
+        const int gg = gi % kGroups;
+        t = gg % kTok;
+        q = (gg / kTok) % 4;
+        j = gg / (4 * kTok);
+    }
 
     __device__ __forceinline__ void load(const GemmParams &p, const BufSrc &xv, int wfirst) {
 #pragma unroll
         for (int it = 0; it < kIters; it++) {
-            const int gi = (int)threadIdx.x + kThreads * it;
-            const int win = gi / kGroups, gg = gi % kGroups;
-            const int t = gg / kPerTok, g = gg % kPerTok;
-            const int k = (wfirst + win) * kWin + g * F::kKpl;
+            int win, j, q, t;
+            coords(it, win, j, q, t);
+            const int k = (wfirst + win) * kWin + j * F::kSub + q * F::kKpl;
             const uint32_t off = ((uint32_t)t * (uint32_t)p.K + (uint32_t)k) * 4u;
 #pragma unroll
             for (int e = 0; e < F::kKpl / 4; e++) {
@@ -270,19 +278,18 @@ struct XStage {
                 v[it][4 * e + 2] = __builtin_bit_cast(float, a.z);
                 v[it][4 * e + 3] = __builtin_bit_cast(float, a.w);
             }
-            kpos[it] = k;
         }
     }
 
     // activations past K (the slice's or a last partial Q8_0 window) are zeroed
-    __device__ __forceinline__ void store(uint8_t *smem, int K) const {
+    __device__ __forceinline__ void store(uint8_t *smem, int wfirst, int K) const {
         using L = WinLayout<F>;
 #pragma unroll
         for (int it = 0; it < kIters; it++) {
-            const int gi = (int)threadIdx.x + kThreads * it;
-            const int win = gi / kGroups, gg = gi % kGroups;
-            const int t = gg / kPerTok, g = gg % kPerTok;
-            const bool in_k = kpos[it] < K;  // K is a multiple of the group size
+            int win, j, q, t;
+            coords(it, win, j, q, t);
+            const int k = (wfirst + win) * kWin + j * F::kSub + q * F::kKpl;
+            const bool in_k = k < K;  // K is a multiple of the group size
             BFrag<F> hi, lo;
             float sum = 0.f;
 #pragma unroll
@@ -294,15 +301,14 @@ struct XStage {
                 lo[F::perm(e)] = l;
                 sum += (float)h + (float)l;
             }
-            int j, q;
-            F::slot(g * F::kKpl, j, q);
             uint8_t *base = smem + (size_t)win * L::kBytes;
             const int pos = ((j * 4 + q) * kTok + t) * F::kKpl;
             *reinterpret_cast<BFrag<F> *>(base + 2 * pos) = hi;
             *reinterpret_cast<BFrag<F> *>(base + 2 * (L::kVals + pos)) = lo;
-            sum += dpp_f32<kDppXor1>(sum);
-            sum += dpp_f32<kDppXor2>(sum);
-            if ((g & 3) == 0) reinterpret_cast<float *>(base + 4 * L::kVals)[j * kTok + t] = sum;
+            // lane groups q = 0..3 of (j, t) are lanes t, t + 16, t + 32, t + 48
+            sum += __shfl_xor(sum, 16, kWave);
+            sum += __shfl_xor(sum, 32, kWave);
+            if (q == 0) reinterpret_cast<float *>(base + 4 * L::kVals)[j * kTok + t] = sum;
         }
     }
 };
@@ -350,7 +356,7 @@ __global__ __launch_bounds__(kThreads) void gemm_n_kernel(GemmParams p) {
                            (uint64_t)p.n * (uint32_t)p.K * 4u);
         XStage<F, KW> xs;
         xs.load(p, xview, wfirst);
-        xs.store(smem, p.K);
+        xs.store(smem, wfirst, p.K);
     }
     __syncthreads();
 
