@@ -68,16 +68,19 @@ hipError_t launch_typed(const RowsParams &p_in, hipStream_t s, int *grid_out) {
     const int waves = kBlockThreads / kWave;
     const size_t lds =
         ((size_t)lds_x_floats<F>(p.K) + (F::kSumGroup ? (size_t)p.K / F::kSumGroup : 0)) * 4;
-    // Tiles of one wave each, unless there are fewer than two per compute
-    // unit and a row has at least 4 unit steps: then the 4 waves of a
-    // workgroup split each tile's K (more workgroups, but each stages x).
+    // Tiles of one wave each.  The MoE down launch (few rows, long rows)
+    // splits each tile's K over the 4 waves of a workgroup when it has fewer
+    // than two tiles per compute unit and at least 4 unit steps per row.  The
+    // other modes never split, so a row's result depends only on (format, K)
+    // and fused rows and the argmax stay bit-identical to the plain matvec.
     KernelPtr<F, MODE> k = kernel_for_ks<F, MODE, 1>(G);
     hipError_t e = ensure_lds((const void *)k, lds);
     if (e != hipSuccess) return e;
     int per_cu = resident_blocks((const void *)k, kBlockThreads, lds);
-    const bool split = iters >= waves && ntiles < 2 * (int64_t)device_cu_count();
+    const bool split = MODE == kModeMoeDown && iters >= waves &&
+                       ntiles < 2 * (int64_t)device_cu_count();
     if (split) {
-        k = kernel_for_ks<F, MODE, kBlockThreads / kWave>(G);
+        k = kernel_for_ks<F, MODE, MODE == kModeMoeDown ? kBlockThreads / kWave : 1>(G);
         e = ensure_lds((const void *)k, lds);
         if (e != hipSuccess) return e;
         per_cu = resident_blocks((const void *)k, kBlockThreads, lds);

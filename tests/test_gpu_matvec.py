@@ -113,6 +113,7 @@ def test_x_extremes():
     ("q6_k", (100, 7, 1, 60), 1536),
     ("q8_0", (300, 11, 5), 576),
     ("q4_k", tuple([3] * 8), 4096),            # the most segments
+    ("q4_k", (100, 37, 3), 14336),             # long rows, several unit steps
 ])
 def test_fused_rows(t, segs, K):
     M = sum(segs)
@@ -142,7 +143,8 @@ def _argmax_gpu(t, bd, M, K, xd):
 
 
 @pytest.mark.parametrize("t,M,K", [("q6_k", 5000, 4096), ("q4_k", 777, 2048), ("q8_0", 1536, 576),
-                                   ("q6_k", 1, 256), ("q6_k", 3001, 1536)])
+                                   ("q6_k", 1, 256), ("q6_k", 3001, 1536), ("q4_k", 300, 14336),
+                                   ("q8_0", 70, 8192)])
 def test_argmax(t, M, K):
     b, x = _case(t, M, K, 500 + M)
     y_ref, a_ref = oracle.qmv(t, b, M, K, x)
