@@ -116,22 +116,27 @@ template <class F, class Pre = NoPre>
 __device__ __forceinline__ void stage_x(const float *__restrict__ x, int K, float *xs,
                                         float *sums, Pre pre = Pre()) {
     const int nt = blockDim.x;
-    // the loop is uniform over the workgroup, so `pre` runs at one point
-    for (int base0 = 0; base0 < K; base0 += nt * 4 * 8) {
+    // unconditional loads through a view of x (past K they read zeros), so
+    // no branch makes the compiler wait for them early
+    const BufSrc xv(reinterpret_cast<const uint8_t *>(x), (uint64_t)K * 4);
+    auto batch = [&](int base0, bool first) {
         const int base = base0 + (int)threadIdx.x * 4;
         float4 v[8];
 #pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const int i = base + j * nt * 4;
-            v[j] = i < K ? *reinterpret_cast<const float4 *>(x + i) : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-        if (base0 == 0) pre();
+        for (int j = 0; j < 8; j++)
+            v[j] = __builtin_bit_cast(float4, xv.ld16((uint32_t)(base + j * nt * 4) * 4u));
+        if (first) pre();
 #pragma unroll
         for (int j = 0; j < 8; j++) {
             const int i = base + j * nt * 4;
             put_x4<F>(xs, sums, i, i < K, v[j]);
         }
-    }
+    };
+    // the first batch is peeled (straight-line code, so the waits for its x
+    // loads do not cover the loads `pre` issues after them); the loop over
+    // the rest is uniform over the workgroup
+    batch(0, true);
+    for (int base0 = nt * 4 * 8; base0 < K; base0 += nt * 4 * 8) batch(base0, false);
     __syncthreads();
 }
 
@@ -255,8 +260,10 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
             base = p.W + (int64_t)sel[slot] * p.moe.mat_bytes + (int64_t)r0 * rb;
             avail = (uint64_t)(p.M - r0) * rb;
         } else {
+            // a wave without items still issues its first loads (see the
+            // staging below): past the end the view is empty and reads zeros
             base = p.W + (int64_t)r0 * rb;
-            avail = (uint64_t)(p.M - r0) * rb;
+            avail = p.M > r0 ? (uint64_t)(p.M - r0) * rb : 0;
         }
         const BufSrc src(base, avail);
         // unit g + ustep: ustep is a multiple of 4, so the position inside a
@@ -387,10 +394,12 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
         }
         __syncthreads();
     } else {
-        // the first item's weights are requested before x is staged, so the
-        // two latencies overlap
-        if (n_items > 0) issue(bufA, tA, itA);
-        stage_x<F>(p.x, p.K, xs, sums);
+        // the first item's weights are requested right after the first
+        // activation loads: the two latencies overlap, and since loads
+        // complete in order, the staging waits only for x, not for the
+        // (slower) weights.  The issue is unconditional so that the wait
+        // count for x is known at compile time.
+        stage_x<F>(p.x, p.K, xs, sums, [&]() { issue(bufA, tA, itA); });
     }
     const float inv_unit = fp8_unit_inverse();
 
