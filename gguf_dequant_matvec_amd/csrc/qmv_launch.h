@@ -43,15 +43,15 @@ constexpr int rows_per_lane() {
     return MODE == kModeMoeDown ? 1 : kR;
 }
 
-template <class F, int MODE, int KS>
+template <class F, int MODE, int KS, bool XR>
 KernelPtr<F, MODE> kernel_for_ks(int G) {
     constexpr int R = rows_per_lane<MODE>();
     switch (G) {
-    case 4: return rows_kernel<F, 4, R, MODE, KS>;
-    case 8: return rows_kernel<F, 8, R, MODE, KS>;
-    case 16: return rows_kernel<F, 16, R, MODE, KS>;
-    case 32: return rows_kernel<F, 32, R, MODE, KS>;
-    default: return rows_kernel<F, 64, R, MODE, KS>;
+    case 4: return rows_kernel<F, 4, R, MODE, KS, XR>;
+    case 8: return rows_kernel<F, 8, R, MODE, KS, XR>;
+    case 16: return rows_kernel<F, 16, R, MODE, KS, XR>;
+    case 32: return rows_kernel<F, 32, R, MODE, KS, XR>;
+    default: return rows_kernel<F, 64, R, MODE, KS, XR>;
     }
 }
 
@@ -73,14 +73,17 @@ hipError_t launch_typed(const RowsParams &p_in, hipStream_t s, int *grid_out) {
     // than two tiles per compute unit and at least 4 unit steps per row.  The
     // other modes never split, so a row's result depends only on (format, K)
     // and fused rows and the argmax stay bit-identical to the plain matvec.
-    KernelPtr<F, MODE> k = kernel_for_ks<F, MODE, 1>(G);
+    // a row of one unit step keeps its activations in registers
+    constexpr bool kXrModes = MODE == kModeStore || MODE == kModeArgmax;
+    KernelPtr<F, MODE> k = iters == 1 ? kernel_for_ks<F, MODE, 1, kXrModes>(G)
+                                      : kernel_for_ks<F, MODE, 1, false>(G);
     hipError_t e = ensure_lds((const void *)k, lds);
     if (e != hipSuccess) return e;
     int per_cu = resident_blocks((const void *)k, kBlockThreads, lds);
     const bool split = MODE == kModeMoeDown && iters >= waves &&
                        ntiles < 2 * (int64_t)device_cu_count();
     if (split) {
-        k = kernel_for_ks<F, MODE, MODE == kModeMoeDown ? kBlockThreads / kWave : 1>(G);
+        k = kernel_for_ks<F, MODE, MODE == kModeMoeDown ? kBlockThreads / kWave : 1, false>(G);
         e = ensure_lds((const void *)k, lds);
         if (e != hipSuccess) return e;
         per_cu = resident_blocks((const void *)k, kBlockThreads, lds);

@@ -187,7 +187,10 @@ __device__ __forceinline__ float fp8_unit_inverse() {
 // share each tile, wave w taking unit steps w, w + 4, ... (needs at least 4
 // steps per row); their per-row partial sums meet in LDS and are added in
 // wave order, so the result is still fixed by (format, K, G, KS).
-template <class F, int G, int R, int MODE, int KS>
+// XR: a row is a single unit step, so every lane keeps the same unit for the
+// whole launch and reads its activations from LDS once, after staging, into
+// registers (plain and argmax modes only).
+template <class F, int G, int R, int MODE, int KS, bool XR>
 __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
     constexpr bool kMoe = MODE == kModeMoeGateUp || MODE == kModeMoeDown;
     extern __shared__ float smem[];
@@ -225,6 +228,7 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
     float acc[R];
 #pragma unroll
     for (int r = 0; r < R; r++) acc[r] = 0.f;
+    float xr[XR ? F::kUnitWeights : 1];  // XR: this lane's activations
 
     // The expert a unit step reads in the down launch (uniform: G divides the
     // units per expert, so a step never straddles two experts).
@@ -348,12 +352,17 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
         it = __builtin_amdgcn_readfirstlane(it);
         const int u = g + G * it;
         if (u < U) {
-            float xv[F::kUnitWeights];
-            F::load_x(xs, u, xv);
-            // u indexes the (concatenated) x and its sums; the block-internal
-            // position only depends on u mod 4, the same inside each expert
+            if constexpr (XR) {
 #pragma unroll
-            for (int r = 0; r < R; r++) F::dot(src[r], xv, sums, u, inv_unit, acc[r]);
+                for (int r = 0; r < R; r++) F::dot(src[r], xr, sums, u, inv_unit, acc[r]);
+            } else {
+                float xv[F::kUnitWeights];
+                F::load_x(xs, u, xv);
+                // u indexes the (concatenated) x and its sums; the block-internal
+                // position only depends on u mod 4, the same inside each expert
+#pragma unroll
+                for (int r = 0; r < R; r++) F::dot(src[r], xv, sums, u, inv_unit, acc[r]);
+            }
         }
         if (it + KS >= iters) finish_tile(t);  // this wave's last step of the tile
     };
@@ -400,6 +409,7 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
         // (slower) weights.  The issue is unconditional so that the wait
         // count for x is known at compile time.
         stage_x<F>(p.x, p.K, xs, sums, [&]() { issue(bufA, tA, itA); });
+        if constexpr (XR) F::load_x(xs, g < U ? g : 0, xr);
     }
     const float inv_unit = fp8_unit_inverse();
 
