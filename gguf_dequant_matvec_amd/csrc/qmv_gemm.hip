@@ -36,6 +36,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -86,14 +87,16 @@ struct GQ4K {
         for (int c = 0; c < 4; c++) r.piece[c] = src.ld8(off + 16 + 32 * c + 8 * q);
         return r;
     }
-    __device__ static bf16x8 codes(const Regs &r, int j) {
+    // mask and bf16 bias arrive in registers, so each code dword is one
+    // v_and_or_b32 (plus a shift): a VOP3 instruction takes no literal here
+    __device__ static bf16x8 codes(const Regs &r, int j, uint32_t mask, uint32_t bias) {
         const uint2 p = r.piece[j >> 1];
         const int sh = (j & 1) * 4;
         uint32_t d[4];
-        d[0] = ((p.x >> sh) & 0x000F000Fu) | kB16;
-        d[1] = ((p.x >> (sh + 8)) & 0x000F000Fu) | kB16;
-        d[2] = ((p.y >> sh) & 0x000F000Fu) | kB16;
-        d[3] = ((p.y >> (sh + 8)) & 0x000F000Fu) | kB16;
+        d[0] = ((p.x >> sh) & mask) | bias;
+        d[1] = ((p.x >> (sh + 8)) & mask) | bias;
+        d[2] = ((p.y >> sh) & mask) | bias;
+        d[3] = ((p.y >> (sh + 8)) & mask) | bias;
         return __builtin_bit_cast(bf16x8, d);
     }
     // y += scale * C - corr * sum(x): w = d*sc*q - dmin*m and the codes are q + 128.
@@ -149,7 +152,7 @@ struct GQ6K {
         r.d = src.ld2(off + 208);
         return r;
     }
-    __device__ static s16x4 codes(const Regs &r, int j) {
+    __device__ static s16x4 codes(const Regs &r, int j, uint32_t, uint32_t) {
         const int n = j / 8, g = (j % 8) / 2, hh = j % 2;
         const uint32_t lo = (r.ql[n][g & 1][hh] >> (4 * (g >> 1))) & 0x0F0F0F0Fu;
         const uint32_t hi = ((r.qh[n][hh] >> (2 * g)) & 0x03030303u) << 4;
@@ -190,7 +193,7 @@ struct GQ80 {
         }
         return r;
     }
-    __device__ static bf16x8 codes(const Regs &r, int j) {
+    __device__ static bf16x8 codes(const Regs &r, int j, uint32_t, uint32_t) {
         const uint32_t w[2] = {r.q[j].x, r.q[j].y};
         uint32_t d[4];
 #pragma unroll
@@ -290,21 +293,31 @@ struct XStage {
             coords(it, win, j, q, t);
             const int k = (wfirst + win) * kWin + j * F::kSub + q * F::kKpl;
             const bool in_k = k < K;  // K is a multiple of the group size
-            BFrag<F> hi, lo;
+            // operand slots (2i, 2i+1) hold activations (perm(2i), perm(2i+1)):
+            // one packed conversion per slot pair for hi, one for lo
+            uint32_t hi[F::kKpl / 2], lo[F::kKpl / 2];
             float sum = 0.f;
 #pragma unroll
-            for (int e = 0; e < F::kKpl; e++) {
-                const float x = in_k ? v[it][e] : 0.f;
-                const __bf16 h = (__bf16)x;
-                const __bf16 l = (__bf16)(x - (float)h);
-                hi[F::perm(e)] = h;
-                lo[F::perm(e)] = l;
-                sum += (float)h + (float)l;
+            for (int i2 = 0; i2 < F::kKpl / 2; i2++) {
+                f32x2 xx;
+                xx.x = in_k ? v[it][F::perm(2 * i2)] : 0.f;
+                xx.y = in_k ? v[it][F::perm(2 * i2 + 1)] : 0.f;
+                const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(xx, bf16x2));
+                const float h0 = __builtin_bit_cast(float, hb << 16);
+                const float h1 = __builtin_bit_cast(float, hb & 0xFFFF0000u);
+                f32x2 rr;
+                rr.x = xx.x - h0;
+                rr.y = xx.y - h1;
+                const uint32_t lb = __builtin_bit_cast(uint32_t, __builtin_convertvector(rr, bf16x2));
+                hi[i2] = hb;
+                lo[i2] = lb;
+                sum += (h0 + __builtin_bit_cast(float, lb << 16)) +
+                       (h1 + __builtin_bit_cast(float, lb & 0xFFFF0000u));
             }
             uint8_t *base = smem + (size_t)win * L::kBytes;
             const int pos = ((j * 4 + q) * kTok + t) * F::kKpl;
-            *reinterpret_cast<BFrag<F> *>(base + 2 * pos) = hi;
-            *reinterpret_cast<BFrag<F> *>(base + 2 * (L::kVals + pos)) = lo;
+            *reinterpret_cast<BFrag<F> *>(base + 2 * pos) = __builtin_bit_cast(BFrag<F>, hi);
+            *reinterpret_cast<BFrag<F> *>(base + 2 * (L::kVals + pos)) = __builtin_bit_cast(BFrag<F>, lo);
             // lane groups q = 0..3 of (j, t) are lanes t, t + 16, t + 32, t + 48
             sum += __shfl_xor(sum, 16, kWave);
             sum += __shfl_xor(sum, 32, kWave);
@@ -360,6 +373,10 @@ __global__ __launch_bounds__(kThreads) void gemm_n_kernel(GemmParams p) {
     }
     __syncthreads();
 
+    // code-packing constants in registers (one SGPR, one VGPR)
+    const uint32_t kmask = __builtin_amdgcn_readfirstlane(0x000F000Fu);
+    uint32_t kbias;
+    asm("v_mov_b32 %0, %1" : "=v"(kbias) : "i"(kB16));
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < KW; i++) {
@@ -376,7 +393,7 @@ __global__ __launch_bounds__(kThreads) void gemm_n_kernel(GemmParams p) {
             const int fo = ((j * 4 + q) * kTok + r) * F::kKpl;
             const Frag<F> ah = *reinterpret_cast<const Frag<F> *>(xhi + fo);
             const Frag<F> al = *reinterpret_cast<const Frag<F> *>(xlo + fo);
-            const Frag<F> b = F::codes(wr[i], j);
+            const Frag<F> b = F::codes(wr[i], j, kmask, kbias);
             f32x4 c = {0.f, 0.f, 0.f, 0.f};
             c = mfma<F>(ah, b, c);
             c = mfma<F>(al, b, c);
@@ -402,13 +419,22 @@ __global__ __launch_bounds__(kThreads) void gemm_n_kernel(GemmParams p) {
     }
 }
 
-// Y[t][i] = sum over slices of the partial sums, in slice order.
+// Y[t][i] = sum over slices of the partial sums, in slice order.  The loads
+// of up to eight slices are issued together before they are added, so the
+// latency is paid once per eight slices, not once per slice.
 __global__ __launch_bounds__(256) void gemm_n_reduce(const float *partial, int slices, int64_t nm,
                                                      float *Y) {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= nm) return;
-    float s = partial[idx];
-    for (int sl = 1; sl < slices; sl++) s += partial[(int64_t)sl * nm + idx];
+    float s = 0.f;
+    for (int s0 = 0; s0 < slices; s0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) v[j] = s0 + j < slices ? partial[(int64_t)(s0 + j) * nm + idx] : 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+            if (s0 + j < slices) s = (s0 + j == 0) ? v[j] : s + v[j];
+    }
     Y[idx] = s;
 }
 
