@@ -143,15 +143,16 @@ __device__ __forceinline__ void stage_x(const float *__restrict__ x, int K, floa
 __device__ __forceinline__ float sigmoidf(float v) { return 1.0f / (1.0f + expf(-v)); }
 __device__ __forceinline__ float siluf(float v) { return v / (1.0f + expf(-v)); }
 
-// MoE selection from the router logits, done by wave 0 of every workgroup:
-// scores s_e = sigmoid(r_e); rank by s_e + b_e (ties to the lower expert);
-// weights = selected s_e over their sum.  Each lane (one expert) counts the
-// experts that outrank it, reading the others' keys with v_readlane, so the
-// selection is one pass of compares with no LDS round trips.  Results land
-// in LDS (and, from workgroup 0, in topk_idx / topk_w).
+// MoE selection from the router logits, done by every wave (each writes the
+// same values into the workgroup's LDS slots, so it can use them without a
+// barrier): scores s_e = sigmoid(r_e); rank by s_e + b_e (ties to the lower
+// expert); weights = selected s_e over their sum.  Each lane (one expert)
+// counts the experts that outrank it, reading the others' keys with
+// v_readlane, so the selection is one pass of compares with no LDS round
+// trips.  Wave 0 of workgroup 0 also writes topk_idx / topk_w.
 __device__ __forceinline__ void moe_select(const MoeArgs &m, int32_t *sel, float *wsel) {
-    if (threadIdx.x >= kWave) return;
-    const int e = threadIdx.x;
+    const int e = threadIdx.x & (kWave - 1);
+    const bool publish = blockIdx.x == 0 && threadIdx.x < kWave;
     const float s = e < m.E ? sigmoidf(m.logits[e]) : 0.f;
     const float v = e < m.E ? s + m.bias[e] + 0.0f : -__builtin_inff();  // -0 -> +0
     int rank = 0;
@@ -169,7 +170,7 @@ __device__ __forceinline__ void moe_select(const MoeArgs &m, int32_t *sel, float
         const float w = s / ssum;
         sel[rank] = e;
         wsel[rank] = w;
-        if (blockIdx.x == 0) {
+        if (publish) {
             m.topk_idx[rank] = e;
             m.topk_w[rank] = w;
         }
@@ -379,15 +380,19 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
     int itA = it0;
 
     if (MODE == kModeMoeGateUp) {
-        // the selection overlaps the first activation loads; the staging
-        // barrier also publishes sel
-        stage_x<F>(p.x, p.K, xs, sums, [&]() { moe_select(p.moe, sel, wsel); });
+        // each wave selects the experts itself and requests its first weights
+        // before x is staged
+        moe_select(p.moe, sel, wsel);
+        if (n_items > 0) issue(bufA, tA, itA);
+        stage_x<F>(p.x, p.K, xs, sums);
     } else if (MODE == kModeMoeDown) {
         if ((int)threadIdx.x < p.moe.k) {
             sel[threadIdx.x] = p.moe.topk_idx[threadIdx.x];
             wsel[threadIdx.x] = p.moe.topk_w[threadIdx.x];
         }
         __syncthreads();
+        // the first weights are requested before the activations are formed
+        if (n_items > 0) issue(bufA, tA, itA);
         // x[s*I + j] = w_s * silu(g_s[j]) * u_s[j]; workgroup 0 keeps h.
         // K = k*I is a multiple of 32, so sum groups never straddle slots.
         const int I = p.moe.I, K = p.K;
@@ -418,7 +423,6 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
     // counters never have to merge "maybe issued" states and each consume
     // waits only for its own loads.
     if (n_items > 0) {
-        if (kMoe) issue(bufA, tA, itA);
         for (int k = 0; k < n_items; k += 2) {
             int tB = tA;
             int itB = itA;
