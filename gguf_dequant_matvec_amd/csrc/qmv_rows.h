@@ -257,12 +257,14 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
             // the tile's rows belong to one selected expert
             const int slot = r0 / p.moe.rows_per_mat;
             const int rin = r0 - slot * p.moe.rows_per_mat;
-            base = p.W + (int64_t)sel[slot] * p.moe.mat_bytes + (int64_t)rin * rb;
+            const int ex = __builtin_amdgcn_readfirstlane(sel[slot]);  // uniform
+            base = p.W + (int64_t)ex * p.moe.mat_bytes + (int64_t)rin * rb;
             avail = (uint64_t)(p.moe.rows_per_mat - rin) * rb;
         } else if (MODE == kModeMoeDown) {
             const int slot = step_slot(it);
             ustep -= slot * p.moe.units_per_mat;
-            base = p.W + (int64_t)sel[slot] * p.moe.mat_bytes + (int64_t)r0 * rb;
+            const int ex = __builtin_amdgcn_readfirstlane(sel[slot]);  // uniform
+            base = p.W + (int64_t)ex * p.moe.mat_bytes + (int64_t)r0 * rb;
             avail = (uint64_t)(p.M - r0) * rb;
         } else {
             // a wave without items still issues its first loads (see the
