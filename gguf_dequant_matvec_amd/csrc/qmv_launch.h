@@ -8,6 +8,7 @@
 namespace qmv {
 
 constexpr int kR = 2;  // row slots per lane
+constexpr int kMaxBlocksPerCU = 2;  // persistent workgroups per compute unit
 
 // Fraction of lane-steps that carry work when a row of U units is spread over
 // G lanes; pick the G (a power of two, >= 4) that maximises it, preferring
@@ -88,6 +89,12 @@ hipError_t launch_typed(const RowsParams &p_in, hipStream_t s, int *grid_out) {
         if (e != hipSuccess) return e;
         per_cu = resident_blocks((const void *)k, kBlockThreads, lds);
     }
+    // Each workgroup stages its own copy of x, and the x loads of a compute
+    // unit's later workgroups queue behind the earlier ones' first weight
+    // loads: with three or more workgroups per compute unit the last ones
+    // start late and end the launch late, so at most two are used (measured
+    // faster at every decode shape).
+    if (per_cu > kMaxBlocksPerCU) per_cu = kMaxBlocksPerCU;
     // persistent grid: at most the workgroups that are resident at once, so
     // no workgroup waits for a second round while compute units idle
     int64_t grid = split ? ntiles : (ntiles + waves - 1) / waves;

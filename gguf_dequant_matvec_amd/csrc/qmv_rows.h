@@ -78,6 +78,9 @@ __device__ __forceinline__ uint64_t argmax_key(float v, int32_t idx) {
     return ((uint64_t)float_key(v) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)idx);
 }
 
+// Items whose weight loads a wave keeps in flight (register sets in its ring).
+constexpr int kPipeDepth = 2;
+
 // Floats of the padded LDS copy of x.
 template <class F>
 __host__ __device__ constexpr int lds_x_floats(int K) {
@@ -105,29 +108,29 @@ __device__ __forceinline__ void put_x4(float *xs, float *sums, int i, bool valid
 // Stage x[0..K) in LDS, plus the sums of its consecutive groups of
 // F::kSumGroup values.  x is stored padded (4 floats after every
 // F::kPadEvery) so that the lanes' 16-byte reads spread over the LDS banks.
-// Loads are issued eight at a time; `pre` runs after the first eight are
-// issued, so work that is independent of x overlaps their latency.  K is a
-// multiple of 32 (K >= 32), so a lane group is either wholly inside [0, K)
-// or wholly outside.
+// Each thread issues NB loads of 4 floats at a time; `pre` runs after the
+// first NB are issued, so work that is independent of x (the first weight
+// loads) overlaps their latency.  Loads complete in order, so any x load
+// issued after `pre` would also wait for what `pre` requested: NB is chosen
+// so that the first batch covers all of x whenever it fits in 16 loads per
+// thread.  K is a multiple of 32 (K >= 32), so a lane group is either wholly
+// inside [0, K) or wholly outside.
 struct NoPre {
     __device__ void operator()() const {}
 };
-template <class F, class Pre = NoPre>
-__device__ __forceinline__ void stage_x(const float *__restrict__ x, int K, float *xs,
-                                        float *sums, Pre pre = Pre()) {
+template <class F, int NB, class Pre>
+__device__ __forceinline__ void stage_x_nb(const BufSrc &xv, int K, float *xs, float *sums,
+                                           Pre &pre) {
     const int nt = blockDim.x;
-    // unconditional loads through a view of x (past K they read zeros), so
-    // no branch makes the compiler wait for them early
-    const BufSrc xv(reinterpret_cast<const uint8_t *>(x), (uint64_t)K * 4);
     auto batch = [&](int base0, bool first) {
         const int base = base0 + (int)threadIdx.x * 4;
-        float4 v[8];
+        float4 v[NB];
 #pragma unroll
-        for (int j = 0; j < 8; j++)
+        for (int j = 0; j < NB; j++)
             v[j] = __builtin_bit_cast(float4, xv.ld16((uint32_t)(base + j * nt * 4) * 4u));
         if (first) pre();
 #pragma unroll
-        for (int j = 0; j < 8; j++) {
+        for (int j = 0; j < NB; j++) {
             const int i = base + j * nt * 4;
             put_x4<F>(xs, sums, i, i < K, v[j]);
         }
@@ -136,7 +139,23 @@ __device__ __forceinline__ void stage_x(const float *__restrict__ x, int K, floa
     // loads do not cover the loads `pre` issues after them); the loop over
     // the rest is uniform over the workgroup
     batch(0, true);
-    for (int base0 = nt * 4 * 8; base0 < K; base0 += nt * 4 * 8) batch(base0, false);
+    for (int base0 = nt * 4 * NB; base0 < K; base0 += nt * 4 * NB) batch(base0, false);
+}
+template <class F, class Pre = NoPre>
+__device__ __forceinline__ void stage_x(const float *__restrict__ x, int K, float *xs,
+                                        float *sums, Pre pre = Pre()) {
+    // unconditional loads through a view of x (past K they read zeros), so
+    // no branch makes the compiler wait for them early
+    const BufSrc xv(reinterpret_cast<const uint8_t *>(x), (uint64_t)K * 4);
+    const int per_thread = (K + (int)blockDim.x * 4 - 1) / ((int)blockDim.x * 4);
+    if (per_thread <= 2)
+        stage_x_nb<F, 2>(xv, K, xs, sums, pre);
+    else if (per_thread <= 4)
+        stage_x_nb<F, 4>(xv, K, xs, sums, pre);
+    else if (per_thread <= 8)
+        stage_x_nb<F, 8>(xv, K, xs, sums, pre);
+    else
+        stage_x_nb<F, 16>(xv, K, xs, sums, pre);
     __syncthreads();
 }
 
@@ -253,24 +272,27 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
         const int r0 = t * kRowsPerTile;
         const uint8_t *base;
         uint64_t avail;
+        // A wave without items still issues its first loads (see the staging
+        // below): past the end the view is empty and reads zeros.
+        const bool live = r0 < p.M;
         if (MODE == kModeMoeGateUp) {
             // the tile's rows belong to one selected expert
-            const int slot = r0 / p.moe.rows_per_mat;
+            int slot = r0 / p.moe.rows_per_mat;
+            slot = slot < p.moe.k ? slot : p.moe.k - 1;
             const int rin = r0 - slot * p.moe.rows_per_mat;
             const int ex = __builtin_amdgcn_readfirstlane(sel[slot]);  // uniform
             base = p.W + (int64_t)ex * p.moe.mat_bytes + (int64_t)rin * rb;
-            avail = (uint64_t)(p.moe.rows_per_mat - rin) * rb;
+            avail = live ? (uint64_t)(p.moe.rows_per_mat - rin) * rb : 0;
         } else if (MODE == kModeMoeDown) {
-            const int slot = step_slot(it);
+            int slot = step_slot(it);
+            slot = slot < p.moe.k ? slot : p.moe.k - 1;
             ustep -= slot * p.moe.units_per_mat;
             const int ex = __builtin_amdgcn_readfirstlane(sel[slot]);  // uniform
             base = p.W + (int64_t)ex * p.moe.mat_bytes + (int64_t)r0 * rb;
-            avail = (uint64_t)(p.M - r0) * rb;
+            avail = live ? (uint64_t)(p.M - r0) * rb : 0;
         } else {
-            // a wave without items still issues its first loads (see the
-            // staging below): past the end the view is empty and reads zeros
             base = p.W + (int64_t)r0 * rb;
-            avail = p.M > r0 ? (uint64_t)(p.M - r0) * rb : 0;
+            avail = live ? (uint64_t)(p.M - r0) * rb : 0;
         }
         const BufSrc src(base, avail);
         // unit g + ustep: ustep is a multiple of 4, so the position inside a
@@ -377,37 +399,55 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
     const int my_tiles = t_first < ntiles ? (ntiles - 1 - t_first) / tile_stride + 1 : 0;
     const int steps = (iters - it0 + KS - 1) / KS;  // this wave's steps per tile
     const int n_items = my_tiles * steps;
-    typename F::Regs bufA[R], bufB[R];
-    int tA = t_first;
-    int itA = it0;
+    // ring of D register sets: D - 1 items' loads stay in flight while one
+    // is multiplied
+    constexpr int D = kPipeDepth;
+    typename F::Regs buf[D][R];
+    int ring_t[D], ring_it[D];  // the item each set holds (wave-uniform)
+    ring_t[0] = t_first;
+    ring_it[0] = it0;
+    auto& bufA = buf[0];
+    int &tA = ring_t[0], &itA = ring_it[0];
 
     if (MODE == kModeMoeGateUp) {
-        // each wave selects the experts itself and requests its first weights
-        // before x is staged
-        moe_select(p.moe, sel, wsel);
-        if (n_items > 0) issue(bufA, tA, itA);
-        stage_x<F>(p.x, p.K, xs, sums);
+        // After the first activation loads are issued, each wave selects the
+        // experts itself and requests its first weights; the activation
+        // stores then wait only for x (loads complete in order).
+        stage_x<F>(p.x, p.K, xs, sums, [&]() {
+            moe_select(p.moe, sel, wsel);
+            issue(bufA, tA, itA);
+        });
     } else if (MODE == kModeMoeDown) {
         if ((int)threadIdx.x < p.moe.k) {
             sel[threadIdx.x] = p.moe.topk_idx[threadIdx.x];
             wsel[threadIdx.x] = p.moe.topk_w[threadIdx.x];
         }
         __syncthreads();
-        // the first weights are requested before the activations are formed
-        if (n_items > 0) issue(bufA, tA, itA);
         // x[s*I + j] = w_s * silu(g_s[j]) * u_s[j]; workgroup 0 keeps h.
         // K = k*I is a multiple of 32, so sum groups never straddle slots.
+        // The gate/up values of the first pass are loaded before the first
+        // weights are requested, as in stage_x.
         const int I = p.moe.I, K = p.K;
-        for (int base = threadIdx.x * 4; base < K; base += blockDim.x * 4) {
-            const int s = base / I, j = base - s * I;
-            const float4 gg = *reinterpret_cast<const float4 *>(p.moe.gu + (int64_t)s * 2 * I + j);
-            const float4 uu = *reinterpret_cast<const float4 *>(p.moe.gu + (int64_t)s * 2 * I + I + j);
+        const int nt = blockDim.x;
+        const BufSrc gv(reinterpret_cast<const uint8_t *>(p.moe.gu), (uint64_t)p.moe.k * 2 * I * 4);
+        auto pass = [&](int base0, bool first) {
+            const int base = base0 + (int)threadIdx.x * 4;
+            const int sl = base < K ? base / I : 0, j = base - sl * I;
+            const uint32_t off = (uint32_t)(sl * 2 * I + j) * 4u;
+            const float4 gg = __builtin_bit_cast(float4, gv.ld16(off));
+            const float4 uu = __builtin_bit_cast(float4, gv.ld16(off + (uint32_t)I * 4u));
+            if (first) {
+                issue(bufA, tA, itA);
+                __builtin_amdgcn_sched_barrier(0);
+            }
             const float4 h = make_float4(siluf(gg.x) * uu.x, siluf(gg.y) * uu.y,
                                          siluf(gg.z) * uu.z, siluf(gg.w) * uu.w);
-            if (blockIdx.x == 0) *reinterpret_cast<float4 *>(p.moe.h + base) = h;
-            const float w = wsel[s];
-            put_x4<F>(xs, sums, base, true, make_float4(w * h.x, w * h.y, w * h.z, w * h.w));
-        }
+            if (blockIdx.x == 0 && base < K) *reinterpret_cast<float4 *>(p.moe.h + base) = h;
+            const float w = wsel[sl];
+            put_x4<F>(xs, sums, base, base < K, make_float4(w * h.x, w * h.y, w * h.z, w * h.w));
+        };
+        pass(0, true);
+        for (int base0 = nt * 4; base0 < K; base0 += nt * 4) pass(base0, false);
         __syncthreads();
     } else {
         // the first item's weights are requested right after the first
@@ -420,30 +460,39 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
     }
     const float inv_unit = fp8_unit_inverse();
 
-    // Both issues of an iteration are unconditional (past the end they repeat
-    // the last item's addresses, which hit in L2), so the compiler's wait
-    // counters never have to merge "maybe issued" states and each consume
-    // waits only for its own loads.
+    // Every issue is unconditional (past the last item it repeats that
+    // item's addresses, which hit in L2), so the compiler's wait counters
+    // never have to merge "maybe issued" states and each consume waits only
+    // for its own loads.  Item q + 1 follows item q: the next unit step of
+    // the tile, or the first step of the wave's next tile.
+    int t_last = t_first, it_last = it0, q_last = 0;  // the newest issued item
+    auto next_item = [&]() {
+        if (q_last + 1 < n_items) {
+            q_last++;
+            if ((it_last += KS) >= iters) {
+                it_last = it0;
+                t_last += tile_stride;
+            }
+        }
+    };
+#pragma unroll
+    for (int j = 1; j < D - 1; j++) {
+        next_item();
+        ring_t[j] = t_last;
+        ring_it[j] = it_last;
+        issue(buf[j], t_last, it_last);
+    }
     if (n_items > 0) {
-        for (int k = 0; k < n_items; k += 2) {
-            int tB = tA;
-            int itB = itA;
-            if (k + 1 < n_items && (itB += KS) >= iters) {
-                itB = it0;
-                tB += tile_stride;
+        for (int k = 0; k < n_items; k += D) {
+#pragma unroll
+            for (int j = 0; j < D; j++) {
+                const int jn = (j + D - 1) % D;  // the set consumed one step ago
+                next_item();
+                ring_t[jn] = t_last;
+                ring_it[jn] = it_last;
+                issue(buf[jn], t_last, it_last);
+                if (k + j < n_items) consume(buf[j], inv_unit, ring_t[j], ring_it[j]);
             }
-            issue(bufB, tB, itB);
-            consume(bufA, inv_unit, tA, itA);
-            int tC = tB;
-            int itC = itB;
-            if (k + 2 < n_items && (itC += KS) >= iters) {
-                itC = it0;
-                tC += tile_stride;
-            }
-            issue(bufA, tC, itC);
-            if (k + 1 < n_items) consume(bufB, inv_unit, tB, itB);
-            tA = tC;
-            itA = itC;
         }
     }
 
