@@ -92,18 +92,21 @@ __device__ __forceinline__ float sbyte(uint32_t v) {
     return (float)(int32_t)(int8_t)((v >> (8 * B)) & 0xFFu);
 }
 
-// Four bytes of v, each holding a value 0..15, to f32 scaled by 2^-9.
-// A byte 0000qqqq read as an OCP fp8 e4m3 code is a subnormal (q < 8) or lies
-// in the first normal binade (q >= 8); both cases decode to exactly q * 2^-9,
-// so one conversion instruction turns two nibbles into two floats.
-__device__ __forceinline__ void nib4_to_f32_x512(uint32_t v, float &a, float &b, float &c,
-                                                 float &d) {
-    f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(v, false);
-    f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(v, true);
-    a = lo.x;
-    b = lo.y;
-    c = hi.x;
-    d = hi.y;
+// Codes as f16 subnormals.  A 16-bit half whose bits 10..15 are zero is the
+// f16 subnormal (bits) * 2^-24, exactly; converting it to f32 is exact, and
+// the compiler folds that conversion into the multiply-add (v_fma_mix_f32
+// reads an f16 half of a register as one operand), so one instruction both
+// converts a code and accumulates its product with an f32 activation.
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+constexpr float kTwo24 = 16777216.0f;  // 2^24: undoes the subnormal scale
+
+__device__ __forceinline__ f16x2_t as_f16x2(uint32_t v) { return __builtin_bit_cast(f16x2_t, v); }
+// Bytes 0 and 1 (resp. 2 and 3) of v moved to the low byte of each half.
+__device__ __forceinline__ uint32_t bytes01_to_halves(uint32_t v) {
+    return __builtin_amdgcn_perm(0u, v, 0x0c010c00u);
+}
+__device__ __forceinline__ uint32_t bytes23_to_halves(uint32_t v) {
+    return __builtin_amdgcn_perm(0u, v, 0x0c030c02u);
 }
 
 // Sum over groups of G consecutive lanes (G a power of two, 4..64), with DPP

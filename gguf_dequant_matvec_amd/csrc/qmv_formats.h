@@ -68,26 +68,31 @@ struct Q4K {
             xv[4 * i + 3] = v.w;
         }
     }
-    // acc += sum over the unit's 64 weights of w * x.
+    // acc += sum over the unit's 64 weights of w * x.  Byte 32c + l of the
+    // unit's nibbles holds weight l (low nibble) and weight 32 + l (high
+    // nibble) of sub-blocks 2c and 2c + 1; each pair of bytes is spread into
+    // the halves of a dword, whose low nibbles are then two f16 subnormals
+    // q * 2^-24 and whose high nibbles (masked in place) are 16 q * 2^-24.
     __device__ static __forceinline__ void dot(const Regs &r, const float *xv, const float *sums,
-                                               int u, float inv_unit, float &acc) {
+                                               int u, float &acc) {
         const uint32_t qw[8] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w};
         float lo0 = 0.f, lo1 = 0.f, hi0 = 0.f, hi1 = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-            float a0, a1, a2, a3, b0, b1, b2, b3;
-            nib4_to_f32_x512(qw[i] & 0x0F0F0F0Fu, a0, a1, a2, a3);
-            nib4_to_f32_x512((qw[i] >> 4) & 0x0F0F0F0Fu, b0, b1, b2, b3);
-            lo0 = fmaf(a0, xv[4 * i + 0], lo0);
-            lo1 = fmaf(a1, xv[4 * i + 1], lo1);
-            lo0 = fmaf(a2, xv[4 * i + 2], lo0);
-            lo1 = fmaf(a3, xv[4 * i + 3], lo1);
-            hi0 = fmaf(b0, xv[32 + 4 * i + 0], hi0);
-            hi1 = fmaf(b1, xv[32 + 4 * i + 1], hi1);
-            hi0 = fmaf(b2, xv[32 + 4 * i + 2], hi0);
-            hi1 = fmaf(b3, xv[32 + 4 * i + 3], hi1);
+            const uint32_t p01 = bytes01_to_halves(qw[i]), p23 = bytes23_to_halves(qw[i]);
+            const f16x2_t a01 = as_f16x2(p01 & 0x000F000Fu), a23 = as_f16x2(p23 & 0x000F000Fu);
+            const f16x2_t b01 = as_f16x2(p01 & 0x00F000F0u), b23 = as_f16x2(p23 & 0x00F000F0u);
+            lo0 = fmaf((float)a01.x, xv[4 * i + 0], lo0);
+            lo1 = fmaf((float)a01.y, xv[4 * i + 1], lo1);
+            lo0 = fmaf((float)a23.x, xv[4 * i + 2], lo0);
+            lo1 = fmaf((float)a23.y, xv[4 * i + 3], lo1);
+            hi0 = fmaf((float)b01.x, xv[32 + 4 * i + 0], hi0);
+            hi1 = fmaf((float)b01.y, xv[32 + 4 * i + 1], hi1);
+            hi0 = fmaf((float)b23.x, xv[32 + 4 * i + 2], hi0);
+            hi1 = fmaf((float)b23.y, xv[32 + 4 * i + 3], hi1);
         }
-        const float alo = lo0 + lo1, ahi = hi0 + hi1;
+        // both sums at the scale 2^-24 (the high nibbles carried 16 q)
+        const float alo = lo0 + lo1, ahi = (hi0 + hi1) * 0.0625f;
         // 6-bit scale and min of sub-blocks 2c and 2c+1, as two bytes each
         // (both decodings are formed and one is selected: no branch).
         const int c = u & 3;
@@ -98,7 +103,7 @@ struct Q4K {
         const uint32_t m_hi = ((s2 >> 4) & 0x0F0Fu) | ((s1 >> 2) & 0x3030u);
         const uint32_t sc = c < 2 ? sc_lo : sc_hi;
         const uint32_t m = c < 2 ? m_lo : m_hi;
-        const float d = half_bits_to_float(r.hdr.x) * inv_unit;
+        const float d = half_bits_to_float(r.hdr.x) * kTwo24;
         const float dmin = half_bits_to_float(r.hdr.x >> 16);
         const float t = fmaf(ubyte<1>(sc), ahi, ubyte<0>(sc) * alo);
         const float mm = fmaf(ubyte<1>(m), sums[2 * u + 1], ubyte<0>(m) * sums[2 * u]);
@@ -156,8 +161,10 @@ struct Q6K {
             }
         }
     }
+    // The 6-bit codes of four sub-blocks are assembled bytewise, then spread
+    // two per dword into f16 subnormals (q * 2^-24) for the multiply-adds.
     __device__ static __forceinline__ void dot(const Regs &r, const float *xv, const float *sums,
-                                               int u, float /*inv_unit*/, float &acc) {
+                                               int u, float &acc) {
         const uint32_t qa[4] = {r.qa.x, r.qa.y, r.qa.z, r.qa.w};
         const uint32_t qb[4] = {r.qb.x, r.qb.y, r.qb.z, r.qb.w};
         const uint32_t qh[4] = {r.qh.x, r.qh.y, r.qh.z, r.qh.w};
@@ -173,10 +180,12 @@ struct Q6K {
             };
 #pragma unroll
             for (int g = 0; g < 4; g++) {
-                A[g] = fmaf(ubyte<0>(q[g]), xv[16 * g + 4 * i + 0], A[g]);
-                A[g] = fmaf(ubyte<1>(q[g]), xv[16 * g + 4 * i + 1], A[g]);
-                A[g] = fmaf(ubyte<2>(q[g]), xv[16 * g + 4 * i + 2], A[g]);
-                A[g] = fmaf(ubyte<3>(q[g]), xv[16 * g + 4 * i + 3], A[g]);
+                const f16x2_t c01 = as_f16x2(bytes01_to_halves(q[g]));
+                const f16x2_t c23 = as_f16x2(bytes23_to_halves(q[g]));
+                A[g] = fmaf((float)c01.x, xv[16 * g + 4 * i + 0], A[g]);
+                A[g] = fmaf((float)c01.y, xv[16 * g + 4 * i + 1], A[g]);
+                A[g] = fmaf((float)c23.x, xv[16 * g + 4 * i + 2], A[g]);
+                A[g] = fmaf((float)c23.y, xv[16 * g + 4 * i + 3], A[g]);
             }
         }
         // sub-block of group g is 8n + 2g + h: its scale is byte 2g + h of the
@@ -186,10 +195,11 @@ struct Q6K {
         const int sbase = 16 * (u >> 2) + 8 * ((u >> 1) & 1) + h;
         const uint32_t w0 = r.sc.x >> (8 * h), w1 = r.sc.y >> (8 * h);
         float t = 0.f;
-        t = fmaf(sbyte<0>(w0), fmaf(-32.f, sums[sbase + 0], A[0]), t);
-        t = fmaf(sbyte<2>(w0), fmaf(-32.f, sums[sbase + 2], A[1]), t);
-        t = fmaf(sbyte<0>(w1), fmaf(-32.f, sums[sbase + 4], A[2]), t);
-        t = fmaf(sbyte<2>(w1), fmaf(-32.f, sums[sbase + 6], A[3]), t);
+        // A[g] * 2^24 is the code sum exactly (power-of-two scaling)
+        t = fmaf(sbyte<0>(w0), fmaf(A[0], kTwo24, -32.f * sums[sbase + 0]), t);
+        t = fmaf(sbyte<2>(w0), fmaf(A[1], kTwo24, -32.f * sums[sbase + 2]), t);
+        t = fmaf(sbyte<0>(w1), fmaf(A[2], kTwo24, -32.f * sums[sbase + 4]), t);
+        t = fmaf(sbyte<2>(w1), fmaf(A[3], kTwo24, -32.f * sums[sbase + 6]), t);
         acc = fmaf(half_bits_to_float(r.d), t, acc);
     }
 };
@@ -222,7 +232,7 @@ struct Q80x2 {
         Q4K::load_x(xs, u, xv);
     }
     __device__ static __forceinline__ void dot(const Regs &r, const float *xv, const float *,
-                                               int, float, float &acc) {
+                                               int, float &acc) {
         const uint32_t D[17] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w,
                                 r.c.x, r.c.y, r.c.z, r.c.w, r.d.x, r.d.y, r.d.z, r.d.w, r.e};
         // block 0: d in D0 bytes 0-1, q[0..1] in D0 bytes 2-3, q[2..29] in
@@ -285,7 +295,7 @@ struct Q80x1 {
         }
     }
     __device__ static __forceinline__ void dot(const Regs &r, const float *xv, const float *,
-                                               int, float, float &acc) {
+                                               int, float &acc) {
         const uint32_t D[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
         float a0 = 0.f, a1 = 0.f;
 #pragma unroll

@@ -196,13 +196,6 @@ __device__ __forceinline__ void moe_select(const MoeArgs &m, int32_t *sel, float
     }
 }
 
-__device__ __forceinline__ float fp8_unit_inverse() {
-    // value of fp8 code 0x01 is the smallest subnormal step (2^-9 for OCP
-    // e4m3); nibble products are scaled back by its exact inverse.
-    f32x2 v = __builtin_amdgcn_cvt_pk_f32_fp8(1u, false);
-    return 1.0f / v.x;
-}
-
 // KS = 1: each wave owns whole tiles.  KS = 4: the four waves of a workgroup
 // share each tile, wave w taking unit steps w, w + 4, ... (needs at least 4
 // steps per row); their per-row partial sums meet in LDS and are added in
@@ -372,21 +365,21 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
             }
         }
     };
-    auto consume = [&](typename F::Regs(&src)[R], const float inv_unit, int t, int it) {
+    auto consume = [&](typename F::Regs(&src)[R], int t, int it) {
         t = __builtin_amdgcn_readfirstlane(t);
         it = __builtin_amdgcn_readfirstlane(it);
         const int u = g + G * it;
         if (u < U) {
             if constexpr (XR) {
 #pragma unroll
-                for (int r = 0; r < R; r++) F::dot(src[r], xr, sums, u, inv_unit, acc[r]);
+                for (int r = 0; r < R; r++) F::dot(src[r], xr, sums, u, acc[r]);
             } else {
                 float xv[F::kUnitWeights];
                 F::load_x(xs, u, xv);
                 // u indexes the (concatenated) x and its sums; the block-internal
                 // position only depends on u mod 4, the same inside each expert
 #pragma unroll
-                for (int r = 0; r < R; r++) F::dot(src[r], xv, sums, u, inv_unit, acc[r]);
+                for (int r = 0; r < R; r++) F::dot(src[r], xv, sums, u, acc[r]);
             }
         }
         if (it + KS >= iters) finish_tile(t);  // this wave's last step of the tile
@@ -458,21 +451,18 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
         stage_x<F>(p.x, p.K, xs, sums, [&]() { issue(bufA, tA, itA); });
         if constexpr (XR) F::load_x(xs, g < U ? g : 0, xr);
     }
-    const float inv_unit = fp8_unit_inverse();
 
-    // Every issue is unconditional (past the last item it repeats that
-    // item's addresses, which hit in L2), so the compiler's wait counters
-    // never have to merge "maybe issued" states and each consume waits only
-    // for its own loads.  Item q + 1 follows item q: the next unit step of
-    // the tile, or the first step of the wave's next tile.
-    int t_last = t_first, it_last = it0, q_last = 0;  // the newest issued item
+    // Every issue is unconditional, so the compiler's wait counters never
+    // have to merge "maybe issued" states and each consume waits only for its
+    // own loads.  Item q + 1 follows item q: the next unit step of the tile,
+    // or the first step of the wave's next tile.  Past the wave's last item
+    // the next tile lies past the last one, whose rows start at or after M:
+    // those issues read through an empty view (zeros, no memory traffic).
+    int t_last = t_first, it_last = it0;  // the newest issued item
     auto next_item = [&]() {
-        if (q_last + 1 < n_items) {
-            q_last++;
-            if ((it_last += KS) >= iters) {
-                it_last = it0;
-                t_last += tile_stride;
-            }
+        if ((it_last += KS) >= iters) {
+            it_last = it0;
+            t_last += tile_stride;
         }
     };
 #pragma unroll
@@ -491,7 +481,7 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
                 ring_t[jn] = t_last;
                 ring_it[jn] = it_last;
                 issue(buf[jn], t_last, it_last);
-                if (k + j < n_items) consume(buf[j], inv_unit, ring_t[j], ring_it[j]);
+                if (k + j < n_items) consume(buf[j], ring_t[j], ring_it[j]);
             }
         }
     }
