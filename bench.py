@@ -311,6 +311,25 @@ def extras(torch, q, synth, step, progress):
         del Y, wsn
     progress("extras: verify done")
 
+    # gate+up with the gated product h = silu(g) * u in the same launch, over
+    # the 32 layers' gate+up stacks (2.1 GB, cold by rotation); the plain
+    # fused gate+up over the same stacks for comparison
+    Ig = step.gu_rows[0]
+    hg = torch.empty(Ig, device=dev)
+    ygu = [torch.empty(m, device=dev) for m in step.gu_rows]
+    per = {}
+    for name, fn in (("silu", lambda lay: q.qmv_gate_up_silu("q4_k", lay["gu"], Ig, Hs, step.x_h, hg)),
+                     ("fused", lambda lay: q.qmv_fused_rows("q4_k", lay["gu"], Hs, step.x_h,
+                                                            step.gu_rows, ygu))):
+        calls = [lambda lay=lay, fn=fn: fn(lay) for lay in step.layers]
+        per[name] = graph_time_us(torch, calls, reps=5)
+    gbytes = step.layers[0]["gu"].numel()
+    r = rec(per["silu"], gbytes + 4 * Hs + 4 * Ig, per="call (32 stacks in turn)")
+    r["fused_rows_same_stacks_us"] = round(per["fused"], 3)
+    out["gate_up_silu_28672x4096"] = r
+    del hg, ygu
+    progress("extras: gated gate+up done")
+
     # Q6_K output projection as a plain matvec (logits written), and a
     # supplementary cold Q8_0 stream at the decode-step scale
     V = step.vocab

@@ -35,7 +35,8 @@ STATUS = {0: "QMV_OK", 1: "QMV_EINVAL", 2: "QMV_ESHAPE", 3: "QMV_EALIGN",
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmv.so")
 
 # every symbol include/qmv.h declares
-EXPORTS = ["qmv_q8_0", "qmv_q4_k", "qmv_q6_k", "qmv_fused_rows", "qmv_argmax", "moe_qmv_topk",
+EXPORTS = ["qmv_q8_0", "qmv_q4_k", "qmv_q6_k", "qmv_fused_rows", "qmv_gate_up_silu", "qmv_argmax",
+           "moe_qmv_topk",
            "qmv_gemm_n", "qmv_dequant", "qmv_quantize", "qmv_row_bytes", "qmv_workspace_bytes",
            "qmv_last_hip_error", "qmv_status_str", "qmv_probe_stream_read",
            "qmv_time_next_launch"]
@@ -71,6 +72,7 @@ def load():
         "qmv_q4_k": [P, i64, i64, P, P, P],
         "qmv_q6_k": [P, i64, i64, P, P, P],
         "qmv_fused_rows": [ci, P, i64, P, i32, P, P, P],
+        "qmv_gate_up_silu": [ci, P, i64, i64, P, P, P],
         "qmv_argmax": [ci, P, i64, i64, P, P, P, P, sz, P],
         "moe_qmv_topk": [P, i64, P, P, i32, i32, ci, P, ci, P, i64, P, P, P, P, sz, P],
         "qmv_gemm_n": [ci, P, i64, i64, i32, P, P, P, sz, P],
@@ -162,6 +164,10 @@ def qmv_fused_rows(t, blocks, K, x, seg_rows, y_seg, stream=None):
     ys = (ctypes.c_void_p * max(len(y_seg), 1))(*[_ptr(y) for y in y_seg])
     _call("qmv_fused_rows", _type(t), _ptr(blocks), K, _ptr(x), n,
           ctypes.cast(rows, ctypes.c_void_p), ctypes.cast(ys, ctypes.c_void_p), _stream(stream))
+
+
+def qmv_gate_up_silu(t, blocks, I, K, x, h, stream=None):
+    _call("qmv_gate_up_silu", _type(t), _ptr(blocks), I, K, _ptr(x), _ptr(h), _stream(stream))
 
 
 def qmv_argmax(t, blocks, M, K, x, idx_out, max_out, workspace, ws_bytes=None, stream=None):

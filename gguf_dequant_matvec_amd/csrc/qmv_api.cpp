@@ -179,6 +179,18 @@ qmv_status qmv_fused_rows(qmv_type t, const void *blocks, int64_t K, const float
     return from_hip(launch_rows_store(t, (const uint8_t *)blocks, total, K, x, seg, stream));
 }
 
+qmv_status qmv_gate_up_silu(qmv_type t, const void *blocks, int64_t I, int64_t K, const float *x,
+                            float *h, hipStream_t stream) {
+    if (I < 1 || I > 0x3FFFFFFFll) return QMV_ESHAPE;
+    qmv_status st = check_matrix(t, blocks, 2 * I, K);
+    if (st != QMV_OK) return st;
+    // the up row of a gate row is addressed by a 32-bit byte offset
+    if ((uint64_t)I * row_bytes_of(t, K) > 0x7FFFFFFFull) return QMV_ESHAPE;
+    if (!x || !h) return QMV_EINVAL;
+    if (!aligned(x, 16) || !aligned(h, 4)) return QMV_EALIGN;
+    return from_hip(launch_rows_silu(t, (const uint8_t *)blocks, I, K, x, h, stream));
+}
+
 qmv_status qmv_argmax(qmv_type t, const void *blocks, int64_t M, int64_t K, const float *x,
                       int32_t *idx_out, float *max_out, void *workspace, size_t ws_bytes,
                       hipStream_t stream) {

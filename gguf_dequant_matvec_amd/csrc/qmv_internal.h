@@ -55,6 +55,8 @@ hipError_t ensure_lds(const void *kernel, size_t bytes);
 
 hipError_t launch_rows_store(int type, const uint8_t *W, int64_t M, int64_t K, const float *x,
                              const SegTable &seg, hipStream_t s);
+hipError_t launch_rows_silu(int type, const uint8_t *W, int64_t I, int64_t K, const float *x,
+                            float *h, hipStream_t s);
 hipError_t launch_rows_argmax(int type, const uint8_t *W, int64_t M, int64_t K, const float *x,
                               uint64_t *partials, int32_t *idx_out, float *max_out,
                               hipStream_t s);

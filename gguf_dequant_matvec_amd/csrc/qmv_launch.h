@@ -64,7 +64,9 @@ hipError_t launch_typed(const RowsParams &p_in, hipStream_t s, int *grid_out) {
     // the MoE down launch needs unit steps that never straddle two experts
     const int G = MODE == kModeMoeDown ? pow2_divisor(p.moe.units_per_mat) : pick_group(U);
     const int iters = (U + G - 1) / G;
-    const int64_t rows_per_tile = (int64_t)rows_per_lane<MODE>() * (kWave / G);
+    // kModeSiluUp: the two row slots hold a gate row and its up row
+    const int64_t rows_per_tile =
+        (MODE == kModeSiluUp ? 1 : (int64_t)rows_per_lane<MODE>()) * (kWave / G);
     const int64_t ntiles = ((int64_t)p.M + rows_per_tile - 1) / rows_per_tile;
     const int waves = kBlockThreads / kWave;
     const size_t lds =
@@ -75,7 +77,7 @@ hipError_t launch_typed(const RowsParams &p_in, hipStream_t s, int *grid_out) {
     // other modes never split, so a row's result depends only on (format, K)
     // and fused rows and the argmax stay bit-identical to the plain matvec.
     // a row of one unit step keeps its activations in registers
-    constexpr bool kXrModes = MODE == kModeStore || MODE == kModeArgmax;
+    constexpr bool kXrModes = MODE == kModeStore || MODE == kModeArgmax || MODE == kModeSiluUp;
     KernelPtr<F, MODE> k = iters == 1 ? kernel_for_ks<F, MODE, 1, kXrModes>(G)
                                       : kernel_for_ks<F, MODE, 1, false>(G);
     hipError_t e = ensure_lds((const void *)k, lds);

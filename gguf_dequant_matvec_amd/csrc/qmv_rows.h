@@ -26,6 +26,12 @@
 //    w_s * silu(g_s) * u_s; one row sum is then the weighted expert mixture,
 //    formed in a fixed order.  G divides the units per expert, so the expert
 //    of each unit step is uniform too.
+//
+// kModeSiluUp (BebeLM page, section "核心算子": the gated FFN h = silu(g) * u;
+// FlareLLM page, section "推理层面的深度优化": gate and up as one stack): the
+// matrix is a stacked gate+up of 2M rows; a tile holds 64/G gate rows in row
+// slot 0 and the matching up rows, M further on, in slot 1, so the owner lane
+// of a row has both results and writes only h = silu(g) * u.
 #pragma once
 
 #include <stdint.h>
@@ -70,7 +76,7 @@ struct RowsParams {
     MoeArgs moe;
 };
 
-enum { kModeStore = 0, kModeArgmax = 1, kModeMoeGateUp = 2, kModeMoeDown = 3 };
+enum { kModeStore = 0, kModeArgmax = 1, kModeMoeGateUp = 2, kModeMoeDown = 3, kModeSiluUp = 4 };
 
 // Packed argmax key: larger value first, then lower index.
 __device__ __forceinline__ uint64_t argmax_key(float v, int32_t idx) {
@@ -220,7 +226,10 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
     const int sub = lane / G, g = lane % G;
     const int U = p.K / F::kUnitWeights;
     const int iters = (U + G - 1) / G;  // unit steps per row
-    constexpr int kRowsPerTile = R * P;
+    // kModeSiluUp: the two row slots are a gate row and its up row
+    constexpr bool kPair = MODE == kModeSiluUp;
+    static_assert(!kPair || R == 2, "gate and up slots");
+    constexpr int kRowsPerTile = kPair ? P : R * P;
     const int ntiles = (p.M + kRowsPerTile - 1) / kRowsPerTile;
     const int tile_stride = KS == 1 ? (int)gridDim.x * waves_per_block : (int)gridDim.x;
     const int it0 = KS == 1 ? 0 : wave;  // this wave's first unit step of a tile
@@ -233,7 +242,8 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
     // byte offset of row slot r inside a tile (rows of a tile are consecutive)
     uint32_t row_off[R];
 #pragma unroll
-    for (int r = 0; r < R; r++) row_off[r] = (uint32_t)(r * P + sub) * rb;
+    for (int r = 0; r < R; r++)
+        row_off[r] = (uint32_t)(kPair ? r * p.M + sub : r * P + sub) * rb;
     const uint32_t lane_uoff = F::unit_offset(g);
 
     float best_v = -__builtin_inff();
@@ -284,8 +294,9 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
             base = p.W + (int64_t)ex * p.moe.mat_bytes + (int64_t)r0 * rb;
             avail = live ? (uint64_t)(p.M - r0) * rb : 0;
         } else {
+            // kModeSiluUp: the view runs to the end of the up rows (2M rows)
             base = p.W + (int64_t)r0 * rb;
-            avail = live ? (uint64_t)(p.M - r0) * rb : 0;
+            avail = live ? (uint64_t)((kPair ? 2 * (int64_t)p.M : (int64_t)p.M) - r0) * rb : 0;
         }
         const BufSrc src(base, avail);
         // unit g + ustep: ustep is a multiple of 4, so the position inside a
@@ -323,7 +334,10 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
             }
         }
         const int r0 = t * kRowsPerTile;
-        if (MODE != kModeArgmax) {
+        if constexpr (kPair) {
+            const int row = r0 + sub;
+            if (owner && row < p.M) p.seg.y[0][row] = siluf(tot[0]) * tot[1];
+        } else if (MODE != kModeArgmax) {
             // segment of the tile's first row and the start of the next one:
             // compile-time indices over the table, all in scalar registers
             float *yb = p.seg.y[0];

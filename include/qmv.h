@@ -101,6 +101,18 @@ qmv_status qmv_fused_rows(qmv_type t, const void *blocks, int64_t K, const float
                           int32_t nseg, const int64_t *seg_rows, float *const *y_seg,
                           hipStream_t stream);
 
+/* ---- fused gate/up with the gated product: h[j] = silu(g_j) * u_j --------
+ * BebeLM page, section "核心算子" (the gated FFN: h = silu(g) * u feeds the
+ * down projection) and FlareLLM page, section "推理层面的深度优化" (gate and
+ * up as one fused row stack).  blocks: a stacked matrix of 2I rows x K
+ * columns in format t, rows 0..I-1 gate and I..2I-1 up (the fused gate+up
+ * layout).  x: f32[K]; h: f32[I] (device).  g_j and u_j equal, bit for bit,
+ * rows j and I + j of the single-token call on the stack; silu(v) =
+ * v / (1 + e^-v) in f32.  One launch; g and u are never written.  Needs
+ * I * row bytes < 2^31 (32-bit offsets between a gate row and its up row). */
+qmv_status qmv_gate_up_silu(qmv_type t, const void *blocks, int64_t I, int64_t K, const float *x,
+                            float *h, hipStream_t stream);
+
 /* ---- fused greedy argmax: the index and value of max_i (dequant(W) x)_i ---
  * FlareLLM page, section "推理层面的深度优化": at temperature 0 the next
  * token is found during the output projection, without a logits buffer.

@@ -66,6 +66,7 @@ def _load():
     lib.oracle_qmv_rows.argtypes = [ci, P, i64, i64, P, i64, P, P, P]
     lib.oracle_qmv.argtypes = [ci, P, i64, i64, P, P, P]
     lib.oracle_argmax.argtypes = [ci, P, i64, i64, P, P, P, P]
+    lib.oracle_gate_up_silu.argtypes = [ci, P, i64, i64, P, P, P, P, P, P]
     lib.oracle_gemm_n.argtypes = [ci, P, i64, i64, i32, P, P, P]
     lib.oracle_moe.argtypes = [P, i64, P, P, i32, i32, ci, P, ci, P, i64,
                                P, P, P, P, P, P, P, P, P]
@@ -158,6 +159,20 @@ def fused_rows(t, blocks: np.ndarray, K: int, x: np.ndarray, seg_rows):
         out.append(qmv(t, blocks[r0 * rb:(r0 + m) * rb], m, K, x))
         r0 += m
     return out
+
+
+def gate_up_silu(t, blocks: np.ndarray, I: int, K: int, x: np.ndarray):
+    """Gated FFN input from a stacked gate+up matrix of 2I rows (BebeLM page,
+    section "核心算子"): returns (h, g, u, a_g, a_u), all f64, with
+    h = silu(g) * u and a_g, a_u the rows' sum |w x|."""
+    t = _type(t)
+    blocks = np.ascontiguousarray(blocks, dtype=np.uint8)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    assert x.size == K and blocks.size >= 2 * I * row_bytes(t, K)
+    h, g, u, ag, au = (np.empty(I, dtype=np.float64) for _ in range(5))
+    _check(_load().oracle_gate_up_silu(t, _ptr(blocks), I, K, _ptr(x), _ptr(h), _ptr(g), _ptr(u),
+                                       _ptr(ag), _ptr(au)), "gate_up_silu")
+    return h, g, u, ag, au
 
 
 def argmax(t, blocks: np.ndarray, M: int, K: int, x: np.ndarray):

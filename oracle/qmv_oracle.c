@@ -435,6 +435,35 @@ int oracle_qmv(int type, const uint8_t *blocks, int64_t M, int64_t K, const floa
 }
 
 /* ------------------------------------------------------------------------- */
+/* Gated FFN input (BebeLM page, section "核心算子": h = silu(g) * u with the  */
+/* gate and up projections; FlareLLM page, section "推理层面的深度优化": gate  */
+/* and up stacked as one matrix): the stack has 2I rows, rows 0..I-1 gate and */
+/* I..2I-1 up; g_j = row j . x, u_j = row I+j . x (f64 as in the matvec),     */
+/* h_j = g_j / (1 + e^-g_j) * u_j.  g, u, a_g, a_u may be NULL.               */
+/* ------------------------------------------------------------------------- */
+
+int oracle_gate_up_silu(int type, const uint8_t *blocks, int64_t I, int64_t K, const float *x,
+                        double *h, double *g, double *u, double *a_g, double *a_u)
+{
+    if (I < 1 || !shape_ok(type, 2 * I, K) || !blocks || !x || !h) return -1;
+    float *wbuf = (float *)malloc((size_t)K * sizeof(float));
+    if (!wbuf) return -1;
+    size_t rb = row_bytes(type, K);
+    for (int64_t j = 0; j < I; j++) {
+        double gv, uv, ag, au;
+        dot_row(type, blocks + (size_t)j * rb, K, x, wbuf, &gv, &ag);
+        dot_row(type, blocks + (size_t)(I + j) * rb, K, x, wbuf, &uv, &au);
+        h[j] = gv / (1.0 + exp(-gv)) * uv;
+        if (g) g[j] = gv;
+        if (u) u[j] = uv;
+        if (a_g) a_g[j] = ag;
+        if (a_u) a_u[j] = au;
+    }
+    free(wbuf);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
 /* Greedy argmax of dequant(W) x: the lowest index among the maximal exact   */
 /* (f64) row results.  Also returns that row's value and its sum |w x|.      */
 /* ------------------------------------------------------------------------- */

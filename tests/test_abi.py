@@ -60,6 +60,10 @@ def test_shape_errors():
     assert status_of(q.qmv_gemm_n, "q4_k", A16, 4, 256, 17, A16, A16, A16, 1 << 20) == "QMV_ESHAPE"
     assert status_of(q.qmv_gemm_n, "q4_k", A16, 4, 256, 0, A16, A16, A16, 1 << 20) == "QMV_ESHAPE"
     assert status_of(q.qmv_fused_rows, "q4_k", A16, 256, A16, [4, 0], [A16, A16]) == "QMV_ESHAPE"
+    assert status_of(q.qmv_gate_up_silu, "q4_k", A16, 0, 256, A16, A16) == "QMV_ESHAPE"
+    assert status_of(q.qmv_gate_up_silu, "q4_k", A16, 8, 100, A16, A16) == "QMV_ESHAPE"
+    # a gate row and its up row must be < 2^31 bytes apart
+    assert status_of(q.qmv_gate_up_silu, "q8_0", A16, 1 << 20, 32768, A16, A16) == "QMV_ESHAPE"
 
 
 def test_pointer_and_type_errors():
@@ -68,12 +72,16 @@ def test_pointer_and_type_errors():
     assert status_of(q.qmv_dequant, 13, A16, 4, 256, A16) == "QMV_EINVAL"
     assert status_of(q.qmv_fused_rows, "q4_k", A16, 256, A16, [1] * 9, [A16] * 9) == "QMV_EINVAL"
     assert status_of(q.qmv_fused_rows, "q4_k", A16, 256, A16, [], []) == "QMV_EINVAL"
+    assert status_of(q.qmv_gate_up_silu, "q4_k", A16, 8, 256, A16, 0) == "QMV_EINVAL"
+    assert status_of(q.qmv_gate_up_silu, 13, A16, 8, 256, A16, A16) == "QMV_EINVAL"
 
 
 def test_alignment_errors():
     assert status_of(q.qmv_q4_k, A16 + 1, 4, 256, A16, A16) == "QMV_EALIGN"
     assert status_of(q.qmv_q4_k, A16, 4, 256, A16 + 4, A16) == "QMV_EALIGN"
     assert status_of(q.qmv_q4_k, A16, 4, 256, A16, A16 + 2) == "QMV_EALIGN"
+    assert status_of(q.qmv_gate_up_silu, "q4_k", A16, 8, 256, A16 + 4, A16) == "QMV_EALIGN"
+    assert status_of(q.qmv_gate_up_silu, "q4_k", A16, 8, 256, A16, A16 + 2) == "QMV_EALIGN"
 
 
 def test_workspace_errors():
