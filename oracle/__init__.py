@@ -21,13 +21,22 @@ import subprocess
 
 import numpy as np
 
+Q4_0 = 2
+Q4_1 = 3
+Q5_0 = 6
+Q5_1 = 7
 Q8_0 = 8
+Q8_1 = 9
 Q4_K = 12
+Q5_K = 13
 Q6_K = 14
-TYPES = {"q8_0": Q8_0, "q4_k": Q4_K, "q6_k": Q6_K}
+TYPES = {"q4_0": Q4_0, "q4_1": Q4_1, "q5_0": Q5_0, "q5_1": Q5_1, "q8_0": Q8_0, "q8_1": Q8_1,
+         "q4_k": Q4_K, "q5_k": Q5_K, "q6_k": Q6_K}
 
-BLOCK_WEIGHTS = {Q8_0: 32, Q4_K: 256, Q6_K: 256}
-BLOCK_BYTES = {Q8_0: 34, Q4_K: 144, Q6_K: 210}
+BLOCK_WEIGHTS = {Q4_0: 32, Q4_1: 32, Q5_0: 32, Q5_1: 32, Q8_0: 32, Q8_1: 32,
+                 Q4_K: 256, Q5_K: 256, Q6_K: 256}
+BLOCK_BYTES = {Q4_0: 18, Q4_1: 20, Q5_0: 22, Q5_1: 24, Q8_0: 34, Q8_1: 36,
+               Q4_K: 144, Q5_K: 176, Q6_K: 210}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "qmv_oracle.c")
@@ -71,7 +80,7 @@ def _load():
     lib.oracle_moe.argtypes = [P, i64, P, P, i32, i32, ci, P, ci, P, i64,
                                P, P, P, P, P, P, P, P, P]
     for name in ("oracle_dequant", "oracle_quantize", "oracle_qmv_rows", "oracle_qmv",
-                 "oracle_argmax", "oracle_gemm_n", "oracle_moe"):
+                 "oracle_argmax", "oracle_gate_up_silu", "oracle_gemm_n", "oracle_moe"):
         getattr(lib, name).restype = ci
     _lib = lib
     return lib

@@ -17,6 +17,11 @@
  *    the fields follow the standard GGUF conventions the pages say the engines
  *    load ("标准GGUF" row of the FlareLLM page's comparison table).  That is a
  *    reading, spelled out as index math at each decoder below.
+ *  - More block formats from the pages' lists: FlareLLM page, section
+ *    "量化技术的全面支持" names the standard 4- to 8-bit quantisations (Q4_0
+ *    through Q8_1) and the K-quants; the BebeLM page, section "局限与未来",
+ *    wants Q5_K_M.  Their layouts again follow the standard GGUF reading,
+ *    written out at each decoder below.
  *  - The matvec itself is the plain definition y = dequant(W) x, each product
  *    formed exactly in f64 and summed in order k = 0..K-1.
  *  - MoE routing: BebeLM page, section "核心算子" (MoE FFN: sigmoid router,
@@ -36,8 +41,14 @@
 #include <string.h>
 #include <stdlib.h>
 
+#define T_Q4_0 2
+#define T_Q4_1 3
+#define T_Q5_0 6
+#define T_Q5_1 7
 #define T_Q8_0 8
+#define T_Q8_1 9
 #define T_Q4_K 12
+#define T_Q5_K 13
 #define T_Q6_K 14
 
 /* ------------------------------------------------------------------------- */
@@ -102,9 +113,8 @@ static void wr16(uint8_t *p, uint16_t v) { p[0] = (uint8_t)(v & 255); p[1] = (ui
 int oracle_block_weights(int type)
 {
     switch (type) {
-    case T_Q8_0: return 32;
-    case T_Q4_K: return 256;
-    case T_Q6_K: return 256;
+    case T_Q4_0: case T_Q4_1: case T_Q5_0: case T_Q5_1: case T_Q8_0: case T_Q8_1: return 32;
+    case T_Q4_K: case T_Q5_K: case T_Q6_K: return 256;
     default: return 0;
     }
 }
@@ -112,8 +122,14 @@ int oracle_block_weights(int type)
 int oracle_block_bytes(int type)
 {
     switch (type) {
+    case T_Q4_0: return 18;   /* fp16 d + 16 B nibbles */
+    case T_Q4_1: return 20;   /* fp16 d, fp16 m + 16 B nibbles */
+    case T_Q5_0: return 22;   /* fp16 d, 4 B high bits, 16 B nibbles */
+    case T_Q5_1: return 24;   /* fp16 d, fp16 m, 4 B high bits, 16 B nibbles */
     case T_Q8_0: return 34;   /* fp16 d + 32 int8 */
+    case T_Q8_1: return 36;   /* fp16 d, fp16 s + 32 int8 */
     case T_Q4_K: return 144;  /* fp16 d, fp16 dmin, 12 B scales, 128 B nibbles */
+    case T_Q5_K: return 176;  /* fp16 d, fp16 dmin, 12 B scales, 32 B high bits, 128 B nibbles */
     case T_Q6_K: return 210;  /* 128 B low nibbles, 64 B high pairs, 16 int8 scales, fp16 d */
     default: return 0;
     }
@@ -205,11 +221,103 @@ static void decode_q6_k(const uint8_t *b, float *w)
     }
 }
 
+/* The 32-weight formats share one nibble order: byte l (0..15) of the code
+ * bytes holds weight l in its low nibble and weight l + 16 in its high
+ * nibble.  The 5-bit formats add bit i of a little-endian 32-bit word as bit
+ * 4 of weight i's code. */
+static int nibble32(const uint8_t *Q, int i) { return (Q[i % 16] >> (4 * (i / 16))) & 15; }
+static uint32_t rd32(const uint8_t *p)
+{
+    return (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24);
+}
+
+/* Q4_0: d at [0,2), codes at [2,18); weight i = d * (q_i - 8), exact. */
+static void decode_q4_0(const uint8_t *b, float *w)
+{
+    float d = oracle_half_to_float(rd16(b));
+    for (int i = 0; i < 32; i++)
+        w[i] = d * (float)(nibble32(b + 2, i) - 8);
+}
+
+/* Q4_1: d at [0,2), m at [2,4), codes at [4,20); weight i = d * q_i + m
+ * (the product is exact, the sum is the one rounding). */
+static void decode_q4_1(const uint8_t *b, float *w)
+{
+    float d = oracle_half_to_float(rd16(b)), m = oracle_half_to_float(rd16(b + 2));
+    for (int i = 0; i < 32; i++)
+        w[i] = d * (float)nibble32(b + 4, i) + m;
+}
+
+/* Q5_0: d at [0,2), high bits H at [2,6), codes at [6,22);
+ * q_i = nibble | bit_i(H) << 4, weight i = d * (q_i - 16), exact. */
+static void decode_q5_0(const uint8_t *b, float *w)
+{
+    float d = oracle_half_to_float(rd16(b));
+    uint32_t H = rd32(b + 2);
+    for (int i = 0; i < 32; i++) {
+        int q = nibble32(b + 6, i) | (int)(((H >> i) & 1u) << 4);
+        w[i] = d * (float)(q - 16);
+    }
+}
+
+/* Q5_1: d at [0,2), m at [2,4), high bits H at [4,8), codes at [8,24);
+ * weight i = d * q_i + m. */
+static void decode_q5_1(const uint8_t *b, float *w)
+{
+    float d = oracle_half_to_float(rd16(b)), m = oracle_half_to_float(rd16(b + 2));
+    uint32_t H = rd32(b + 4);
+    for (int i = 0; i < 32; i++) {
+        int q = nibble32(b + 8, i) | (int)(((H >> i) & 1u) << 4);
+        w[i] = d * (float)q + m;
+    }
+}
+
+/* Q8_1: d at [0,2), s at [2,4) (d times the code sum, kept for activation
+ * use; not part of the weight value), 32 signed codes at [4,36);
+ * weight i = d * q_i, exact. */
+static void decode_q8_1(const uint8_t *b, float *w)
+{
+    float d = oracle_half_to_float(rd16(b));
+    for (int i = 0; i < 32; i++)
+        w[i] = d * (float)(int8_t)b[4 + i];
+}
+
+/* Q5_K: d at [0,2), dmin at [2,4), packed scales S at [4,16) (the Q4_K
+ * packing), high bits QH at [16,48), nibbles Q at [48,176).  Weight i lies
+ * in 64-weight chunk c = i/64 with h = (i%64)/32 and l = i%32: its nibble is
+ * the low (h = 0) or high (h = 1) nibble of Q[32c + l], its fifth bit is bit
+ * 2c + h of QH[l], and sub-block j = i/32.  Weight value
+ * (d*sc_j)*q - (dmin*m_j), q in 0..31. */
+static void decode_q5_k(const uint8_t *b, float *w)
+{
+    float d = oracle_half_to_float(rd16(b));
+    float dmin = oracle_half_to_float(rd16(b + 2));
+    const uint8_t *S = b + 4, *QH = b + 16, *Q = b + 48;
+    for (int i = 0; i < 256; i++) {
+        int c = i / 64, h = (i % 64) / 32, l = i % 32;
+        int j = i / 32;
+        int sc, m;
+        int q = ((Q[32 * c + l] >> (4 * h)) & 15) | (((QH[l] >> (2 * c + h)) & 1) << 4);
+        q4k_scale_min(S, j, &sc, &m);
+        float s = d * (float)sc;
+        float o = dmin * (float)m;
+        w[i] = s * (float)q - o;
+    }
+}
+
 static void decode_block(int type, const uint8_t *b, float *w)
 {
-    if (type == T_Q8_0) decode_q8_0(b, w);
-    else if (type == T_Q4_K) decode_q4_k(b, w);
-    else decode_q6_k(b, w);
+    switch (type) {
+    case T_Q4_0: decode_q4_0(b, w); break;
+    case T_Q4_1: decode_q4_1(b, w); break;
+    case T_Q5_0: decode_q5_0(b, w); break;
+    case T_Q5_1: decode_q5_1(b, w); break;
+    case T_Q8_0: decode_q8_0(b, w); break;
+    case T_Q8_1: decode_q8_1(b, w); break;
+    case T_Q4_K: decode_q4_k(b, w); break;
+    case T_Q5_K: decode_q5_k(b, w); break;
+    default: decode_q6_k(b, w); break;
+    }
 }
 
 static void decode_row(int type, const uint8_t *row, int64_t K, float *w)
@@ -252,13 +360,15 @@ static void encode_q8_0(const float *w, uint8_t *b)
     }
 }
 
-/* Q4_K, per 32-weight sub-block j with lo_j = min(0, min w) and hi_j = max w:
+/* Q4_K and Q5_K, per 32-weight sub-block j with lo_j = min(0, min w) and
+ * hi_j = max w, for codes 0..top (top = 15 or 31):
  *   dmin = max_j(-lo_j)/62 -> fp16;  m_j = min(63, ceil(-lo_j/dmin16));
- *   L_j = -dmin16*m_j;  s_j = (hi_j - L_j)/15;  d = max_j s_j / 62 -> fp16;
- *   sc_j = min(63, ceil(s_j/d16));  q = clamp(round((w - L_j)/(d16*sc_j)), 0, 15).
+ *   L_j = -dmin16*m_j;  s_j = (hi_j - L_j)/top;  d = max_j s_j / 62 -> fp16;
+ *   sc_j = min(63, ceil(s_j/d16));  q = clamp(round((w - L_j)/(d16*sc_j)), 0, top).
  * The mins are fixed first so that each scale covers the offset that the
- * rounded min really produces. */
-static void encode_q4_k(const float *w, uint8_t *b)
+ * rounded min really produces.  Writes d, dmin and the packed scales (bytes
+ * 0..15, the layout both formats share) and returns the codes. */
+static void encode_kq_minmax(const float *w, int top, uint8_t *b, int *codes)
 {
     float lo[8], hi[8], L[8], s[8];
     int sc[8], m[8];
@@ -284,7 +394,7 @@ static void encode_q4_k(const float *w, uint8_t *b)
         }
         m[j] = mj;
         L[j] = -(dmin16 * (float)mj);
-        s[j] = (hi[j] - L[j]) / 15.0f;
+        s[j] = (hi[j] - L[j]) / (float)top;
         if (s[j] > maxs) maxs = s[j];
     }
     uint16_t d_h = oracle_float_to_half(maxs / 62.0f);
@@ -299,26 +409,160 @@ static void encode_q4_k(const float *w, uint8_t *b)
     }
     wr16(b, d_h);
     wr16(b + 2, dmin_h);
-    uint8_t *S = b + 4, *Q = b + 16;
+    uint8_t *S = b + 4;
     for (int j = 0; j < 4; j++) {
         S[j] = (uint8_t)((sc[j] & 63) | ((sc[j + 4] >> 4) << 6));
         S[j + 4] = (uint8_t)((m[j] & 63) | ((m[j + 4] >> 4) << 6));
         S[j + 8] = (uint8_t)((sc[j + 4] & 15) | ((m[j + 4] & 15) << 4));
     }
-    memset(Q, 0, 128);
     for (int i = 0; i < 256; i++) {
-        int j = i / 32;
+        int jj = i / 32;
         int q = 0;
-        if (sc[j] > 0) {
-            float step = d16 * (float)sc[j];
-            float t = roundf((w[i] - L[j]) / step);
+        if (sc[jj] > 0) {
+            float step = d16 * (float)sc[jj];
+            float t = roundf((w[i] - L[jj]) / step);
             if (t < 0.0f) t = 0.0f;
-            if (t > 15.0f) t = 15.0f;
+            if (t > (float)top) t = (float)top;
             q = (int)t;
         }
-        int c = i / 64, h = (i % 64) / 32, l = i % 32;
-        Q[32 * c + l] |= (uint8_t)(h ? (q << 4) : q);
+        codes[i] = q;
     }
+}
+
+static void encode_q4_k(const float *w, uint8_t *b)
+{
+    int codes[256];
+    encode_kq_minmax(w, 15, b, codes);
+    uint8_t *Q = b + 16;
+    memset(Q, 0, 128);
+    for (int i = 0; i < 256; i++) {
+        int c = i / 64, h = (i % 64) / 32, l = i % 32;
+        Q[32 * c + l] |= (uint8_t)(h ? (codes[i] << 4) : codes[i]);
+    }
+}
+
+static void encode_q5_k(const float *w, uint8_t *b)
+{
+    int codes[256];
+    encode_kq_minmax(w, 31, b, codes);
+    uint8_t *QH = b + 16, *Q = b + 48;
+    memset(QH, 0, 160);
+    for (int i = 0; i < 256; i++) {
+        int c = i / 64, h = (i % 64) / 32, l = i % 32;
+        Q[32 * c + l] |= (uint8_t)((codes[i] & 15) << (4 * h));
+        QH[l] |= (uint8_t)((codes[i] >> 4) << (2 * c + h));
+    }
+}
+
+/* 32-weight formats.  Symmetric ones (Q4_0, Q5_0, Q8_1): d = max|w| / half
+ * (half = 7, 15, 127) -> fp16, code = clamp(round(w/d16), -half-1, half)
+ * stored with its offset (8, 16, or as a signed byte).  Asymmetric ones
+ * (Q4_1, Q5_1): m = min w -> fp16, d = (max w - m16)/top -> fp16,
+ * q = clamp(round((w - m16)/d16), 0, top). */
+static void put_codes32(uint8_t *Q, uint8_t *H, const int *q)
+{
+    memset(Q, 0, 16);
+    uint32_t hb = 0;
+    for (int i = 0; i < 32; i++) {
+        Q[i % 16] |= (uint8_t)((q[i] & 15) << (4 * (i / 16)));
+        hb |= (uint32_t)((q[i] >> 4) & 1) << i;
+    }
+    if (H) {
+        H[0] = (uint8_t)hb;
+        H[1] = (uint8_t)(hb >> 8);
+        H[2] = (uint8_t)(hb >> 16);
+        H[3] = (uint8_t)(hb >> 24);
+    }
+}
+
+static void encode_sym32(const float *w, int half, uint16_t *d_h, int *q)
+{
+    float amax = 0.0f;
+    for (int i = 0; i < 32; i++)
+        if (fabsf(w[i]) > amax) amax = fabsf(w[i]);
+    *d_h = oracle_float_to_half(amax / (float)half);
+    float d16 = oracle_half_to_float(*d_h);
+    for (int i = 0; i < 32; i++) {
+        float t = d16 > 0.0f ? roundf(w[i] / d16) : 0.0f;
+        if (t < (float)(-half - 1)) t = (float)(-half - 1);
+        if (t > (float)half) t = (float)half;
+        q[i] = (int)t;
+    }
+}
+
+static void encode_asym32(const float *w, int top, uint16_t *d_h, uint16_t *m_h, int *q)
+{
+    float mn = w[0], mx = w[0];
+    for (int i = 1; i < 32; i++) {
+        if (w[i] < mn) mn = w[i];
+        if (w[i] > mx) mx = w[i];
+    }
+    *m_h = oracle_float_to_half(mn);
+    float m16 = oracle_half_to_float(*m_h);
+    *d_h = oracle_float_to_half((mx - m16) / (float)top);
+    float d16 = oracle_half_to_float(*d_h);
+    for (int i = 0; i < 32; i++) {
+        float t = d16 > 0.0f ? roundf((w[i] - m16) / d16) : 0.0f;
+        if (t < 0.0f) t = 0.0f;
+        if (t > (float)top) t = (float)top;
+        q[i] = (int)t;
+    }
+}
+
+static void encode_q4_0(const float *w, uint8_t *b)
+{
+    int q[32];
+    uint16_t d;
+    encode_sym32(w, 7, &d, q);
+    for (int i = 0; i < 32; i++) q[i] += 8;
+    wr16(b, d);
+    put_codes32(b + 2, NULL, q);
+}
+
+static void encode_q5_0(const float *w, uint8_t *b)
+{
+    int q[32];
+    uint16_t d;
+    encode_sym32(w, 15, &d, q);
+    for (int i = 0; i < 32; i++) q[i] += 16;
+    wr16(b, d);
+    put_codes32(b + 6, b + 2, q);
+}
+
+static void encode_q4_1(const float *w, uint8_t *b)
+{
+    int q[32];
+    uint16_t d, m;
+    encode_asym32(w, 15, &d, &m, q);
+    wr16(b, d);
+    wr16(b + 2, m);
+    put_codes32(b + 4, NULL, q);
+}
+
+static void encode_q5_1(const float *w, uint8_t *b)
+{
+    int q[32];
+    uint16_t d, m;
+    encode_asym32(w, 31, &d, &m, q);
+    wr16(b, d);
+    wr16(b + 2, m);
+    put_codes32(b + 8, b + 4, q);
+}
+
+/* Q8_1: as Q8_0 with d16 for the codes, plus s = d16 * sum(q) -> fp16. */
+static void encode_q8_1(const float *w, uint8_t *b)
+{
+    int q[32];
+    uint16_t d;
+    encode_sym32(w, 127, &d, q);
+    float d16 = oracle_half_to_float(d);
+    int sum = 0;
+    for (int i = 0; i < 32; i++) {
+        b[4 + i] = (uint8_t)(int8_t)q[i];
+        sum += q[i];
+    }
+    wr16(b, d);
+    wr16(b + 2, oracle_float_to_half(d16 * (float)sum));
 }
 
 /* Q6_K, per 16-weight sub-block j: s_j = max|w|/31; d = max_j s_j / 126 -> fp16;
@@ -374,9 +618,17 @@ int oracle_quantize(int type, const float *w, int64_t M, int64_t K, uint8_t *blo
     for (int64_t t = 0; t < nblk; t++) {
         const float *src = w + t * bw;
         uint8_t *dst = blocks_out + t * bb;
-        if (type == T_Q8_0) encode_q8_0(src, dst);
-        else if (type == T_Q4_K) encode_q4_k(src, dst);
-        else encode_q6_k(src, dst);
+        switch (type) {
+        case T_Q4_0: encode_q4_0(src, dst); break;
+        case T_Q4_1: encode_q4_1(src, dst); break;
+        case T_Q5_0: encode_q5_0(src, dst); break;
+        case T_Q5_1: encode_q5_1(src, dst); break;
+        case T_Q8_0: encode_q8_0(src, dst); break;
+        case T_Q8_1: encode_q8_1(src, dst); break;
+        case T_Q4_K: encode_q4_k(src, dst); break;
+        case T_Q5_K: encode_q5_k(src, dst); break;
+        default: encode_q6_k(src, dst); break;
+        }
     }
     return 0;
 }

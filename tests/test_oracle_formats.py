@@ -150,3 +150,81 @@ def test_quantiser_uses_every_code_level(t):
     span = ws.max(axis=1) - ws.min(axis=1)
     assert np.all(np.abs(whs.max(axis=1) - ws.max(axis=1)) <= span / 8)
     assert np.all(np.abs(whs.min(axis=1) - ws.min(axis=1)) <= span / 8)
+
+
+# ---------------------------------------------------------------------------
+# the 32-weight formats and Q5_K (FlareLLM page, section "量化技术的全面支持";
+# BebeLM page, section "局限与未来")
+# ---------------------------------------------------------------------------
+
+SYM = {"q4_0": 7, "q5_0": 15, "q8_1": 127}
+ASYM = {"q4_1": 15, "q5_1": 31}
+
+
+@pytest.mark.parametrize("t", sorted(SYM) + sorted(ASYM))
+def test_32_weight_round_trip(t):
+    """Symmetric rule: d = max|w| / half, codes round(w / d16); the error is
+    at most half a step.  Asymmetric rule: m = min w, d = (max - m16) / top;
+    the error is half a step plus what the fp16 rounding of m and d can push
+    past the clamped ends."""
+    w = synth.weights(15, 32, 2048)
+    wh = oracle.dequant(t, oracle.quantize(t, w), 32, 2048)
+    wb, whb = _blocks_of(w, 32), _blocks_of(wh, 32)
+    ulp = np.abs(wb).max(axis=1, keepdims=True) * 2.0 ** -22
+    if t in SYM:
+        d16 = np.abs(wb).max(axis=1, keepdims=True) / SYM[t] * (1 + EPS16)
+        bound = 0.5 * d16 + ulp
+    else:
+        mn, mx = wb.min(axis=1, keepdims=True), wb.max(axis=1, keepdims=True)
+        d16 = (mx - mn) * (1 + 2 * EPS16) / ASYM[t] + np.abs(mn) * EPS16
+        bound = 0.5 * d16 + 2 * (np.abs(mn) + (mx - mn)) * EPS16 + ulp
+    err = np.abs(wb - whb)
+    assert np.all(err <= bound), float((err - bound).max())
+    assert err.mean() > 1e-4 * np.abs(wb).mean()
+
+
+def test_q5_k_round_trip():
+    w = synth.weights(16, 64, 4096)
+    b = oracle.quantize("q5_k", w)
+    wh = oracle.dequant("q5_k", b, 64, 4096)
+    wsub, whsub = w.reshape(-1, 8, 32).astype(np.float64), wh.reshape(-1, 8, 32).astype(np.float64)
+    lo = np.minimum(0.0, wsub.min(axis=2))
+    hi = wsub.max(axis=2)
+    dmin16 = (-lo).max(axis=1, keepdims=True) / 62.0 * (1 + EPS16)
+    s = (hi - lo + dmin16) / 31.0
+    d16 = s.max(axis=1, keepdims=True) / 62.0 * (1 + EPS16)
+    step = s + d16
+    ulp = np.abs(wsub).max(axis=2) * 2.0 ** -23
+    bound = (0.5 * step + 4 * ulp)[:, :, None]
+    err = np.abs(wsub - whsub)
+    assert np.all(err <= bound), float((err - bound).max())
+    # finer than Q4_K on the same data: 31 levels instead of 15
+    e4 = np.abs(w - oracle.dequant("q4_k", oracle.quantize("q4_k", w), 64, 4096)).mean()
+    assert err.mean() < 0.7 * e4
+
+
+@pytest.mark.parametrize("t", ["q4_0", "q4_1", "q5_0", "q5_1", "q8_1", "q5_k"])
+def test_new_formats_zero_and_constant(t):
+    K = 256
+    z = np.zeros((2, K), dtype=np.float32)
+    assert not oracle.dequant(t, oracle.quantize(t, z), 2, K).any()
+    c = np.full((1, K), 0.0125, dtype=np.float32)
+    wh = oracle.dequant(t, oracle.quantize(t, c), 1, K)
+    assert np.allclose(wh, 0.0125, rtol=0, atol=0.0125 / 20)
+
+
+@pytest.mark.parametrize("t,lo,hi", [("q4_0", 1, 15), ("q5_0", 1, 31), ("q4_1", 0, 15),
+                                     ("q5_1", 0, 31), ("q5_k", 0, 31)])
+def test_new_formats_reach_the_extreme_codes(t, lo, hi):
+    """On N(0, 0.02) data every block reaches its extreme stored codes: the
+    symmetric rule maps +-max|w| to 8 -+ 7 (16 -+ 15), the others min and max
+    to 0 and the top code.  Codes are read back from the decoded values."""
+    w = synth.weights(17, 8, 1024)
+    b = oracle.quantize(t, w)
+    wh = oracle.dequant(t, b, 8, 1024).reshape(-1, 32).astype(np.float64)
+    ws = w.reshape(-1, 32).astype(np.float64)
+    # the extreme decoded values sit within one step of the inputs' extremes
+    span = ws.max(axis=1) - ws.min(axis=1)
+    assert np.all(np.abs(wh.max(axis=1) - ws.max(axis=1)) <= span / (hi - lo) * 1.01)
+    assert np.all(np.abs(wh.min(axis=1) - ws.min(axis=1)) <= span / (hi - lo) * 1.01 +
+                  (np.abs(ws).max(axis=1) / (hi // 2) if t in ("q4_0", "q5_0") else 0))
