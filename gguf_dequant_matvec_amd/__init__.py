@@ -15,12 +15,21 @@ from __future__ import annotations
 import ctypes
 import os
 
+Q4_0 = 2
+Q4_1 = 3
+Q5_0 = 6
+Q5_1 = 7
 Q8_0 = 8
+Q8_1 = 9
 Q4_K = 12
+Q5_K = 13
 Q6_K = 14
-TYPES = {"q8_0": Q8_0, "q4_k": Q4_K, "q6_k": Q6_K}
-BLOCK_WEIGHTS = {Q8_0: 32, Q4_K: 256, Q6_K: 256}
-BLOCK_BYTES = {Q8_0: 34, Q4_K: 144, Q6_K: 210}
+TYPES = {"q4_0": Q4_0, "q4_1": Q4_1, "q5_0": Q5_0, "q5_1": Q5_1, "q8_0": Q8_0, "q8_1": Q8_1,
+         "q4_k": Q4_K, "q5_k": Q5_K, "q6_k": Q6_K}
+BLOCK_WEIGHTS = {Q4_0: 32, Q4_1: 32, Q5_0: 32, Q5_1: 32, Q8_0: 32, Q8_1: 32,
+                 Q4_K: 256, Q5_K: 256, Q6_K: 256}
+BLOCK_BYTES = {Q4_0: 18, Q4_1: 20, Q5_0: 22, Q5_1: 24, Q8_0: 34, Q8_1: 36,
+               Q4_K: 144, Q5_K: 176, Q6_K: 210}
 
 OP_ARGMAX = 1
 OP_MOE = 2
@@ -35,7 +44,8 @@ STATUS = {0: "QMV_OK", 1: "QMV_EINVAL", 2: "QMV_ESHAPE", 3: "QMV_EALIGN",
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmv.so")
 
 # every symbol include/qmv.h declares
-EXPORTS = ["qmv_q8_0", "qmv_q4_k", "qmv_q6_k", "qmv_fused_rows", "qmv_gate_up_silu", "qmv_argmax",
+EXPORTS = ["qmv_q8_0", "qmv_q4_k", "qmv_q6_k", "qmv_q4_0", "qmv_q4_1", "qmv_q5_0", "qmv_q5_1",
+           "qmv_q8_1", "qmv_q5_k", "qmv_fused_rows", "qmv_gate_up_silu", "qmv_argmax",
            "moe_qmv_topk",
            "qmv_gemm_n", "qmv_dequant", "qmv_quantize", "qmv_row_bytes", "qmv_workspace_bytes",
            "qmv_last_hip_error", "qmv_status_str", "qmv_probe_stream_read",
@@ -71,6 +81,12 @@ def load():
         "qmv_q8_0": [P, i64, i64, P, P, P],
         "qmv_q4_k": [P, i64, i64, P, P, P],
         "qmv_q6_k": [P, i64, i64, P, P, P],
+        "qmv_q4_0": [P, i64, i64, P, P, P],
+        "qmv_q4_1": [P, i64, i64, P, P, P],
+        "qmv_q5_0": [P, i64, i64, P, P, P],
+        "qmv_q5_1": [P, i64, i64, P, P, P],
+        "qmv_q8_1": [P, i64, i64, P, P, P],
+        "qmv_q5_k": [P, i64, i64, P, P, P],
         "qmv_fused_rows": [ci, P, i64, P, i32, P, P, P],
         "qmv_gate_up_silu": [ci, P, i64, i64, P, P, P],
         "qmv_argmax": [ci, P, i64, i64, P, P, P, P, sz, P],
@@ -153,9 +169,33 @@ def qmv_q6_k(blocks, M, K, x, y, stream=None):
 
 
 def qmv(t, blocks, M, K, x, y, stream=None):
-    """Dispatch to qmv_q8_0 / qmv_q4_k / qmv_q6_k by format."""
-    fn = {Q8_0: qmv_q8_0, Q4_K: qmv_q4_k, Q6_K: qmv_q6_k}[_type(t)]
-    fn(blocks, M, K, x, y, stream)
+    """Single-token matvec in format t (any of TYPES)."""
+    _call("qmv_" + {v: k for k, v in TYPES.items()}[_type(t)], _ptr(blocks), M, K, _ptr(x), _ptr(y),
+          _stream(stream))
+
+
+def qmv_q4_0(blocks, M, K, x, y, stream=None):
+    _call("qmv_q4_0", _ptr(blocks), M, K, _ptr(x), _ptr(y), _stream(stream))
+
+
+def qmv_q4_1(blocks, M, K, x, y, stream=None):
+    _call("qmv_q4_1", _ptr(blocks), M, K, _ptr(x), _ptr(y), _stream(stream))
+
+
+def qmv_q5_0(blocks, M, K, x, y, stream=None):
+    _call("qmv_q5_0", _ptr(blocks), M, K, _ptr(x), _ptr(y), _stream(stream))
+
+
+def qmv_q5_1(blocks, M, K, x, y, stream=None):
+    _call("qmv_q5_1", _ptr(blocks), M, K, _ptr(x), _ptr(y), _stream(stream))
+
+
+def qmv_q8_1(blocks, M, K, x, y, stream=None):
+    _call("qmv_q8_1", _ptr(blocks), M, K, _ptr(x), _ptr(y), _stream(stream))
+
+
+def qmv_q5_k(blocks, M, K, x, y, stream=None):
+    _call("qmv_q5_k", _ptr(blocks), M, K, _ptr(x), _ptr(y), _stream(stream))
 
 
 def qmv_fused_rows(t, blocks, K, x, seg_rows, y_seg, stream=None):

@@ -26,7 +26,9 @@ std::map<std::pair<const void *, size_t>, int> g_occ;  // (kernel, lds) -> block
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-bool valid_type(int t) { return t == kQ80 || t == kQ4K || t == kQ6K; }
+bool valid_type(int t) { return block_weights_of(t) != 0; }
+// formats with a verify-product kernel and a device quantiser
+bool core_type(int t) { return t == kQ80 || t == kQ4K || t == kQ6K; }
 
 qmv_status check_matrix(int t, const void *blocks, int64_t M, int64_t K) {
     if (!valid_type(t)) return QMV_EINVAL;
@@ -153,6 +155,30 @@ qmv_status qmv_q6_k(const void *blocks, int64_t M, int64_t K, const float *x, fl
                     hipStream_t stream) {
     return single(kQ6K, blocks, M, K, x, y, stream);
 }
+qmv_status qmv_q5_k(const void *blocks, int64_t M, int64_t K, const float *x, float *y,
+                    hipStream_t stream) {
+    return single(kQ5K, blocks, M, K, x, y, stream);
+}
+qmv_status qmv_q4_0(const void *blocks, int64_t M, int64_t K, const float *x, float *y,
+                    hipStream_t stream) {
+    return single(kQ40, blocks, M, K, x, y, stream);
+}
+qmv_status qmv_q4_1(const void *blocks, int64_t M, int64_t K, const float *x, float *y,
+                    hipStream_t stream) {
+    return single(kQ41, blocks, M, K, x, y, stream);
+}
+qmv_status qmv_q5_0(const void *blocks, int64_t M, int64_t K, const float *x, float *y,
+                    hipStream_t stream) {
+    return single(kQ50, blocks, M, K, x, y, stream);
+}
+qmv_status qmv_q5_1(const void *blocks, int64_t M, int64_t K, const float *x, float *y,
+                    hipStream_t stream) {
+    return single(kQ51, blocks, M, K, x, y, stream);
+}
+qmv_status qmv_q8_1(const void *blocks, int64_t M, int64_t K, const float *x, float *y,
+                    hipStream_t stream) {
+    return single(kQ81, blocks, M, K, x, y, stream);
+}
 
 qmv_status qmv_fused_rows(qmv_type t, const void *blocks, int64_t K, const float *x,
                           int32_t nseg, const int64_t *seg_rows, float *const *y_seg,
@@ -216,7 +242,7 @@ qmv_status moe_qmv_topk(const float *x, int64_t H, const float *router, const fl
     if (E < 1 || E > 64 || k < 1 || k > E) return QMV_ESHAPE;
     if (H < 1 || I < 1 || (int64_t)k * I > QMV_MAX_K || (int64_t)k * 2 * I > 0x7FFFFFFFll)
         return QMV_ESHAPE;
-    if (dn_t == QMV_Q8_0 && I % 128 != 0) return QMV_ESHAPE;
+    if (block_weights_of(dn_t) == 32 && I % 128 != 0) return QMV_ESHAPE;
     qmv_status st = check_matrix(gu_t, gate_up, 2 * I, H);
     if (st != QMV_OK) return st;
     st = check_matrix(dn_t, down, H, I);
@@ -235,6 +261,7 @@ qmv_status moe_qmv_topk(const float *x, int64_t H, const float *router, const fl
 qmv_status qmv_gemm_n(qmv_type t, const void *blocks, int64_t M, int64_t K, int32_t n,
                       const float *X, float *Y, void *workspace, size_t ws_bytes,
                       hipStream_t stream) {
+    if (!core_type(t)) return QMV_EINVAL;
     qmv_status st = check_matrix(t, blocks, M, K);
     if (st != QMV_OK) return st;
     if (n < 1 || n > QMV_MAX_N) return QMV_ESHAPE;
@@ -257,7 +284,7 @@ qmv_status qmv_dequant(qmv_type t, const void *blocks, int64_t M, int64_t K, flo
 
 qmv_status qmv_quantize(qmv_type t, const float *w, int64_t M, int64_t K, void *blocks_out,
                         hipStream_t stream) {
-    if (!valid_type(t)) return QMV_EINVAL;
+    if (!core_type(t)) return QMV_EINVAL;
     if (!w || !blocks_out) return QMV_EINVAL;
     if (M < 1 || K < 1 || K % block_weights_of(t) != 0) return QMV_ESHAPE;
     if (!aligned(w, 4)) return QMV_EALIGN;

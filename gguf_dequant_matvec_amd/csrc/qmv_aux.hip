@@ -74,6 +74,72 @@ __global__ void dequant_q6_k(const uint8_t *W, int64_t ngroups, float *out) {
     store16(out + t * 16, v);
 }
 
+// Q5_K: the Q4_K decoding with a fifth code bit, bit 2c + h of high byte l.
+__global__ void dequant_q5_k(const uint8_t *W, int64_t ngroups, float *out) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= ngroups) return;
+    const uint8_t *blk = W + (t >> 4) * 176;
+    const int i0 = 16 * (int)(t & 15);
+    const int j = i0 / 32, c = i0 / 64, hi = (i0 % 64) / 32, l0 = i0 % 32;
+    const uint8_t *S = blk + 4;
+    int sc, m;
+    if (j < 4) {
+        sc = S[j] & 63;
+        m = S[j + 4] & 63;
+    } else {
+        sc = (S[j + 4] & 15) | ((S[j - 4] >> 6) << 4);
+        m = (S[j + 4] >> 4) | ((S[j] >> 6) << 4);
+    }
+    const float s = half_bits_to_float(load2(blk)) * (float)sc;
+    const float o = half_bits_to_float(load2(blk + 2)) * (float)m;
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        const int l = l0 + i;
+        const int q = ((blk[48 + 32 * c + l] >> (4 * hi)) & 15) | (((blk[16 + l] >> (2 * c + hi)) & 1) << 4);
+        v[i] = s * (float)q - o;
+    }
+    store16(out + t * 16, v);
+}
+
+// 32-weight nibble formats: thread t writes half h = t & 1 of block t >> 1,
+// i.e. the low (h = 0) or high (h = 1) nibbles of the 16 code bytes.
+// w = d * (q - kOff), or d * q + m (kMin; the product is exact, so the one
+// rounding is the same with or without contraction).
+template <int kBytes, bool kMin, int kHigh, int kCodes, int kOff>
+__global__ void dequant_nib32(const uint8_t *W, int64_t ngroups, float *out) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= ngroups) return;
+    const uint8_t *blk = W + (t >> 1) * kBytes;
+    const int h = (int)(t & 1);
+    const float d = half_bits_to_float(load2(blk));
+    const float m = kMin ? half_bits_to_float(load2(blk + 2)) : 0.f;
+    uint32_t H = 0;
+    if (kHigh)
+        H = (uint32_t)blk[kHigh] | ((uint32_t)blk[kHigh + 1] << 8) | ((uint32_t)blk[kHigh + 2] << 16) |
+            ((uint32_t)blk[kHigh + 3] << 24);
+    float v[16];
+#pragma unroll
+    for (int l = 0; l < 16; l++) {
+        int q = (blk[kCodes + l] >> (4 * h)) & 15;
+        if (kHigh) q |= (int)((H >> (16 * h + l)) & 1u) << 4;
+        v[l] = kMin ? d * (float)q + m : d * (float)(q - kOff);
+    }
+    store16(out + t * 16, v);
+}
+
+__global__ void dequant_q8_1(const uint8_t *W, int64_t ngroups, float *out) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= ngroups) return;
+    const uint8_t *blk = W + (t >> 1) * 36;
+    const int half = (int)(t & 1);
+    const float d = half_bits_to_float(load2(blk));
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) v[i] = d * (float)(int8_t)blk[4 + 16 * half + i];
+    store16(out + t * 16, v);
+}
+
 // ---------------------------------------------------------------------------
 // Quantise: one thread per block, f32 arithmetic without contraction so the
 // bytes are reproducible: Q8_0 d = max|w|/127, q = round(w * (1/d));
@@ -262,6 +328,20 @@ hipError_t launch_dequant(int type, const uint8_t *W, int64_t M, int64_t K, floa
     case kQ80: hipLaunchKernelGGL(dequant_q8_0, dim3(grid), dim3(256), 0, s, W, ngroups, out); break;
     case kQ4K: hipLaunchKernelGGL(dequant_q4_k, dim3(grid), dim3(256), 0, s, W, ngroups, out); break;
     case kQ6K: hipLaunchKernelGGL(dequant_q6_k, dim3(grid), dim3(256), 0, s, W, ngroups, out); break;
+    case kQ5K: hipLaunchKernelGGL(dequant_q5_k, dim3(grid), dim3(256), 0, s, W, ngroups, out); break;
+    case kQ40:
+        hipLaunchKernelGGL((dequant_nib32<18, false, 0, 2, 8>), dim3(grid), dim3(256), 0, s, W, ngroups, out);
+        break;
+    case kQ41:
+        hipLaunchKernelGGL((dequant_nib32<20, true, 0, 4, 0>), dim3(grid), dim3(256), 0, s, W, ngroups, out);
+        break;
+    case kQ50:
+        hipLaunchKernelGGL((dequant_nib32<22, false, 2, 6, 16>), dim3(grid), dim3(256), 0, s, W, ngroups, out);
+        break;
+    case kQ51:
+        hipLaunchKernelGGL((dequant_nib32<24, true, 4, 8, 0>), dim3(grid), dim3(256), 0, s, W, ngroups, out);
+        break;
+    case kQ81: hipLaunchKernelGGL(dequant_q8_1, dim3(grid), dim3(256), 0, s, W, ngroups, out); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -309,4 +309,195 @@ struct Q80x1 {
     }
 };
 
+// ---------------------------------------------------------------------------
+// Q5_K (BebeLM page, section "局限与未来": Q5_K_M): the Q4_K super-block plus
+// 32 bytes of fifth bits.  Unit u = chunk c = u & 3 of block u / 4, as in
+// Q4_K: weights 64c + l (low nibble of byte 32c + l, fifth bit 2c of high
+// byte l) and 64c + 32 + l (high nibble, fifth bit 2c + 1).  The 5-bit codes
+// are assembled bytewise, then spread two per dword into f16 subnormals.
+// ---------------------------------------------------------------------------
+struct Q5K {
+    static constexpr int kBlockWeights = 256;
+    static constexpr int kBlockBytes = 176;
+    static constexpr int kUnitWeights = 64;
+    static constexpr int kSumGroup = 32;
+    static constexpr int kPadEvery = 64;
+    struct Regs {
+        uint4 hdr, q0, q1, h0, h1;
+    };
+    __device__ static __forceinline__ uint32_t unit_offset(int u) {
+        return (uint32_t)(u >> 2) * kBlockBytes;
+    }
+    __device__ static __forceinline__ Regs load(const BufSrc &src, uint32_t off, int u) {
+        const uint32_t c = u & 3;
+        Regs r;
+        r.hdr = src.ld16(off);
+        r.h0 = src.ld16(off + 16);
+        r.h1 = src.ld16(off + 32);
+        r.q0 = src.ld16(off + 48 + 32 * c);
+        r.q1 = src.ld16(off + 64 + 32 * c);
+        return r;
+    }
+    __device__ static __forceinline__ void load_x(const float *xs, int u, float *xv) {
+        Q4K::load_x(xs, u, xv);
+    }
+    __device__ static __forceinline__ void dot(const Regs &r, const float *xv, const float *sums,
+                                               int u, float &acc) {
+        const uint32_t qw[8] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w};
+        const uint32_t hw[8] = {r.h0.x, r.h0.y, r.h0.z, r.h0.w, r.h1.x, r.h1.y, r.h1.z, r.h1.w};
+        const int c = u & 3;
+        float lo0 = 0.f, lo1 = 0.f, hi0 = 0.f, hi1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const uint32_t t = hw[i] >> (2 * c);
+            const uint32_t a = (qw[i] & 0x0F0F0F0Fu) | ((t & 0x01010101u) << 4);
+            const uint32_t b = ((qw[i] >> 4) & 0x0F0F0F0Fu) | ((t & 0x02020202u) << 3);
+            const f16x2_t a01 = as_f16x2(bytes01_to_halves(a)), a23 = as_f16x2(bytes23_to_halves(a));
+            const f16x2_t b01 = as_f16x2(bytes01_to_halves(b)), b23 = as_f16x2(bytes23_to_halves(b));
+            lo0 = fmaf((float)a01.x, xv[4 * i + 0], lo0);
+            lo1 = fmaf((float)a01.y, xv[4 * i + 1], lo1);
+            lo0 = fmaf((float)a23.x, xv[4 * i + 2], lo0);
+            lo1 = fmaf((float)a23.y, xv[4 * i + 3], lo1);
+            hi0 = fmaf((float)b01.x, xv[32 + 4 * i + 0], hi0);
+            hi1 = fmaf((float)b01.y, xv[32 + 4 * i + 1], hi1);
+            hi0 = fmaf((float)b23.x, xv[32 + 4 * i + 2], hi0);
+            hi1 = fmaf((float)b23.y, xv[32 + 4 * i + 3], hi1);
+        }
+        const float alo = lo0 + lo1, ahi = hi0 + hi1;  // at the scale 2^-24
+        // 6-bit scales and mins of sub-blocks 2c and 2c + 1 (the Q4_K packing)
+        const int sh = (c & 1) * 16;
+        const uint32_t s0 = r.hdr.y >> sh, s1 = r.hdr.z >> sh, s2 = r.hdr.w >> sh;
+        const uint32_t sc_lo = s0 & 0x3F3Fu, m_lo = s1 & 0x3F3Fu;
+        const uint32_t sc_hi = (s2 & 0x0F0Fu) | ((s0 >> 2) & 0x3030u);
+        const uint32_t m_hi = ((s2 >> 4) & 0x0F0Fu) | ((s1 >> 2) & 0x3030u);
+        const uint32_t sc = c < 2 ? sc_lo : sc_hi;
+        const uint32_t m = c < 2 ? m_lo : m_hi;
+        const float d = half_bits_to_float(r.hdr.x) * kTwo24;
+        const float dmin = half_bits_to_float(r.hdr.x >> 16);
+        const float t = fmaf(ubyte<1>(sc), ahi, ubyte<0>(sc) * alo);
+        const float mm = fmaf(ubyte<1>(m), sums[2 * u + 1], ubyte<0>(m) * sums[2 * u]);
+        acc = fmaf(d, t, acc);
+        acc = fmaf(-dmin, mm, acc);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// 32-weight nibble formats, one block per unit (FlareLLM page, section
+// "量化技术的全面支持": the standard 4- and 5-bit quantisations).  Code byte l
+// (0..15) holds weight l in its low nibble and weight l + 16 in its high
+// nibble; the 5-bit formats add bit i of a little-endian 32-bit word as the
+// fifth bit of weight i.  w = d * (q - kOff) (Q4_0: 8, Q5_0: 16) or
+// w = d * q + m (Q4_1, Q5_1, kMin); both are applied once per block through
+// the block's activation sum.  kHigh: byte offset of the fifth-bit word (0:
+// none); kCodes: byte offset of the 16 code bytes.
+// ---------------------------------------------------------------------------
+template <int kBytes, bool kMin, int kHigh, int kCodes, int kOff>
+struct Nib32 {
+    static constexpr int kBlockWeights = 32;
+    static constexpr int kBlockBytes = kBytes;
+    static constexpr int kUnitWeights = 32;
+    static constexpr int kSumGroup = 32;
+    static constexpr int kPadEvery = 32;
+    struct Regs {
+        uint4 q;
+        uint32_t hdr;  // d (and m in the high half)
+        uint32_t hb;   // fifth bits
+    };
+    __device__ static __forceinline__ uint32_t unit_offset(int u) { return (uint32_t)u * kBytes; }
+    __device__ static __forceinline__ Regs load(const BufSrc &src, uint32_t off, int) {
+        Regs r;
+        r.hdr = kMin ? src.ld4(off) : src.ld2(off);
+        r.hb = kHigh ? src.ld4(off + kHigh) : 0u;
+        r.q = src.ld16(off + kCodes);
+        return r;
+    }
+    // 36 floats per unit in LDS: 32 activations and 4 pad
+    __device__ static __forceinline__ void load_x(const float *xs, int u, float *xv) {
+        const float4 *p = reinterpret_cast<const float4 *>(xs + 36 * u);
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            float4 v = p[i];
+            xv[4 * i] = v.x;
+            xv[4 * i + 1] = v.y;
+            xv[4 * i + 2] = v.z;
+            xv[4 * i + 3] = v.w;
+        }
+    }
+    // Bits 0..3 of t moved to bit 4 of bytes 0..3 (the multiply places bit
+    // k at bit 8k without carries).
+    __device__ static __forceinline__ uint32_t fifth_bits(uint32_t t) {
+        return (((t & 15u) * 0x00204081u) & 0x01010101u) << 4;
+    }
+    __device__ static __forceinline__ void dot(const Regs &r, const float *xv, const float *sums,
+                                               int u, float &acc) {
+        const uint32_t qw[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
+        float lo0 = 0.f, lo1 = 0.f, hi0 = 0.f, hi1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            uint32_t a = qw[i] & 0x0F0F0F0Fu;          // weights 4i .. 4i+3
+            uint32_t b = (qw[i] >> 4) & 0x0F0F0F0Fu;   // weights 16+4i .. 16+4i+3
+            if (kHigh) {
+                a |= fifth_bits(r.hb >> (4 * i));
+                b |= fifth_bits(r.hb >> (16 + 4 * i));
+            }
+            const f16x2_t a01 = as_f16x2(bytes01_to_halves(a)), a23 = as_f16x2(bytes23_to_halves(a));
+            const f16x2_t b01 = as_f16x2(bytes01_to_halves(b)), b23 = as_f16x2(bytes23_to_halves(b));
+            lo0 = fmaf((float)a01.x, xv[4 * i + 0], lo0);
+            lo1 = fmaf((float)a01.y, xv[4 * i + 1], lo1);
+            lo0 = fmaf((float)a23.x, xv[4 * i + 2], lo0);
+            lo1 = fmaf((float)a23.y, xv[4 * i + 3], lo1);
+            hi0 = fmaf((float)b01.x, xv[16 + 4 * i + 0], hi0);
+            hi1 = fmaf((float)b01.y, xv[16 + 4 * i + 1], hi1);
+            hi0 = fmaf((float)b23.x, xv[16 + 4 * i + 2], hi0);
+            hi1 = fmaf((float)b23.y, xv[16 + 4 * i + 3], hi1);
+        }
+        const float qx = ((lo0 + lo1) + (hi0 + hi1)) * kTwo24;  // sum q x, exact scaling
+        const float d = half_bits_to_float(r.hdr);
+        if constexpr (kMin) {
+            acc = fmaf(d, qx, fmaf(half_bits_to_float(r.hdr >> 16), sums[u], acc));
+        } else {
+            acc = fmaf(d, fmaf(-(float)kOff, sums[u], qx), acc);
+        }
+    }
+};
+using Q40 = Nib32<18, false, 0, 2, 8>;
+using Q41 = Nib32<20, true, 0, 4, 0>;
+using Q50 = Nib32<22, false, 2, 6, 16>;
+using Q51 = Nib32<24, true, 4, 8, 0>;
+
+// ---------------------------------------------------------------------------
+// Q8_1 as weights: Q8_0 plus an fp16 field s (the scaled code sum, meant for
+// activations, not used here); one 36-byte block per unit.
+// ---------------------------------------------------------------------------
+struct Q81x1 {
+    static constexpr int kBlockWeights = 32;
+    static constexpr int kBlockBytes = 36;
+    static constexpr int kUnitWeights = 32;
+    static constexpr int kSumGroup = 0;
+    static constexpr int kPadEvery = 32;
+    struct Regs {
+        uint4 a, b;
+        uint32_t c;
+    };
+    __device__ static __forceinline__ uint32_t unit_offset(int u) { return (uint32_t)u * 36; }
+    __device__ static __forceinline__ Regs load(const BufSrc &src, uint32_t off, int) {
+        Regs r;
+        r.c = src.ld4(off);
+        r.a = src.ld16(off + 4);
+        r.b = src.ld16(off + 20);
+        return r;
+    }
+    __device__ static __forceinline__ void load_x(const float *xs, int u, float *xv) {
+        Q80x1::load_x(xs, u, xv);
+    }
+    __device__ static __forceinline__ void dot(const Regs &r, const float *xv, const float *sums,
+                                               int u, float &acc) {
+        Q80x1::Regs q;
+        q.a = r.a;
+        q.b = r.b;
+        q.c = r.c;  // d in the low half; the sum field is ignored
+        Q80x1::dot(q, xv, sums, u, acc);
+    }
+};
+
 }  // namespace qmv

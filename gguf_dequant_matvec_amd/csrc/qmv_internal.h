@@ -10,15 +10,30 @@ namespace qmv {
 
 struct SegTable;
 
-enum { kQ80 = 8, kQ4K = 12, kQ6K = 14 };
+enum { kQ40 = 2, kQ41 = 3, kQ50 = 6, kQ51 = 7, kQ80 = 8, kQ81 = 9, kQ4K = 12, kQ5K = 13, kQ6K = 14 };
 
 constexpr int kMaxGrid = 2048;  // largest persistent grid (argmax partial slots)
 
 inline int block_weights_of(int type) {
-    return type == kQ80 ? 32 : (type == kQ4K || type == kQ6K) ? 256 : 0;
+    switch (type) {
+    case kQ40: case kQ41: case kQ50: case kQ51: case kQ80: case kQ81: return 32;
+    case kQ4K: case kQ5K: case kQ6K: return 256;
+    default: return 0;
+    }
 }
 inline int block_bytes_of(int type) {
-    return type == kQ80 ? 34 : type == kQ4K ? 144 : type == kQ6K ? 210 : 0;
+    switch (type) {
+    case kQ40: return 18;
+    case kQ41: return 20;
+    case kQ50: return 22;
+    case kQ51: return 24;
+    case kQ80: return 34;
+    case kQ81: return 36;
+    case kQ4K: return 144;
+    case kQ5K: return 176;
+    case kQ6K: return 210;
+    default: return 0;
+    }
 }
 inline size_t row_bytes_of(int type, int64_t K) {
     const int bw = block_weights_of(type);

@@ -55,8 +55,33 @@
 extern "C" {
 #endif
 
-/* Block formats, numbered with their GGUF tensor type ids. */
-typedef enum { QMV_Q8_0 = 8, QMV_Q4_K = 12, QMV_Q6_K = 14 } qmv_type;
+/* Block formats, numbered with their GGUF tensor type ids.  Q8_0, Q4_K and
+ * Q6_K are the formats of the pages' models; Q4_0, Q4_1, Q5_0, Q5_1, Q8_1
+ * (FlareLLM page, section "量化技术的全面支持": the standard 4- to 8-bit
+ * quantisations) and Q5_K (BebeLM page, section "局限与未来": Q5_K_M) are
+ * served by the single-token, fused-row, gated gate/up, argmax, MoE and
+ * dequantisation calls; qmv_gemm_n and qmv_quantize take the first three
+ * only.  Blocks (standard GGUF layouts, little-endian):
+ *   Q4_0 18 B: fp16 d, 16 code bytes;                w = d * (q - 8)
+ *   Q4_1 20 B: fp16 d, fp16 m, 16 code bytes;        w = d * q + m
+ *   Q5_0 22 B: fp16 d, u32 fifth bits, 16 code bytes; w = d * (q - 16)
+ *   Q5_1 24 B: fp16 d, fp16 m, u32 fifth bits, 16 code bytes; w = d * q + m
+ *   Q8_1 36 B: fp16 d, fp16 s (unused for weights), 32 int8; w = d * q
+ *   Q5_K 176 B: Q4_K's d, dmin and 12 scale bytes, 32 bytes of fifth bits,
+ *     128 nibble bytes; w = d * sc_j * q - dmin * m_j, q in 0..31
+ * (32-weight formats: code byte l holds weight l in its low nibble and l + 16
+ * in its high nibble; bit i of the u32 is the fifth bit of weight i.) */
+typedef enum {
+    QMV_Q4_0 = 2,
+    QMV_Q4_1 = 3,
+    QMV_Q5_0 = 6,
+    QMV_Q5_1 = 7,
+    QMV_Q8_0 = 8,
+    QMV_Q8_1 = 9,
+    QMV_Q4_K = 12,
+    QMV_Q5_K = 13,
+    QMV_Q6_K = 14
+} qmv_type;
 
 typedef enum {
     QMV_OK = 0,
@@ -86,6 +111,20 @@ qmv_status qmv_q8_0(const void *blocks, int64_t M, int64_t K, const float *x, fl
 qmv_status qmv_q4_k(const void *blocks, int64_t M, int64_t K, const float *x, float *y,
                     hipStream_t stream);
 qmv_status qmv_q6_k(const void *blocks, int64_t M, int64_t K, const float *x, float *y,
+                    hipStream_t stream);
+/* The same for the further formats above (FlareLLM page, section
+ * "量化技术的全面支持"; BebeLM page, section "局限与未来"). */
+qmv_status qmv_q4_0(const void *blocks, int64_t M, int64_t K, const float *x, float *y,
+                    hipStream_t stream);
+qmv_status qmv_q4_1(const void *blocks, int64_t M, int64_t K, const float *x, float *y,
+                    hipStream_t stream);
+qmv_status qmv_q5_0(const void *blocks, int64_t M, int64_t K, const float *x, float *y,
+                    hipStream_t stream);
+qmv_status qmv_q5_1(const void *blocks, int64_t M, int64_t K, const float *x, float *y,
+                    hipStream_t stream);
+qmv_status qmv_q8_1(const void *blocks, int64_t M, int64_t K, const float *x, float *y,
+                    hipStream_t stream);
+qmv_status qmv_q5_k(const void *blocks, int64_t M, int64_t K, const float *x, float *y,
                     hipStream_t stream);
 
 /* ---- fused row stack: one launch over nseg row segments sharing x --------
@@ -141,7 +180,7 @@ qmv_status qmv_argmax(qmv_type t, const void *blocks, int64_t M, int64_t K, cons
  *   at byte 0; from byte 256 f32 gu[k][2I] (per slot: the I gate results,
  *   then the I up results); then f32 h[k][I] = silu(g) * u.
  * Constraints: 1 <= k <= E <= 64; H and I multiples of their formats' B;
- *   k * I <= QMV_MAX_K; with a Q8_0 down projection, I a multiple of 128.  Three launches; the selection never leaves the GPU. */
+ *   k * I <= QMV_MAX_K; with a 32-weight down format, I a multiple of 128.  Three launches; the selection never leaves the GPU. */
 qmv_status moe_qmv_topk(const float *x, int64_t H, const float *router, const float *bias,
                         int32_t E, int32_t k, qmv_type gu_t, const void *gate_up,
                         qmv_type dn_t, const void *down, int64_t I, float *y,

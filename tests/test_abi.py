@@ -37,6 +37,9 @@ def test_row_bytes_and_workspace():
     assert q.qmv_row_bytes("q4_k", 4096) == 2304
     assert q.qmv_row_bytes("q6_k", 1536) == 1260
     assert q.qmv_row_bytes("q4_k", 100) == 0
+    assert [q.qmv_row_bytes(t, 64) for t in ("q4_0", "q4_1", "q5_0", "q5_1", "q8_1")] == \
+        [36, 40, 44, 48, 72]
+    assert q.qmv_row_bytes("q5_k", 512) == 352
     assert q.qmv_workspace_bytes(q.OP_ARGMAX, 128000, 4096) >= 8 * 2048
     assert q.qmv_workspace_bytes(q.OP_MOE, 2048, 1536, 32, 4) == 256 + 3 * 4 * 1536 * 4
     assert q.load().qmv_status_str(3) == b"pointer misaligned"
@@ -57,6 +60,9 @@ def test_shape_errors():
     assert status_of(q.qmv_q6_k, A16, 4, 0, A16, A16) == "QMV_ESHAPE"
     assert status_of(q.qmv_q8_0, A16, 4, 48, A16, A16) == "QMV_ESHAPE"
     assert status_of(q.qmv_q8_0, A16, 4, q.MAX_K + 32, A16, A16) == "QMV_ESHAPE"
+    assert status_of(q.qmv_q5_k, A16, 4, 128, A16, A16) == "QMV_ESHAPE"
+    assert status_of(q.qmv_q4_0, A16, 4, 48, A16, A16) == "QMV_ESHAPE"
+    assert status_of(q.qmv_q5_1, A16, 0, 64, A16, A16) == "QMV_ESHAPE"
     assert status_of(q.qmv_gemm_n, "q4_k", A16, 4, 256, 17, A16, A16, A16, 1 << 20) == "QMV_ESHAPE"
     assert status_of(q.qmv_gemm_n, "q4_k", A16, 4, 256, 0, A16, A16, A16, 1 << 20) == "QMV_ESHAPE"
     assert status_of(q.qmv_fused_rows, "q4_k", A16, 256, A16, [4, 0], [A16, A16]) == "QMV_ESHAPE"
@@ -69,11 +75,15 @@ def test_shape_errors():
 def test_pointer_and_type_errors():
     assert status_of(q.qmv_q4_k, 0, 4, 256, A16, A16) == "QMV_EINVAL"
     assert status_of(q.qmv_q4_k, A16, 4, 256, 0, A16) == "QMV_EINVAL"
-    assert status_of(q.qmv_dequant, 13, A16, 4, 256, A16) == "QMV_EINVAL"
+    assert status_of(q.qmv_dequant, 11, A16, 4, 256, A16) == "QMV_EINVAL"   # Q3_K: not served
+    assert status_of(q.qmv_dequant, 4, A16, 4, 256, A16) == "QMV_EINVAL"
+    # the verify product and the device quantiser take Q8_0, Q4_K and Q6_K only
+    assert status_of(q.qmv_gemm_n, "q5_k", A16, 4, 256, 8, A16, A16, A16, 1 << 20) == "QMV_EINVAL"
+    assert status_of(q.qmv_quantize, "q4_0", A16, 4, 256, A16) == "QMV_EINVAL"
     assert status_of(q.qmv_fused_rows, "q4_k", A16, 256, A16, [1] * 9, [A16] * 9) == "QMV_EINVAL"
     assert status_of(q.qmv_fused_rows, "q4_k", A16, 256, A16, [], []) == "QMV_EINVAL"
     assert status_of(q.qmv_gate_up_silu, "q4_k", A16, 8, 256, A16, 0) == "QMV_EINVAL"
-    assert status_of(q.qmv_gate_up_silu, 13, A16, 8, 256, A16, A16) == "QMV_EINVAL"
+    assert status_of(q.qmv_gate_up_silu, 11, A16, 8, 256, A16, A16) == "QMV_EINVAL"
 
 
 def test_alignment_errors():

@@ -30,6 +30,13 @@ SHAPES = [
     ("q6_k", 97, 14336),
     ("q8_0", 1, 32), ("q8_0", 1536, 576), ("q8_0", 37, 224), ("q8_0", 100, 4096),
     ("q8_0", 19, 96),
+    # further formats: Q5_K (256-weight super-blocks) and the 32-weight ones
+    ("q5_k", 1, 256), ("q5_k", 77, 2048), ("q5_k", 1000, 4096), ("q5_k", 97, 14336),
+    ("q4_0", 1, 32), ("q4_0", 300, 4096), ("q4_0", 37, 224),
+    ("q4_1", 129, 2048), ("q4_1", 19, 96),
+    ("q5_0", 300, 4096), ("q5_0", 37, 224),
+    ("q5_1", 129, 2048), ("q5_1", 1, 32),
+    ("q8_1", 1536, 576), ("q8_1", 33, 224),
 ]
 
 
@@ -68,7 +75,9 @@ def test_qmv_parity(t, M, K):
 
 
 @pytest.mark.parametrize("t,M,K", [("q4_k", 40, 4096), ("q6_k", 40, 1536), ("q8_0", 40, 576),
-                                   ("q8_0", 9, 224), ("q4_k", 33, 14336)])
+                                   ("q8_0", 9, 224), ("q4_k", 33, 14336), ("q5_k", 40, 4096),
+                                   ("q4_0", 40, 576), ("q4_1", 40, 576), ("q5_0", 40, 576),
+                                   ("q5_1", 40, 576), ("q8_1", 40, 576)])
 def test_qmv_one_hot_is_exact(t, M, K):
     b, _ = _case(t, M, K, 300)
     W = oracle.dequant(t, b, M, K)
@@ -114,6 +123,9 @@ def test_x_extremes():
     ("q8_0", (300, 11, 5), 576),
     ("q4_k", tuple([3] * 8), 4096),            # the most segments
     ("q4_k", (100, 37, 3), 14336),             # long rows, several unit steps
+    ("q5_k", (512, 128, 128), 2048),
+    ("q4_0", (64, 16, 16), 4096),
+    ("q5_1", (33, 7), 224),
 ])
 def test_fused_rows(t, segs, K):
     M = sum(segs)
@@ -144,7 +156,8 @@ def _argmax_gpu(t, bd, M, K, xd):
 
 @pytest.mark.parametrize("t,M,K", [("q6_k", 5000, 4096), ("q4_k", 777, 2048), ("q8_0", 1536, 576),
                                    ("q6_k", 1, 256), ("q6_k", 3001, 1536), ("q4_k", 300, 14336),
-                                   ("q8_0", 70, 8192)])
+                                   ("q8_0", 70, 8192), ("q5_k", 3000, 4096), ("q4_0", 2000, 2048),
+                                   ("q8_1", 900, 576)])
 def test_argmax(t, M, K):
     b, x = _case(t, M, K, 500 + M)
     y_ref, a_ref = oracle.qmv(t, b, M, K, x)

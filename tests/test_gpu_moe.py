@@ -166,6 +166,9 @@ def test_moe_k1_and_tie_to_lower_expert():
     (5, 256, 128, 2, "q8_0", "q8_0"),     # Q8_0 experts, odd expert count, 1-block units
     (6, 512, 256, 3, "q8_0", "q8_0"),     # Q8_0 experts, 2-block units
     (64, 256, 256, 6, "q4_k", "q8_0"),    # the most experts
+    (8, 512, 256, 4, "q5_k", "q4_0"),     # further formats: Q5_K gate/up, Q4_0 down
+    (6, 256, 128, 2, "q5_0", "q5_1"),
+    (4, 256, 256, 2, "q4_1", "q8_1"),
 ])
 def test_moe_small_shapes(E, H, I, k, gu_t, dn_t):
     ex = experts((50 + E, E, H, I, gu_t, dn_t))

@@ -67,6 +67,9 @@ SHAPES = [
     ("q6_k", 64, 4096),
     ("q8_0", 77, 576),
     ("q8_0", 33, 224),     # one 32-weight block per unit
+    ("q5_k", 200, 2048),
+    ("q4_0", 96, 4096),
+    ("q5_1", 45, 224),
 ]
 
 
