@@ -76,11 +76,13 @@ def _load():
     lib.oracle_qmv.argtypes = [ci, P, i64, i64, P, P, P]
     lib.oracle_argmax.argtypes = [ci, P, i64, i64, P, P, P, P]
     lib.oracle_gate_up_silu.argtypes = [ci, P, i64, i64, P, P, P, P, P, P]
+    lib.oracle_short_conv.argtypes = [ci, P, i64, i64, P, P, P, ci, P, P, P, P, P, P, P]
     lib.oracle_gemm_n.argtypes = [ci, P, i64, i64, i32, P, P, P]
     lib.oracle_moe.argtypes = [P, i64, P, P, i32, i32, ci, P, ci, P, i64,
                                P, P, P, P, P, P, P, P, P]
     for name in ("oracle_dequant", "oracle_quantize", "oracle_qmv_rows", "oracle_qmv",
-                 "oracle_argmax", "oracle_gate_up_silu", "oracle_gemm_n", "oracle_moe"):
+                 "oracle_argmax", "oracle_gate_up_silu", "oracle_short_conv", "oracle_gemm_n",
+                 "oracle_moe"):
         getattr(lib, name).restype = ci
     _lib = lib
     return lib
@@ -182,6 +184,36 @@ def gate_up_silu(t, blocks: np.ndarray, I: int, K: int, x: np.ndarray):
     _check(_load().oracle_gate_up_silu(t, _ptr(blocks), I, K, _ptr(x), _ptr(h), _ptr(g), _ptr(u),
                                        _ptr(ag), _ptr(au)), "gate_up_silu")
     return h, g, u, ag, au
+
+
+def short_conv(in_t, in_proj: np.ndarray, D: int, H: int, h: np.ndarray, w_conv: np.ndarray,
+               state: np.ndarray, out_t=None, out_proj: np.ndarray = None):
+    """One token of the gated short convolution (BebeLM page, section
+    "门控短卷积"): returns a dict with y, bx, state (the new one), A (in_proj
+    rows' sum |w h|, 3D) and, when out_proj is given, out and a_out; f64."""
+    in_t = _type(in_t)
+    in_proj = np.ascontiguousarray(in_proj, dtype=np.uint8)
+    h = np.ascontiguousarray(h, dtype=np.float32)
+    w_conv = np.ascontiguousarray(w_conv, dtype=np.float32).reshape(D, 3)
+    state = np.ascontiguousarray(state, dtype=np.float32).reshape(D, 2)
+    assert h.size == H and in_proj.size >= 3 * D * row_bytes(in_t, H)
+    r = {k: np.empty(n, dtype=np.float64) for k, n in
+         (("y", D), ("bx", D), ("state", 2 * D), ("A", 3 * D))}
+    out = a_out = None
+    ot = 0
+    if out_proj is not None:
+        ot = _type(out_t)
+        out_proj = np.ascontiguousarray(out_proj, dtype=np.uint8)
+        assert out_proj.size >= H * row_bytes(ot, D)
+        out, a_out = np.empty(H, dtype=np.float64), np.empty(H, dtype=np.float64)
+    _check(_load().oracle_short_conv(in_t, _ptr(in_proj), D, H, _ptr(h), _ptr(w_conv), _ptr(state),
+                                     ot, _ptr(out_proj), _ptr(r["state"]), _ptr(r["y"]),
+                                     _ptr(r["bx"]), _ptr(out), _ptr(a_out), _ptr(r["A"])),
+           "short_conv")
+    r["state"] = r["state"].reshape(D, 2)
+    if out is not None:
+        r["out"], r["a_out"] = out, a_out
+    return r
 
 
 def argmax(t, blocks: np.ndarray, M: int, K: int, x: np.ndarray):

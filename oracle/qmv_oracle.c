@@ -716,6 +716,74 @@ int oracle_gate_up_silu(int type, const uint8_t *blocks, int64_t I, int64_t K, c
 }
 
 /* ------------------------------------------------------------------------- */
+/* Gated short convolution for one token (BebeLM page, section "门控短卷积"   */
+/* and "核心算子": B, C, x = split(in_proj(h), 3); Bx = B * x; a causal        */
+/* depthwise convolution of kernel size 3 over the Bx sequence, its state the */
+/* last 2 positions; y = C * conv_out; out = out_proj(y)).                    */
+/* in_proj: 3D rows x H columns (rows 0..D-1 B, D..2D-1 C, 2D..3D-1 x);       */
+/* out_proj: H rows x D columns.  w_conv[c][k], k = 0..2: tap k multiplies    */
+/* the input k - 2 positions back, so conv_out_c = w[c][0] s[c][0] +           */
+/* w[c][1] s[c][1] + w[c][2] Bx_c with s[c][0] the older and s[c][1] the       */
+/* newer cached Bx (causal: only the current and past inputs).  The state    */
+/* after the token is (s[c][1], Bx_c).  All in f64; state_in is read as       */
+/* given.  Outputs (NULL to skip): y[D], bx[D], out[H], a_out[H] =            */
+/* sum_j |W_out[i,j] y_j|, and A[3D] = the in_proj rows' sum |w h|.            */
+/* ------------------------------------------------------------------------- */
+
+int oracle_short_conv(int in_type, const uint8_t *in_proj, int64_t D, int64_t H, const float *h,
+                      const float *w_conv, const float *state_in, int out_type,
+                      const uint8_t *out_proj, double *state_out, double *y, double *bx_out,
+                      double *out, double *a_out, double *A)
+{
+    if (D < 1 || !shape_ok(in_type, 3 * D, H) || !in_proj || !h || !w_conv || !state_in)
+        return -1;
+    if (out && (!out_proj || !shape_ok(out_type, H, D))) return -1;
+    float *wbuf = (float *)malloc((size_t)(H > D ? H : D) * sizeof(float));
+    double *yy = (double *)malloc((size_t)D * sizeof(double));
+    if (!wbuf || !yy) { free(wbuf); free(yy); return -1; }
+    size_t rb = row_bytes(in_type, H);
+    for (int64_t c = 0; c < D; c++) {
+        double b, cc, xv, ab, ac, ax;
+        dot_row(in_type, in_proj + (size_t)c * rb, H, h, wbuf, &b, &ab);
+        dot_row(in_type, in_proj + (size_t)(D + c) * rb, H, h, wbuf, &cc, &ac);
+        dot_row(in_type, in_proj + (size_t)(2 * D + c) * rb, H, h, wbuf, &xv, &ax);
+        double bx = b * xv;
+        double s0 = state_in[2 * c], s1 = state_in[2 * c + 1];
+        double conv = (double)w_conv[3 * c] * s0 + (double)w_conv[3 * c + 1] * s1 +
+                      (double)w_conv[3 * c + 2] * bx;
+        yy[c] = cc * conv;
+        if (y) y[c] = yy[c];
+        if (bx_out) bx_out[c] = bx;
+        if (state_out) {
+            state_out[2 * c] = s1;
+            state_out[2 * c + 1] = bx;
+        }
+        if (A) {
+            A[c] = ab;
+            A[D + c] = ac;
+            A[2 * D + c] = ax;
+        }
+    }
+    if (out) {
+        size_t orb = row_bytes(out_type, D);
+        for (int64_t i = 0; i < H; i++) {
+            decode_row(out_type, out_proj + (size_t)i * orb, D, wbuf);
+            double acc = 0.0, at = 0.0;
+            for (int64_t j = 0; j < D; j++) {
+                double p = (double)wbuf[j] * yy[j];
+                acc += p;
+                at += fabs(p);
+            }
+            out[i] = acc;
+            if (a_out) a_out[i] = at;
+        }
+    }
+    free(wbuf);
+    free(yy);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
 /* Greedy argmax of dequant(W) x: the lowest index among the maximal exact   */
 /* (f64) row results.  Also returns that row's value and its sum |w x|.      */
 /* ------------------------------------------------------------------------- */
