@@ -34,6 +34,7 @@ BLOCK_BYTES = {Q4_0: 18, Q4_1: 20, Q5_0: 22, Q5_1: 24, Q8_0: 34, Q8_1: 36,
 OP_ARGMAX = 1
 OP_MOE = 2
 OP_GEMM_N = 3
+OP_SHORT_CONV = 4
 MAX_K = 32768
 MAX_SEGMENTS = 8
 MAX_N = 16
@@ -45,7 +46,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmv.so")
 
 # every symbol include/qmv.h declares
 EXPORTS = ["qmv_q8_0", "qmv_q4_k", "qmv_q6_k", "qmv_q4_0", "qmv_q4_1", "qmv_q5_0", "qmv_q5_1",
-           "qmv_q8_1", "qmv_q5_k", "qmv_fused_rows", "qmv_gate_up_silu", "qmv_argmax",
+           "qmv_q8_1", "qmv_q5_k", "qmv_fused_rows", "qmv_gate_up_silu", "qmv_short_conv", "qmv_argmax",
            "moe_qmv_topk",
            "qmv_gemm_n", "qmv_dequant", "qmv_quantize", "qmv_row_bytes", "qmv_workspace_bytes",
            "qmv_last_hip_error", "qmv_status_str", "qmv_probe_stream_read",
@@ -89,6 +90,7 @@ def load():
         "qmv_q5_k": [P, i64, i64, P, P, P],
         "qmv_fused_rows": [ci, P, i64, P, i32, P, P, P],
         "qmv_gate_up_silu": [ci, P, i64, i64, P, P, P],
+        "qmv_short_conv": [ci, P, i64, i64, P, P, P, ci, P, P, P, sz, P],
         "qmv_argmax": [ci, P, i64, i64, P, P, P, P, sz, P],
         "moe_qmv_topk": [P, i64, P, P, i32, i32, ci, P, ci, P, i64, P, P, P, P, sz, P],
         "qmv_gemm_n": [ci, P, i64, i64, i32, P, P, P, sz, P],
@@ -208,6 +210,14 @@ def qmv_fused_rows(t, blocks, K, x, seg_rows, y_seg, stream=None):
 
 def qmv_gate_up_silu(t, blocks, I, K, x, h, stream=None):
     _call("qmv_gate_up_silu", _type(t), _ptr(blocks), I, K, _ptr(x), _ptr(h), _stream(stream))
+
+
+def qmv_short_conv(in_t, in_proj, D, H, h, w_conv, state, out_t, out_proj, out, workspace,
+                   ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _call("qmv_short_conv", _type(in_t), _ptr(in_proj), D, H, _ptr(h), _ptr(w_conv), _ptr(state),
+          _type(out_t), _ptr(out_proj), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream))
 
 
 def qmv_argmax(t, blocks, M, K, x, idx_out, max_out, workspace, ws_bytes=None, stream=None):

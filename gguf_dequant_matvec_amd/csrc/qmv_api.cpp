@@ -108,6 +108,10 @@ size_t qmv_workspace_bytes(qmv_op op, int64_t a, int64_t b, int32_t c, int32_t d
         // logits[E] padded to 256 B, then gu[k][2I] and h[k][I] in f32
         return 256 + 3 * (size_t)d * (size_t)b * sizeof(float);
     }
+    if (op == QMV_OP_SHORT_CONV) {
+        if (a < 1) return 0;
+        return ((size_t)a * sizeof(float) + 15) / 16 * 16;  // y[D]
+    }
     if (op == QMV_OP_GEMM_N) {
         if (a < 1 || b < 1 || c < 1 || c > QMV_MAX_N) return 0;
         return gemm_n_workspace(a, b, c);
@@ -215,6 +219,26 @@ qmv_status qmv_gate_up_silu(qmv_type t, const void *blocks, int64_t I, int64_t K
     if (!x || !h) return QMV_EINVAL;
     if (!aligned(x, 16) || !aligned(h, 4)) return QMV_EALIGN;
     return from_hip(launch_rows_silu(t, (const uint8_t *)blocks, I, K, x, h, stream));
+}
+
+qmv_status qmv_short_conv(qmv_type in_t, const void *in_proj, int64_t D, int64_t H, const float *h,
+                          const float *w_conv, float *state, qmv_type out_t, const void *out_proj,
+                          float *out, void *workspace, size_t ws_bytes, hipStream_t stream) {
+    if (D < 1 || D > 0x1FFFFFFFll) return QMV_ESHAPE;
+    qmv_status st = check_matrix(in_t, in_proj, 3 * D, H);
+    if (st != QMV_OK) return st;
+    st = check_matrix(out_t, out_proj, H, D);
+    if (st != QMV_OK) return st;
+    // the x row of a channel is 2D rows past its B row (32-bit byte offset)
+    if ((uint64_t)2 * D * row_bytes_of(in_t, H) > 0x7FFFFFFFull) return QMV_ESHAPE;
+    if (!h || !w_conv || !state || !out) return QMV_EINVAL;
+    if (!aligned(h, 16) || !aligned(w_conv, 4) || !aligned(state, 4) || !aligned(out, 4))
+        return QMV_EALIGN;
+    if (!workspace || ws_bytes < qmv_workspace_bytes(QMV_OP_SHORT_CONV, D, 0, 0, 0))
+        return QMV_EWORKSPACE;
+    if (!aligned(workspace, 16)) return QMV_EALIGN;
+    return from_hip(launch_short_conv(in_t, (const uint8_t *)in_proj, D, H, h, w_conv, state, out_t,
+                                      (const uint8_t *)out_proj, out, (float *)workspace, stream));
 }
 
 qmv_status qmv_argmax(qmv_type t, const void *blocks, int64_t M, int64_t K, const float *x,

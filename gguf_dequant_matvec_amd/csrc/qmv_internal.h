@@ -72,6 +72,9 @@ hipError_t launch_rows_store(int type, const uint8_t *W, int64_t M, int64_t K, c
                              const SegTable &seg, hipStream_t s);
 hipError_t launch_rows_silu(int type, const uint8_t *W, int64_t I, int64_t K, const float *x,
                             float *h, hipStream_t s);
+hipError_t launch_short_conv(int in_t, const uint8_t *in_proj, int64_t D, int64_t H,
+                             const float *h, const float *w_conv, float *state, int out_t,
+                             const uint8_t *out_proj, float *out, float *y, hipStream_t s);
 hipError_t launch_rows_argmax(int type, const uint8_t *W, int64_t M, int64_t K, const float *x,
                               uint64_t *partials, int32_t *idx_out, float *max_out,
                               hipStream_t s);

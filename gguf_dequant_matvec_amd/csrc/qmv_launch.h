@@ -41,7 +41,7 @@ using KernelPtr = void (*)(RowsParams);
 // and long rows (k experts), so it keeps one slot for more tiles.
 template <int MODE>
 constexpr int rows_per_lane() {
-    return MODE == kModeMoeDown ? 1 : kR;
+    return MODE == kModeMoeDown ? 1 : MODE == kModeShortConv ? 3 : kR;
 }
 
 template <class F, int MODE, int KS, bool XR>
@@ -64,9 +64,10 @@ hipError_t launch_typed(const RowsParams &p_in, hipStream_t s, int *grid_out) {
     // the MoE down launch needs unit steps that never straddle two experts
     const int G = MODE == kModeMoeDown ? pow2_divisor(p.moe.units_per_mat) : pick_group(U);
     const int iters = (U + G - 1) / G;
-    // kModeSiluUp: the two row slots hold a gate row and its up row
+    // stacked modes: the row slots hold rows M apart (gate/up; B/C/x)
     const int64_t rows_per_tile =
-        (MODE == kModeSiluUp ? 1 : (int64_t)rows_per_lane<MODE>()) * (kWave / G);
+        (MODE == kModeSiluUp || MODE == kModeShortConv ? 1 : (int64_t)rows_per_lane<MODE>()) *
+        (kWave / G);
     const int64_t ntiles = ((int64_t)p.M + rows_per_tile - 1) / rows_per_tile;
     const int waves = kBlockThreads / kWave;
     const size_t lds =
@@ -77,7 +78,8 @@ hipError_t launch_typed(const RowsParams &p_in, hipStream_t s, int *grid_out) {
     // other modes never split, so a row's result depends only on (format, K)
     // and fused rows and the argmax stay bit-identical to the plain matvec.
     // a row of one unit step keeps its activations in registers
-    constexpr bool kXrModes = MODE == kModeStore || MODE == kModeArgmax || MODE == kModeSiluUp;
+    constexpr bool kXrModes = MODE == kModeStore || MODE == kModeArgmax || MODE == kModeSiluUp ||
+                              MODE == kModeShortConv;
     KernelPtr<F, MODE> k = iters == 1 ? kernel_for_ks<F, MODE, 1, kXrModes>(G)
                                       : kernel_for_ks<F, MODE, 1, false>(G);
     hipError_t e = ensure_lds((const void *)k, lds);

@@ -27,6 +27,13 @@
 //    formed in a fixed order.  G divides the units per expert, so the expert
 //    of each unit step is uniform too.
 //
+// kModeShortConv (BebeLM page, section "门控短卷积": B, C, x = split(in_proj(h),
+// 3); Bx = B * x; causal depthwise conv of kernel size 3 with a 2-position
+// state; y = C * conv): the matrix is in_proj, 3M rows; a tile holds 64/G
+// channels' B, C and x rows in row slots 0, 1 and 2, so the owner lane of a
+// channel forms Bx, the convolution with the channel's state and taps, and y,
+// and shifts the state; the 3M row results are never written.
+//
 // kModeSiluUp (BebeLM page, section "核心算子": the gated FFN h = silu(g) * u;
 // FlareLLM page, section "推理层面的深度优化": gate and up as one stack): the
 // matrix is a stacked gate+up of 2M rows; a tile holds 64/G gate rows in row
@@ -74,9 +81,18 @@ struct RowsParams {
     SegTable seg;
     uint64_t *partials;  // argmax mode: one packed (value, index) key per workgroup
     MoeArgs moe;
+    const float *conv_w;  // kModeShortConv: taps [M][3]
+    float *conv_state;    // kModeShortConv: state [M][2], updated in place
 };
 
-enum { kModeStore = 0, kModeArgmax = 1, kModeMoeGateUp = 2, kModeMoeDown = 3, kModeSiluUp = 4 };
+enum {
+    kModeStore = 0,
+    kModeArgmax = 1,
+    kModeMoeGateUp = 2,
+    kModeMoeDown = 3,
+    kModeSiluUp = 4,
+    kModeShortConv = 5
+};
 
 // Packed argmax key: larger value first, then lower index.
 __device__ __forceinline__ uint64_t argmax_key(float v, int32_t idx) {
@@ -226,9 +242,11 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
     const int sub = lane / G, g = lane % G;
     const int U = p.K / F::kUnitWeights;
     const int iters = (U + G - 1) / G;  // unit steps per row
-    // kModeSiluUp: the two row slots are a gate row and its up row
-    constexpr bool kPair = MODE == kModeSiluUp;
-    static_assert(!kPair || R == 2, "gate and up slots");
+    // kModeSiluUp / kModeShortConv: the row slots are rows M apart in a
+    // stack (gate and up; B, C and x)
+    constexpr bool kPair = MODE == kModeSiluUp || MODE == kModeShortConv;
+    static_assert(MODE != kModeSiluUp || R == 2, "gate and up slots");
+    static_assert(MODE != kModeShortConv || R == 3, "B, C and x slots");
     constexpr int kRowsPerTile = kPair ? P : R * P;
     const int ntiles = (p.M + kRowsPerTile - 1) / kRowsPerTile;
     const int tile_stride = KS == 1 ? (int)gridDim.x * waves_per_block : (int)gridDim.x;
@@ -294,9 +312,9 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
             base = p.W + (int64_t)ex * p.moe.mat_bytes + (int64_t)r0 * rb;
             avail = live ? (uint64_t)(p.M - r0) * rb : 0;
         } else {
-            // kModeSiluUp: the view runs to the end of the up rows (2M rows)
+            // stacked modes: the view runs to the end of the stack (R M rows)
             base = p.W + (int64_t)r0 * rb;
-            avail = live ? (uint64_t)((kPair ? 2 * (int64_t)p.M : (int64_t)p.M) - r0) * rb : 0;
+            avail = live ? (uint64_t)((kPair ? R * (int64_t)p.M : (int64_t)p.M) - r0) * rb : 0;
         }
         const BufSrc src(base, avail);
         // unit g + ustep: ustep is a multiple of 4, so the position inside a
@@ -334,9 +352,22 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
             }
         }
         const int r0 = t * kRowsPerTile;
-        if constexpr (kPair) {
+        if constexpr (MODE == kModeSiluUp) {
             const int row = r0 + sub;
             if (owner && row < p.M) p.seg.y[0][row] = siluf(tot[0]) * tot[1];
+        } else if constexpr (MODE == kModeShortConv) {
+            const int ch = r0 + sub;
+            if (owner && ch < p.M) {
+                const float bx = tot[0] * tot[2];
+                const float *w = p.conv_w + 3 * (int64_t)ch;
+                float *st = p.conv_state + 2 * (int64_t)ch;
+                const float s0 = st[0], s1 = st[1];
+                // tap 2 takes the current input, tap 0 the oldest cached one
+                const float conv = fmaf(w[2], bx, fmaf(w[1], s1, w[0] * s0));
+                p.seg.y[0][ch] = tot[1] * conv;
+                st[0] = s1;
+                st[1] = bx;
+            }
         } else if (MODE != kModeArgmax) {
             // segment of the tile's first row and the start of the next one:
             // compile-time indices over the table, all in scalar registers

@@ -93,7 +93,7 @@ typedef enum {
 } qmv_status;
 
 /* Operations that need a workspace, for qmv_workspace_bytes(). */
-typedef enum { QMV_OP_ARGMAX = 1, QMV_OP_MOE = 2, QMV_OP_GEMM_N = 3 } qmv_op;
+typedef enum { QMV_OP_ARGMAX = 1, QMV_OP_MOE = 2, QMV_OP_GEMM_N = 3, QMV_OP_SHORT_CONV = 4 } qmv_op;
 
 /* Largest K (columns) any entry point accepts: x is staged whole in LDS. */
 #define QMV_MAX_K 32768
@@ -151,6 +151,27 @@ qmv_status qmv_fused_rows(qmv_type t, const void *blocks, int64_t K, const float
  * I * row bytes < 2^31 (32-bit offsets between a gate row and its up row). */
 qmv_status qmv_gate_up_silu(qmv_type t, const void *blocks, int64_t I, int64_t K, const float *x,
                             float *h, hipStream_t stream);
+
+/* ---- gated short convolution, one token -----------------------------------
+ * BebeLM page, section "门控短卷积" (B, C, x = split(in_proj(h), 3); Bx = B * x;
+ * causal depthwise convolution over the Bx sequence; y = C * conv;
+ * out = out_proj(y); only the last 2 positions are cached) and section
+ * "核心算子" (kernel size 3, a convolution state instead of a KV cache).
+ * in_proj: 3D rows x H columns in format in_t (rows 0..D-1 B, D..2D-1 C,
+ *   2D..3D-1 x).  out_proj: H rows x D columns in format out_t.
+ * h: f32[H].  w_conv: f32[D][3]; tap k multiplies the input k - 2 positions
+ *   back (tap 2 the current Bx).  state: f32[D][2], (older, newer) cached Bx
+ *   per channel, read and then replaced by (newer, current Bx) -- zero it
+ *   before the first token.  out: f32[H].
+ * workspace: device, >= qmv_workspace_bytes(QMV_OP_SHORT_CONV, D, 0, 0, 0)
+ *   bytes, 16-byte aligned; it receives y (f32[D]).
+ * Two launches: in_proj with the gates, the convolution and the state shift
+ * (the 3D row results are never written), then out_proj on y.  state, out
+ * and workspace must not overlap each other or the inputs.  Needs 2D * row
+ * bytes < 2^31 (32-bit offsets from a channel's B row to its x row). */
+qmv_status qmv_short_conv(qmv_type in_t, const void *in_proj, int64_t D, int64_t H, const float *h,
+                          const float *w_conv, float *state, qmv_type out_t, const void *out_proj,
+                          float *out, void *workspace, size_t ws_bytes, hipStream_t stream);
 
 /* ---- fused greedy argmax: the index and value of max_i (dequant(W) x)_i ---
  * FlareLLM page, section "推理层面的深度优化": at temperature 0 the next
@@ -218,7 +239,7 @@ qmv_status qmv_quantize(qmv_type t, const float *w, int64_t M, int64_t K, void *
 /* Bytes of one row of K weights in format t; 0 if K is not a multiple of B. */
 size_t qmv_row_bytes(qmv_type t, int64_t K);
 /* Workspace an operation needs.  ARGMAX: (M, K, -, -); MOE: (H, I, E, k);
- * GEMM_N: (M, K, n, -). */
+ * GEMM_N: (M, K, n, -); SHORT_CONV: (D, -, -, -). */
 size_t qmv_workspace_bytes(qmv_op op, int64_t a, int64_t b, int32_t c, int32_t d);
 /* Raw HIP error code of this thread's last QMV_EHIP (0 if none). */
 int qmv_last_hip_error(void);

@@ -108,6 +108,19 @@ def test_workspace_errors():
     w64 = q.qmv_workspace_bytes(q.OP_MOE, 256, 64, 4, 2)
     bad_i = (A16, 256, A16, A16, 4, 2, "q8_0", A16, "q8_0", A16, 64, A16, A16, A16, A16)
     assert status_of(q.moe_qmv_topk, *bad_i, w64) == "QMV_ESHAPE"
+    wc = q.qmv_workspace_bytes(q.OP_SHORT_CONV, 2048)
+    assert wc == 8192
+    conv = ("q4_k", A16, 2048, 2048, A16, A16, A16, "q4_k", A16, A16, A16)
+    assert status_of(q.qmv_short_conv, *conv, wc - 4) == "QMV_EWORKSPACE"
+    assert status_of(q.qmv_short_conv, "q4_k", A16, 0, 2048, A16, A16, A16, "q4_k", A16, A16, A16,
+                     wc) == "QMV_ESHAPE"
+    # out_proj has D = 100 columns: not a multiple of Q4_K's 256
+    assert status_of(q.qmv_short_conv, "q8_0", A16, 100, 256, A16, A16, A16, "q4_k", A16, A16, A16,
+                     wc) == "QMV_ESHAPE"
+    assert status_of(q.qmv_short_conv, "q4_k", A16, 2048, 2048, A16 + 4, A16, A16, "q4_k", A16, A16,
+                     A16, wc) == "QMV_EALIGN"
+    assert status_of(q.qmv_short_conv, "q4_k", A16, 2048, 2048, A16, A16, 0, "q4_k", A16, A16, A16,
+                     wc) == "QMV_EINVAL"
     wg = q.qmv_workspace_bytes(q.OP_GEMM_N, 4096, 4096, 16)
     assert wg > 0
     assert status_of(q.qmv_gemm_n, "q4_k", A16, 4096, 4096, 16, A16, A16, A16, wg - 4) == \
