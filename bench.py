@@ -285,6 +285,27 @@ def extras(torch, q, synth, step, progress):
     del sets, gu, dn
     progress("extras: MoE done")
 
+    # LFM2-style gated short-convolution block, one token: in_proj 6144 x 2048
+    # with the gates, the depthwise conv (k = 3) and its state in one launch,
+    # then out_proj 2048 x 2048 (Q4_K), cold by rotation
+    D = H = 2048
+    inp = make("q4_k", 3 * D, H, synth.T_W, 9)
+    outp = make("q4_k", H, D, synth.T_W, 10)
+    n = GiB // (inp.numel() + outp.numel()) + 1
+    sets = [(inp.clone(), outp.clone()) for _ in range(n)]
+    wc = synth.normal_device(9, synth.T_W, (D, 3), 0.5, dev)
+    stc = torch.zeros(D, 2, device=dev)
+    hc = synth.normal_device(9, synth.T_X, (H,), 1.0, dev)
+    outc = torch.empty(H, device=dev)
+    wsc = torch.empty(q.qmv_workspace_bytes(q.OP_SHORT_CONV, D), dtype=torch.uint8, device=dev)
+    calls = [lambda S=S: q.qmv_short_conv("q4_k", S[0], D, H, hc, wc, stc, "q4_k", S[1], outc, wsc)
+             for S in sets]
+    us = graph_time_us(torch, calls, reps=5)
+    nbytes = inp.numel() + outp.numel() + 4 * H + 12 * D + 16 * D + 8 * D + 4 * H
+    out["short_conv_lfm2_block"] = rec(us, nbytes, per="token (2 launches)", replicas=n)
+    del sets, inp, outp
+    progress("extras: short conv done")
+
     # small-batch verify (n = 8, 16) over the decode-step weights
     Hs, Is = step.H, step.I
     mats = []
