@@ -38,6 +38,7 @@ OP_SHORT_CONV = 4
 MAX_K = 32768
 MAX_SEGMENTS = 8
 MAX_N = 16
+MAX_PREFILL_N = 16384
 
 STATUS = {0: "QMV_OK", 1: "QMV_EINVAL", 2: "QMV_ESHAPE", 3: "QMV_EALIGN",
           4: "QMV_EWORKSPACE", 5: "QMV_EHIP"}
@@ -48,7 +49,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmv.so")
 EXPORTS = ["qmv_q8_0", "qmv_q4_k", "qmv_q6_k", "qmv_q4_0", "qmv_q4_1", "qmv_q5_0", "qmv_q5_1",
            "qmv_q8_1", "qmv_q5_k", "qmv_fused_rows", "qmv_gate_up_silu", "qmv_short_conv", "qmv_argmax",
            "moe_qmv_topk",
-           "qmv_gemm_n", "qmv_dequant", "qmv_quantize", "qmv_row_bytes", "qmv_workspace_bytes",
+           "qmv_gemm_n", "qmv_gemm", "qmv_dequant", "qmv_quantize", "qmv_row_bytes", "qmv_workspace_bytes",
            "qmv_last_hip_error", "qmv_status_str", "qmv_probe_stream_read",
            "qmv_time_next_launch"]
 
@@ -94,6 +95,7 @@ def load():
         "qmv_argmax": [ci, P, i64, i64, P, P, P, P, sz, P],
         "moe_qmv_topk": [P, i64, P, P, i32, i32, ci, P, ci, P, i64, P, P, P, P, sz, P],
         "qmv_gemm_n": [ci, P, i64, i64, i32, P, P, P, sz, P],
+        "qmv_gemm": [ci, P, i64, i64, i64, P, P, P],
         "qmv_dequant": [ci, P, i64, i64, P, P],
         "qmv_quantize": [ci, P, i64, i64, P, P],
         "qmv_probe_stream_read": [P, sz, P, P],
@@ -241,6 +243,10 @@ def qmv_gemm_n(t, blocks, M, K, n, X, Y, workspace=None, ws_bytes=None, stream=N
         ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _call("qmv_gemm_n", _type(t), _ptr(blocks), M, K, n, _ptr(X), _ptr(Y), _ptr(workspace),
           ws_bytes, _stream(stream))
+
+
+def qmv_gemm(t, blocks, M, K, n, X, Y, stream=None):
+    _call("qmv_gemm", _type(t), _ptr(blocks), M, K, n, _ptr(X), _ptr(Y), _stream(stream))
 
 
 def qmv_dequant(t, blocks, M, K, w_out, stream=None):

@@ -297,6 +297,19 @@ qmv_status qmv_gemm_n(qmv_type t, const void *blocks, int64_t M, int64_t K, int3
     return from_hip(launch_gemm_n(t, (const uint8_t *)blocks, M, K, n, X, Y, workspace, stream));
 }
 
+qmv_status qmv_gemm(qmv_type t, const void *blocks, int64_t M, int64_t K, int64_t n, const float *X,
+                    float *Y, hipStream_t stream) {
+    if (!core_type(t)) return QMV_EINVAL;
+    qmv_status st = check_matrix(t, blocks, M, K);
+    if (st != QMV_OK) return st;
+    if (n < 1 || n > QMV_MAX_PREFILL_N) return QMV_ESHAPE;
+    // X is addressed with 32-bit byte offsets
+    if ((uint64_t)n * (uint64_t)K * 4u > 0xFFFFFFFFull) return QMV_ESHAPE;
+    if (!X || !Y) return QMV_EINVAL;
+    if (!aligned(X, 16) || !aligned(Y, 4)) return QMV_EALIGN;
+    return from_hip(launch_gemm(t, (const uint8_t *)blocks, M, K, n, X, Y, stream));
+}
+
 qmv_status qmv_dequant(qmv_type t, const void *blocks, int64_t M, int64_t K, float *w_out,
                        hipStream_t stream) {
     qmv_status st = check_matrix(t, blocks, M, K);

@@ -475,12 +475,255 @@ hipError_t launch_typed(const GemmParams &p, hipStream_t s) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Prefill-size product (n up to thousands of tokens; BebeLM page, section
+// "性能表现": prompts are processed in batches).  With many tokens there is
+// parallelism across token blocks, so K is not split: a workgroup owns 128
+// rows and a block of 16 * TT tokens and walks every 256-weight window of
+// the rows.  Per window it stages X for its tokens (bf16 hi/lo operand
+// fragments and per-sub-block sums) in LDS, then multiplies while the next
+// window's weights are in flight in a second register set.  Each weight sub-block's codes and scales are formed
+// once and used by the TT token tiles.  Two workgroups share a compute unit,
+// so one's X staging overlaps the other's multiply.  Every output is one fixed-order sum
+// over the windows, so results are deterministic and need no workspace.
+// Workgroups are mapped so that those sharing rows run on the same XCD
+// (workgroups go to XCDs round-robin): their weights come from that XCD's L2.
+// ---------------------------------------------------------------------------
+constexpr int kPfTiles = 4;                 // token tiles of 16 per workgroup
+constexpr int kPfTokens = 16 * kPfTiles;    // tokens per workgroup
+constexpr int kXcds = 8;
+
+template <class F>
+struct PfLayout {
+    static constexpr int kVals = F::kNSub * 4 * kPfTokens * F::kKpl;  // = 256 * kPfTokens
+    static constexpr int kBytes = kVals * 2 * 2 + F::kNSub * kPfTokens * 4;
+};
+
+// X staging of one window for kPfTokens tokens; lane-group order as in the
+// small-batch staging (tokens fastest within 16, then the four lane groups),
+// then token tiles, then sub-blocks.
+template <class F>
+struct XStagePf {
+    static constexpr int kGroups = kPfTokens * kWin / F::kKpl;
+    static constexpr int kIters = kGroups / kThreads;
+    static_assert(kGroups % kThreads == 0, "whole iterations");
+    float v[kIters][F::kKpl];
+
+    __device__ static __forceinline__ void coords(int it, int &j, int &q, int &t) {
+        const int gi = (int)threadIdx.x + kThreads * it;
+        const int tl = gi % 16;
+        q = (gi / 16) % 4;
+        const int tt = (gi / 64) % kPfTiles;
+        j = gi / (64 * kPfTiles);
+        t = tt * 16 + tl;
+    }
+    __device__ __forceinline__ void load(const BufSrc &xv, int K, int tok0, int win) {
+#pragma unroll
+        for (int it = 0; it < kIters; it++) {
+            int j, q, t;
+            coords(it, j, q, t);
+            const int k = win * kWin + j * F::kSub + q * F::kKpl;
+            const uint32_t off = ((uint32_t)(tok0 + t) * (uint32_t)K + (uint32_t)k) * 4u;
+#pragma unroll
+            for (int e = 0; e < F::kKpl / 4; e++) {
+                const uint4 a = xv.ld16(off + 16 * e);
+                v[it][4 * e] = __builtin_bit_cast(float, a.x);
+                v[it][4 * e + 1] = __builtin_bit_cast(float, a.y);
+                v[it][4 * e + 2] = __builtin_bit_cast(float, a.z);
+                v[it][4 * e + 3] = __builtin_bit_cast(float, a.w);
+            }
+        }
+    }
+    __device__ __forceinline__ void store(uint8_t *base, int win, int K) const {
+        using L = PfLayout<F>;
+#pragma unroll
+        for (int it = 0; it < kIters; it++) {
+            int j, q, t;
+            coords(it, j, q, t);
+            const int k = win * kWin + j * F::kSub + q * F::kKpl;
+            const bool in_k = k < K;
+            uint32_t hi[F::kKpl / 2], lo[F::kKpl / 2];
+            float sum = 0.f;
+#pragma unroll
+            for (int i2 = 0; i2 < F::kKpl / 2; i2++) {
+                f32x2 xx;
+                xx.x = in_k ? v[it][F::perm(2 * i2)] : 0.f;
+                xx.y = in_k ? v[it][F::perm(2 * i2 + 1)] : 0.f;
+                const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(xx, bf16x2));
+                const float h0 = __builtin_bit_cast(float, hb << 16);
+                const float h1 = __builtin_bit_cast(float, hb & 0xFFFF0000u);
+                f32x2 rr;
+                rr.x = xx.x - h0;
+                rr.y = xx.y - h1;
+                const uint32_t lb = __builtin_bit_cast(uint32_t, __builtin_convertvector(rr, bf16x2));
+                hi[i2] = hb;
+                lo[i2] = lb;
+                sum += (h0 + __builtin_bit_cast(float, lb << 16)) +
+                       (h1 + __builtin_bit_cast(float, lb & 0xFFFF0000u));
+            }
+            const int pos = ((j * 4 + q) * kPfTokens + t) * F::kKpl;
+            *reinterpret_cast<BFrag<F> *>(base + 2 * pos) = __builtin_bit_cast(BFrag<F>, hi);
+            *reinterpret_cast<BFrag<F> *>(base + 2 * (L::kVals + pos)) = __builtin_bit_cast(BFrag<F>, lo);
+            // lane groups q = 0..3 of (j, t) are lanes tl, tl + 16, tl + 32, tl + 48
+            sum += __shfl_xor(sum, 16, kWave);
+            sum += __shfl_xor(sum, 32, kWave);
+            if (q == 0) reinterpret_cast<float *>(base + 4 * L::kVals)[j * kPfTokens + t] = sum;
+        }
+    }
+};
+
+template <class F>
+__global__ __launch_bounds__(kThreads, 2) void gemm_pf_kernel(GemmParams p, int token_blocks,
+                                                            int row_groups_pad) {
+    using L = PfLayout<F>;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int r = lane & 15, q = lane >> 4;
+    // XCD-aware order: workgroups b and b + 8 share an XCD; consecutive
+    // workgroups of one XCD take the token blocks of one row group
+    const int b = (int)blockIdx.x;
+    const int local = b / kXcds;
+    const int tb = local % token_blocks;
+    const int rg = (b % kXcds) + kXcds * (local / token_blocks);
+    if (rg * kRowsPerWG >= p.M) return;  // padding of the row groups
+    (void)row_groups_pad;
+    const int row0 = __builtin_amdgcn_readfirstlane(rg * kRowsPerWG + wave * 16);
+    const int tok0 = tb * kPfTokens;
+    const int nblocks = p.K / 32;
+    const int wtotal = (p.K + kWin - 1) / kWin;
+
+    const int rows_left = p.M - row0 > 0 ? p.M - row0 : 0;
+    const BufSrc src(p.W + (int64_t)row0 * p.row_bytes,
+                     (uint64_t)rows_left * (uint64_t)(uint32_t)p.row_bytes);
+    const uint32_t lane_off = (uint32_t)r * (uint32_t)p.row_bytes;
+    const BufSrc xview(reinterpret_cast<const uint8_t *>(p.X), (uint64_t)p.n * (uint32_t)p.K * 4u);
+
+    auto nvalid_of = [&](int wi) {
+        if constexpr (std::is_same<F, GQ80>::value) {
+            const int left = nblocks - wi * 8;
+            return left < 8 ? left : 8;
+        } else {
+            return F::kNSub;
+        }
+    };
+    auto wload = [&](int wi) {
+        wi = __builtin_amdgcn_readfirstlane(wi < wtotal ? wi : wtotal - 1);
+        return F::load(src, lane_off + (uint32_t)wi * F::kWinBytes, q, nvalid_of(wi));
+    };
+
+    const uint32_t kmask = __builtin_amdgcn_readfirstlane(0x000F000Fu);
+    uint32_t kbias;
+    asm("v_mov_b32 %0, %1" : "=v"(kbias) : "i"(kB16));
+    f32x4 acc[kPfTiles];
+#pragma unroll
+    for (int tt = 0; tt < kPfTiles; tt++) acc[tt] = {0.f, 0.f, 0.f, 0.f};
+
+    typename F::Regs wcur = wload(0);
+
+    auto multiply = [&](const typename F::Regs &w, const uint8_t *base, int wi) {
+        const __bf16 *xhi = reinterpret_cast<const __bf16 *>(base);
+        const __bf16 *xlo = xhi + L::kVals;
+        const float *xsum = reinterpret_cast<const float *>(base + 4 * L::kVals);
+        const int nsub = nvalid_of(wi);
+#pragma unroll
+        for (int j = 0; j < F::kNSub; j++) {
+            if (j >= nsub) break;
+            const Frag<F> bcode = F::codes(w, j, kmask, kbias);
+            float scale, corr;
+            F::scales(w, j, scale, corr);
+#pragma unroll
+            for (int tt = 0; tt < kPfTiles; tt++) {
+                const int fo = ((j * 4 + q) * kPfTokens + tt * 16 + r) * F::kKpl;
+                const Frag<F> ah = *reinterpret_cast<const Frag<F> *>(xhi + fo);
+                const Frag<F> al = *reinterpret_cast<const Frag<F> *>(xlo + fo);
+                f32x4 c = {0.f, 0.f, 0.f, 0.f};
+                c = mfma<F>(ah, bcode, c);
+                c = mfma<F>(al, bcode, c);
+                const float4 sx = *reinterpret_cast<const float4 *>(xsum + j * kPfTokens + tt * 16 + 4 * q);
+                acc[tt][0] = fmaf(scale, c[0], fmaf(-corr, sx.x, acc[tt][0]));
+                acc[tt][1] = fmaf(scale, c[1], fmaf(-corr, sx.y, acc[tt][1]));
+                acc[tt][2] = fmaf(scale, c[2], fmaf(-corr, sx.z, acc[tt][2]));
+                acc[tt][3] = fmaf(scale, c[3], fmaf(-corr, sx.w, acc[tt][3]));
+                // keep each tile's operand reads and epilogue next to its
+                // MFMAs (hoisting or sinking them across tiles would need
+                // more registers than a wave has)
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    };
+
+    // Per window: stage X for the workgroup's tokens, then multiply while the
+    // next window's weights are in flight (the load is unconditional: after
+    // the last window it repeats it and nothing reads the result).  The X
+    // load latency is hidden by the other workgroup on the compute unit (two
+    // fit: one LDS buffer each).  The register sets trade places by a copy,
+    // so the loop body exists once.
+    for (int wi = 0; wi < wtotal; wi++) {
+        const int wn = wi + 1 < wtotal ? wi + 1 : wi;
+        {
+            XStagePf<F> xs;
+            xs.load(xview, p.K, tok0, wi);
+            xs.store(smem, wi, p.K);
+        }
+        __syncthreads();
+        typename F::Regs wnext = wload(wn);
+        multiply(wcur, smem, wi);
+        __syncthreads();
+        wcur = wnext;
+    }
+
+    const int row = row0 + r;
+    if (row < p.M) {
+#pragma unroll
+        for (int tt = 0; tt < kPfTiles; tt++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int t = tok0 + tt * 16 + 4 * q + i;
+                if (t < p.n) p.Y[(int64_t)t * p.M + row] = acc[tt][i];
+            }
+    }
+}
+
+template <class F>
+hipError_t launch_pf(GemmParams p, hipStream_t s) {
+    const size_t lds = (size_t)PfLayout<F>::kBytes;
+    hipError_t e = ensure_lds((const void *)gemm_pf_kernel<F>, lds);
+    if (e != hipSuccess) return e;
+    const int row_groups = (p.M + kRowsPerWG - 1) / kRowsPerWG;
+    const int rg_pad = (row_groups + kXcds - 1) / kXcds * kXcds;
+    const int token_blocks = (p.n + kPfTokens - 1) / kPfTokens;
+    const int64_t grid = (int64_t)rg_pad * token_blocks;
+    if (grid > 0x7FFFFFFFll) return hipErrorInvalidValue;
+    return launch_main(gemm_pf_kernel<F>, dim3((unsigned)grid), dim3(kThreads), lds, s, p,
+                       token_blocks, rg_pad);
+}
+
 }  // namespace
 
 size_t gemm_n_workspace(int64_t M, int64_t K, int32_t n) {
     const int64_t kw = windows_per_slice(M, K);
     const int64_t slices = ((K + kWin - 1) / kWin + kw - 1) / kw;
     return slices > 1 ? (size_t)slices * (size_t)n * (size_t)M * sizeof(float) : 0;
+}
+
+hipError_t launch_gemm(int type, const uint8_t *W, int64_t M, int64_t K, int64_t n, const float *X,
+                       float *Y, hipStream_t s) {
+    GemmParams p{};
+    p.W = W;
+    p.M = (int32_t)M;
+    p.K = (int32_t)K;
+    p.n = (int32_t)n;
+    p.row_bytes = (int32_t)row_bytes_of(type, K);
+    p.X = X;
+    p.Y = Y;
+    p.partial = nullptr;
+    switch (type) {
+    case kQ4K: return launch_pf<GQ4K>(p, s);
+    case kQ6K: return launch_pf<GQ6K>(p, s);
+    case kQ80: return launch_pf<GQ80>(p, s);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_gemm_n(int type, const uint8_t *W, int64_t M, int64_t K, int32_t n,

@@ -101,6 +101,8 @@ typedef enum { QMV_OP_ARGMAX = 1, QMV_OP_MOE = 2, QMV_OP_GEMM_N = 3, QMV_OP_SHOR
 #define QMV_MAX_SEGMENTS 8
 /* Most columns in one qmv_gemm_n call. */
 #define QMV_MAX_N 16
+/* Most tokens in one qmv_gemm call. */
+#define QMV_MAX_PREFILL_N 16384
 
 /* ---- single token: y[M] = dequant(W)[M x K] . x[K] ----------------------
  * blocks: M*K/B blocks, row-major (row i is K/B consecutive blocks).
@@ -221,6 +223,18 @@ qmv_status moe_qmv_topk(const float *x, int64_t H, const float *router, const fl
 qmv_status qmv_gemm_n(qmv_type t, const void *blocks, int64_t M, int64_t K, int32_t n,
                       const float *X, float *Y, void *workspace, size_t ws_bytes,
                       hipStream_t stream);
+
+/* ---- prefill-size product: Y[n][M] = X[n][K] . dequant(W)^T --------------
+ * BebeLM page, section "性能表现" (prompt tokens are processed as a batch,
+ * unlike the one-token decode).  X: f32 n x K row-major, Y: f32 n x M
+ * row-major, 1 <= n <= QMV_MAX_PREFILL_N and n * K * 4 < 2^32.  Formats
+ * Q8_0, Q4_K, Q6_K.  Same arithmetic as qmv_gemm_n (bf16 MFMA on the exact
+ * codes, X as bf16 hi + lo, f32 scales per sub-block), so within 1e-5 *
+ * sum_k |w_ik x_k| per output; K is not split (a workgroup covers 64 tokens
+ * by 128 rows and walks all of K), so each output is one fixed-order sum:
+ * deterministic, no workspace. */
+qmv_status qmv_gemm(qmv_type t, const void *blocks, int64_t M, int64_t K, int64_t n, const float *X,
+                    float *Y, hipStream_t stream);
 
 /* ---- dequantise to f32 (verification surface): w_out[M][K] --------------
  * Bit-exact block decoding, the values every matvec above is defined on. */

@@ -80,6 +80,10 @@ def test_pointer_and_type_errors():
     # the verify product and the device quantiser take Q8_0, Q4_K and Q6_K only
     assert status_of(q.qmv_gemm_n, "q5_k", A16, 4, 256, 8, A16, A16, A16, 1 << 20) == "QMV_EINVAL"
     assert status_of(q.qmv_quantize, "q4_0", A16, 4, 256, A16) == "QMV_EINVAL"
+    assert status_of(q.qmv_gemm, "q5_k", A16, 4, 256, 64, A16, A16) == "QMV_EINVAL"
+    assert status_of(q.qmv_gemm, "q4_k", A16, 4, 256, 0, A16, A16) == "QMV_ESHAPE"
+    assert status_of(q.qmv_gemm, "q4_k", A16, 4, 256, q.MAX_PREFILL_N + 1, A16, A16) == "QMV_ESHAPE"
+    assert status_of(q.qmv_gemm, "q4_k", A16, 4, 256, 64, A16 + 4, A16) == "QMV_EALIGN"
     assert status_of(q.qmv_fused_rows, "q4_k", A16, 256, A16, [1] * 9, [A16] * 9) == "QMV_EINVAL"
     assert status_of(q.qmv_fused_rows, "q4_k", A16, 256, A16, [], []) == "QMV_EINVAL"
     assert status_of(q.qmv_gate_up_silu, "q4_k", A16, 8, 256, A16, 0) == "QMV_EINVAL"

@@ -1,0 +1,78 @@
+"""GPU parity for qmv_gemm, the prefill-size product Y[n][M] = X[n][K] W^T
+(BebeLM page, section "性能表现": prompt tokens go through as a batch),
+against the oracle's f64 product (the same definition as the small batch).
+
+Bound: as the verify product (exact codes on the matrix cores, X as bf16
+hi + lo, f32 scales), within 1e-5 * sum_k |w_ik X[j][k]| per output.
+Also: permuting X's rows permutes Y's rows bit for bit (tokens are
+independent MFMA rows) and two runs are identical (K is not split).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import assert_rel, dev, empty, host, quantized
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import gguf_dequant_matvec_amd as q  # noqa: E402
+
+
+def gemm_gpu(t, bd, M, K, X):
+    n = X.shape[0]
+    Y = empty(n * M)
+    q.qmv_gemm(t, bd, M, K, n, dev(X), Y)
+    return host(Y).reshape(n, M)
+
+
+SHAPES = [
+    ("q4_k", 300, 4096, 100),    # ragged rows and a partial token block
+    ("q4_k", 129, 2048, 64),
+    ("q4_k", 40, 256, 17),
+    ("q6_k", 129, 1536, 70),
+    ("q6_k", 64, 4096, 33),
+    ("q8_0", 77, 224, 130),      # a partial last window of Q8_0 blocks
+    ("q8_0", 200, 576, 65),
+    ("q4_k", 33, 512, 1),
+]
+
+
+@pytest.mark.parametrize("t,M,K,n", SHAPES)
+def test_gemm_parity(t, M, K, n):
+    b = quantized(t, M, K, 1100 + M)
+    X = synth.activations(1101 + M, K, n=n)
+    Yr, Ar = oracle.gemm_n(t, b, M, K, X)
+    Y = gemm_gpu(t, dev(b), M, K, X)
+    worst = assert_rel(Y.ravel(), Yr.ravel(), Ar.ravel(), what=f"{t} {M}x{K} n={n}")
+    print(f"{t} {M}x{K} n={n}: worst |dY|/sum|wx| = {worst:.2e}")
+
+
+@pytest.mark.parametrize("t", ["q4_k", "q6_k", "q8_0"])
+def test_gemm_token_permutation_and_determinism(t):
+    M, K, n = 260, 1024, 150
+    b = quantized(t, M, K, 1110)
+    X = synth.activations(1111, K, n=n)
+    bd = dev(b)
+    Y = gemm_gpu(t, bd, M, K, X)
+    perm = np.random.default_rng(7).permutation(n)
+    Yp = gemm_gpu(t, bd, M, K, X[perm])
+    assert np.array_equal(Yp.view(np.uint32), Y[perm].view(np.uint32))
+    Y2 = gemm_gpu(t, bd, M, K, X)
+    assert np.array_equal(Y2.view(np.uint32), Y.view(np.uint32))
+
+
+def test_gemm_llama8b_gate_up_n512_sampled():
+    t, M, K, n = "q4_k", sum(synth.CONFIG4["gate_up"]), synth.CONFIG4["hidden"], 512
+    b = quantized(t, M, K, 902)
+    X = synth.activations(1120, K, n=n)
+    Y = gemm_gpu(t, dev(b), M, K, X)
+    g = np.random.default_rng(9)
+    rows = np.unique(np.concatenate([[0, M - 1], g.integers(0, M, 48)])).astype(np.int64)
+    for j in [0, 1, 63, 64, 200, 511]:
+        yr, ar = oracle.qmv_rows(t, b, M, K, X[j], rows)
+        assert_rel(Y[j, rows], yr, ar, what=f"token {j}")
