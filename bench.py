@@ -332,6 +332,25 @@ def extras(torch, q, synth, step, progress):
         del Y, wsn
     progress("extras: verify done")
 
+    # prefill-size product (n = 64, 256, 512) over the same weights
+    for nn in (64, 256, 512):
+        Xh = synth.normal_device(11, synth.T_X, (nn, Hs), 1.0, dev)
+        Xi = synth.normal_device(11, synth.T_XN, (nn, Is), 1.0, dev)
+        Y = torch.empty(nn * sum(step.gu_rows), device=dev)
+        calls = [lambda m=m, M_=M_, K_=K_: q.qmv_gemm("q4_k", m, M_, K_, nn,
+                                                     Xh if K_ == Hs else Xi, Y)
+                 for m, M_, K_ in mats]
+        us = graph_time_us(torch, calls, reps=1) * len(calls)   # per 32-layer pass
+        io = sum(4 * nn * (K_ + M_) for _, M_, K_ in mats)
+        flops = sum(2 * nn * M_ * K_ for _, M_, K_ in mats)
+        r = rec(us, wbytes + io, per=f"32-layer pass ({len(calls)} calls)", n=nn)
+        r["tflops"] = round(flops / (us * 1e-6) / 1e12, 2)
+        r["pct_of_bf16_mfma_peak"] = round(100 * flops / (us * 1e-6) / 2.5e15, 1)
+        r["tok_per_s"] = round(nn / (us * 1e-6), 1)
+        out[f"prefill_n{nn}_32_layers_q4_k"] = r
+        del Y
+    progress("extras: prefill done")
+
     # gate+up with the gated product h = silu(g) * u in the same launch, over
     # the 32 layers' gate+up stacks (2.1 GB, cold by rotation); the plain
     # fused gate+up over the same stacks for comparison

@@ -489,12 +489,13 @@ hipError_t launch_typed(const GemmParams &p, hipStream_t s) {
 // Workgroups are mapped so that those sharing rows run on the same XCD
 // (workgroups go to XCDs round-robin): their weights come from that XCD's L2.
 // ---------------------------------------------------------------------------
-constexpr int kPfTiles = 4;                 // token tiles of 16 per workgroup
-constexpr int kPfTokens = 16 * kPfTiles;    // tokens per workgroup
 constexpr int kXcds = 8;
 
-template <class F>
+// TT: token tiles of 16 per workgroup (1, 2 or 4, chosen per call so that
+// there are enough workgroups)
+template <class F, int TT>
 struct PfLayout {
+    static constexpr int kPfTokens = 16 * TT;
     static constexpr int kVals = F::kNSub * 4 * kPfTokens * F::kKpl;  // = 256 * kPfTokens
     static constexpr int kBytes = kVals * 2 * 2 + F::kNSub * kPfTokens * 4;
 };
@@ -502,8 +503,9 @@ struct PfLayout {
 // X staging of one window for kPfTokens tokens; lane-group order as in the
 // small-batch staging (tokens fastest within 16, then the four lane groups),
 // then token tiles, then sub-blocks.
-template <class F>
+template <class F, int TT>
 struct XStagePf {
+    static constexpr int kPfTiles = TT, kPfTokens = 16 * TT;
     static constexpr int kGroups = kPfTokens * kWin / F::kKpl;
     static constexpr int kIters = kGroups / kThreads;
     static_assert(kGroups % kThreads == 0, "whole iterations");
@@ -535,7 +537,7 @@ struct XStagePf {
         }
     }
     __device__ __forceinline__ void store(uint8_t *base, int win, int K) const {
-        using L = PfLayout<F>;
+        using L = PfLayout<F, TT>;
 #pragma unroll
         for (int it = 0; it < kIters; it++) {
             int j, q, t;
@@ -572,10 +574,11 @@ struct XStagePf {
     }
 };
 
-template <class F>
+template <class F, int TT>
 __global__ __launch_bounds__(kThreads, 2) void gemm_pf_kernel(GemmParams p, int token_blocks,
                                                             int row_groups_pad) {
-    using L = PfLayout<F>;
+    using L = PfLayout<F, TT>;
+    constexpr int kPfTiles = TT, kPfTokens = 16 * TT;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -662,7 +665,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_pf_kernel(GemmParams p, int 
     for (int wi = 0; wi < wtotal; wi++) {
         const int wn = wi + 1 < wtotal ? wi + 1 : wi;
         {
-            XStagePf<F> xs;
+            XStagePf<F, TT> xs;
             xs.load(xview, p.K, tok0, wi);
             xs.store(smem, wi, p.K);
         }
@@ -685,18 +688,30 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_pf_kernel(GemmParams p, int 
     }
 }
 
-template <class F>
-hipError_t launch_pf(GemmParams p, hipStream_t s) {
-    const size_t lds = (size_t)PfLayout<F>::kBytes;
-    hipError_t e = ensure_lds((const void *)gemm_pf_kernel<F>, lds);
+template <class F, int TT>
+hipError_t launch_pf_tt(GemmParams p, int rg_pad, hipStream_t s) {
+    const size_t lds = (size_t)PfLayout<F, TT>::kBytes;
+    hipError_t e = ensure_lds((const void *)gemm_pf_kernel<F, TT>, lds);
     if (e != hipSuccess) return e;
-    const int row_groups = (p.M + kRowsPerWG - 1) / kRowsPerWG;
-    const int rg_pad = (row_groups + kXcds - 1) / kXcds * kXcds;
-    const int token_blocks = (p.n + kPfTokens - 1) / kPfTokens;
+    const int token_blocks = (p.n + 16 * TT - 1) / (16 * TT);
     const int64_t grid = (int64_t)rg_pad * token_blocks;
     if (grid > 0x7FFFFFFFll) return hipErrorInvalidValue;
-    return launch_main(gemm_pf_kernel<F>, dim3((unsigned)grid), dim3(kThreads), lds, s, p,
+    return launch_main(gemm_pf_kernel<F, TT>, dim3((unsigned)grid), dim3(kThreads), lds, s, p,
                        token_blocks, rg_pad);
+}
+
+// the most tokens per workgroup that still gives two workgroups per compute
+// unit; fewer tokens per workgroup otherwise (more workgroups, each staging
+// X for fewer tokens)
+template <class F>
+hipError_t launch_pf(GemmParams p, hipStream_t s) {
+    const int row_groups = (p.M + kRowsPerWG - 1) / kRowsPerWG;
+    const int rg_pad = (row_groups + kXcds - 1) / kXcds * kXcds;
+    const int64_t want = 2 * (int64_t)device_cu_count();
+    auto wgs = [&](int tt) { return (int64_t)rg_pad * ((p.n + 16 * tt - 1) / (16 * tt)); };
+    if (wgs(4) >= want) return launch_pf_tt<F, 4>(p, rg_pad, s);
+    if (wgs(2) >= want) return launch_pf_tt<F, 2>(p, rg_pad, s);
+    return launch_pf_tt<F, 1>(p, rg_pad, s);
 }
 
 }  // namespace
