@@ -33,6 +33,10 @@
  *  - Small-batch verify: FlareLLM page, same section (n-gram speculative
  *    decoding verifies several drafted tokens against the same weights).
  *
+ *  - Prefill-size product: BebeLM page, section "性能表现" (prompts go
+ *    through as batches); the same definition as the small batch, so
+ *    oracle_gemm_n serves both.
+ *
  * Every function returns 0 on success and -1 on a bad argument.
  */
 #include <math.h>
