@@ -570,7 +570,9 @@ def main():
         for (kind, t, K, b, fn), (a, z) in zip(launches, pairs):
             q.qmv_time_next_launch(a, z)
             fn()
-        torch.cuda.synchronize()
+            # one launch at a time: a dispatch queued behind a running kernel
+            # would carry its wait in its start timestamp
+            torch.cuda.synchronize()
         for (kind, t, K, b, fn), (a, z) in zip(launches, pairs):
             d = per.setdefault(kind, dict(fmt=t, K=K, ms=0.0, n=0, bytes=0))
             d["ms"] += a.elapsed_time(z)
@@ -589,6 +591,11 @@ def main():
     dom_bytes = sum(d["bytes"] for d in dom) / sum(d["n"] for d in dom)
     dom_ms = sum(d["ms"] for d in dom) / sum(d["n"] for d in dom)
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+
+    # the same launches back to back in a HIP graph: events around the
+    # replays, divided by the launch count (includes the gaps between them)
+    dom_calls = [fn for (kind, t, K, b, fn) in launches if kind in ("qkv", "o", "gate_up")]
+    dom_graph_us = graph_time_us(torch, dom_calls, reps=max(2, args.steps // 5))
 
     progress("per-launch timing done; streaming-read probe")
     # achievable streaming-read ceiling on this device (same 128-bit loads)
@@ -658,6 +665,7 @@ def main():
             "kernel": DOMINANT + " (q4_k, K=4096: QKV, O, gate+up launches)",
             "algorithmic_bytes_per_launch": round(dom_bytes),
             "us_per_launch": round(dom_ms * 1e3, 3),
+            "us_per_launch_in_graph": round(dom_graph_us, 3),
         },
     }
     if not args.no_extras:
