@@ -47,11 +47,10 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmv.so")
 
 # every symbol include/qmv.h declares
 EXPORTS = ["qmv_q8_0", "qmv_q4_k", "qmv_q6_k", "qmv_q4_0", "qmv_q4_1", "qmv_q5_0", "qmv_q5_1",
-           "qmv_q8_1", "qmv_q5_k", "qmv_fused_rows", "qmv_gate_up_silu", "qmv_short_conv", "qmv_argmax",
-           "moe_qmv_topk",
-           "qmv_gemm_n", "qmv_gemm", "qmv_dequant", "qmv_quantize", "qmv_row_bytes", "qmv_workspace_bytes",
-           "qmv_last_hip_error", "qmv_status_str", "qmv_probe_stream_read",
-           "qmv_time_next_launch"]
+           "qmv_q8_1", "qmv_q5_k", "qmv_fused_rows", "qmv_fused_rows2", "qmv_gate_up_silu",
+           "qmv_short_conv", "qmv_argmax", "moe_qmv_topk", "qmv_gemm_n", "qmv_gemm", "qmv_dequant",
+           "qmv_quantize", "qmv_row_bytes", "qmv_workspace_bytes", "qmv_last_hip_error",
+           "qmv_status_str", "qmv_probe_stream_read", "qmv_time_next_launch"]
 
 
 class QmvError(RuntimeError):
@@ -90,6 +89,7 @@ def load():
         "qmv_q8_1": [P, i64, i64, P, P, P],
         "qmv_q5_k": [P, i64, i64, P, P, P],
         "qmv_fused_rows": [ci, P, i64, P, i32, P, P, P],
+        "qmv_fused_rows2": [ci, P, i32, P, P, ci, P, i32, P, P, i64, P, P],
         "qmv_gate_up_silu": [ci, P, i64, i64, P, P, P],
         "qmv_short_conv": [ci, P, i64, i64, P, P, P, ci, P, P, P, sz, P],
         "qmv_argmax": [ci, P, i64, i64, P, P, P, P, sz, P],
@@ -208,6 +208,20 @@ def qmv_fused_rows(t, blocks, K, x, seg_rows, y_seg, stream=None):
     ys = (ctypes.c_void_p * max(len(y_seg), 1))(*[_ptr(y) for y in y_seg])
     _call("qmv_fused_rows", _type(t), _ptr(blocks), K, _ptr(x), n,
           ctypes.cast(rows, ctypes.c_void_p), ctypes.cast(ys, ctypes.c_void_p), _stream(stream))
+
+
+def qmv_fused_rows2(t1, blocks1, seg_rows1, y_seg1, t2, blocks2, seg_rows2, y_seg2, K, x,
+                    stream=None):
+    def arrays(seg_rows, y_seg):
+        rows = (ctypes.c_int64 * max(len(seg_rows), 1))(*seg_rows)
+        ys = (ctypes.c_void_p * max(len(y_seg), 1))(*[_ptr(y) for y in y_seg])
+        return rows, ys
+    r1, y1 = arrays(seg_rows1, y_seg1)
+    r2, y2 = arrays(seg_rows2, y_seg2)
+    _call("qmv_fused_rows2", _type(t1), _ptr(blocks1), len(seg_rows1), ctypes.cast(r1, ctypes.c_void_p),
+          ctypes.cast(y1, ctypes.c_void_p), _type(t2), _ptr(blocks2), len(seg_rows2),
+          ctypes.cast(r2, ctypes.c_void_p), ctypes.cast(y2, ctypes.c_void_p), K, _ptr(x),
+          _stream(stream))
 
 
 def qmv_gate_up_silu(t, blocks, I, K, x, h, stream=None):

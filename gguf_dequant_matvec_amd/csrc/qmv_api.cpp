@@ -184,12 +184,12 @@ qmv_status qmv_q8_1(const void *blocks, int64_t M, int64_t K, const float *x, fl
     return single(kQ81, blocks, M, K, x, y, stream);
 }
 
-qmv_status qmv_fused_rows(qmv_type t, const void *blocks, int64_t K, const float *x,
-                          int32_t nseg, const int64_t *seg_rows, float *const *y_seg,
-                          hipStream_t stream) {
+// Segment table of one row stack; total rows in *total.
+static qmv_status build_segments(int32_t nseg, const int64_t *seg_rows, float *const *y_seg,
+                                 SegTable &seg, int64_t *total_out) {
     if (!seg_rows || !y_seg) return QMV_EINVAL;
     if (nseg < 1 || nseg > QMV_MAX_SEGMENTS) return QMV_EINVAL;
-    SegTable seg{};
+    seg = SegTable{};
     seg.n = nseg;
     int64_t total = 0;
     for (int s = 0; s < nseg; s++) {
@@ -202,7 +202,40 @@ qmv_status qmv_fused_rows(qmv_type t, const void *blocks, int64_t K, const float
         total += seg_rows[s];
     }
     seg.start[nseg] = (int32_t)total;
-    qmv_status st = check_matrix(t, blocks, total, K);
+    *total_out = total;
+    return QMV_OK;
+}
+
+qmv_status qmv_fused_rows2(qmv_type t1, const void *blocks1, int32_t nseg1,
+                           const int64_t *seg_rows1, float *const *y_seg1, qmv_type t2,
+                           const void *blocks2, int32_t nseg2, const int64_t *seg_rows2,
+                           float *const *y_seg2, int64_t K, const float *x, hipStream_t stream) {
+    auto mixable = [](int t) { return t == kQ4K || t == kQ5K || t == kQ6K; };
+    if (!mixable(t1) || !mixable(t2) || t1 == t2) return QMV_EINVAL;
+    SegTable seg1, seg2;
+    int64_t M1 = 0, M2 = 0;
+    qmv_status st = build_segments(nseg1, seg_rows1, y_seg1, seg1, &M1);
+    if (st != QMV_OK) return st;
+    st = build_segments(nseg2, seg_rows2, y_seg2, seg2, &M2);
+    if (st != QMV_OK) return st;
+    st = check_matrix(t1, blocks1, M1, K);
+    if (st != QMV_OK) return st;
+    st = check_matrix(t2, blocks2, M2, K);
+    if (st != QMV_OK) return st;
+    if (!x) return QMV_EINVAL;
+    if (!aligned(x, 16)) return QMV_EALIGN;
+    return from_hip(launch_rows_mixed(t1, (const uint8_t *)blocks1, M1, seg1, t2,
+                                      (const uint8_t *)blocks2, M2, seg2, K, x, stream));
+}
+
+qmv_status qmv_fused_rows(qmv_type t, const void *blocks, int64_t K, const float *x,
+                          int32_t nseg, const int64_t *seg_rows, float *const *y_seg,
+                          hipStream_t stream) {
+    SegTable seg;
+    int64_t total = 0;
+    qmv_status st = build_segments(nseg, seg_rows, y_seg, seg, &total);
+    if (st != QMV_OK) return st;
+    st = check_matrix(t, blocks, total, K);
     if (st != QMV_OK) return st;
     if (!x) return QMV_EINVAL;
     if (!aligned(x, 16)) return QMV_EALIGN;

@@ -70,6 +70,9 @@ hipError_t ensure_lds(const void *kernel, size_t bytes);
 
 hipError_t launch_rows_store(int type, const uint8_t *W, int64_t M, int64_t K, const float *x,
                              const SegTable &seg, hipStream_t s);
+hipError_t launch_rows_mixed(int t1, const uint8_t *W1, int64_t M1, const SegTable &seg1, int t2,
+                             const uint8_t *W2, int64_t M2, const SegTable &seg2, int64_t K,
+                             const float *x, hipStream_t s);
 hipError_t launch_rows_silu(int type, const uint8_t *W, int64_t I, int64_t K, const float *x,
                             float *h, hipStream_t s);
 hipError_t launch_short_conv(int in_t, const uint8_t *in_proj, int64_t D, int64_t H,

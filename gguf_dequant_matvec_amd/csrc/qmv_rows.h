@@ -225,8 +225,10 @@ __device__ __forceinline__ void moe_select(const MoeArgs &m, int32_t *sel, float
 // XR: a row is a single unit step, so every lane keeps the same unit for the
 // whole launch and reads its activations from LDS once, after staging, into
 // registers (plain and argmax modes only).
+// The body takes its workgroup index `bid` among `nblk` workgroups, so one
+// launch can run two bodies side by side on separate workgroup ranges.
 template <class F, int G, int R, int MODE, int KS, bool XR>
-__global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
+__device__ __forceinline__ void rows_body(const RowsParams &p, const int bid, const int nblk) {
     constexpr bool kMoe = MODE == kModeMoeGateUp || MODE == kModeMoeDown;
     extern __shared__ float smem[];
     float *xs = smem;
@@ -249,7 +251,7 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
     static_assert(MODE != kModeShortConv || R == 3, "B, C and x slots");
     constexpr int kRowsPerTile = kPair ? P : R * P;
     const int ntiles = (p.M + kRowsPerTile - 1) / kRowsPerTile;
-    const int tile_stride = KS == 1 ? (int)gridDim.x * waves_per_block : (int)gridDim.x;
+    const int tile_stride = KS == 1 ? nblk * waves_per_block : nblk;
     const int it0 = KS == 1 ? 0 : wave;  // this wave's first unit step of a tile
     static_assert(KS == 1 || KS == kBlockThreads / kWave, "K split over the workgroup's waves");
     // K-split partial sums: [tile parity][wave][row slot][row in wave]
@@ -433,7 +435,7 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
     // Items of this wave: tiles t_first, t_first + stride, ..., each with
     // `iters` unit steps.
     const int t_first = __builtin_amdgcn_readfirstlane(
-        KS == 1 ? (int)blockIdx.x * waves_per_block + wave : (int)blockIdx.x);
+        KS == 1 ? bid * waves_per_block + wave : bid);
     const int my_tiles = t_first < ntiles ? (ntiles - 1 - t_first) / tile_stride + 1 : 0;
     const int steps = (iters - it0 + KS - 1) / KS;  // this wave's steps per tile
     const int n_items = my_tiles * steps;
@@ -480,7 +482,7 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
             }
             const float4 h = make_float4(siluf(gg.x) * uu.x, siluf(gg.y) * uu.y,
                                          siluf(gg.z) * uu.z, siluf(gg.w) * uu.w);
-            if (blockIdx.x == 0 && base < K) *reinterpret_cast<float4 *>(p.moe.h + base) = h;
+            if (bid == 0 && base < K) *reinterpret_cast<float4 *>(p.moe.h + base) = h;
             const float w = wsel[sl];
             put_x4<F>(xs, sums, base, base < K, make_float4(w * h.x, w * h.y, w * h.z, w * h.w));
         };
@@ -543,9 +545,26 @@ __global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
         if (threadIdx.x == 0) {
             uint64_t k = wave_best[0];
             for (int w = 1; w < waves_per_block; w++) k = wave_best[w] > k ? wave_best[w] : k;
-            p.partials[blockIdx.x] = k;
+            p.partials[bid] = k;
         }
     }
+}
+
+template <class F, int G, int R, int MODE, int KS, bool XR>
+__global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
+    rows_body<F, G, R, MODE, KS, XR>(p, (int)blockIdx.x, (int)gridDim.x);
+}
+
+// Two row stacks of different formats sharing x in one launch (the fused
+// rows of a mixed-format model, e.g. Q4_K Q and K with a Q6_K V): workgroups
+// [0, g1) run the first stack's body, the rest the second's.  Each stack's
+// rows are computed exactly as by its own launch (same lane group G).
+template <class F1, class F2, int G, bool XR>
+__global__ __launch_bounds__(kBlockThreads) void rows2_kernel(RowsParams p1, RowsParams p2, int g1) {
+    if ((int)blockIdx.x < g1)
+        rows_body<F1, G, 2, kModeStore, 1, XR>(p1, (int)blockIdx.x, g1);
+    else
+        rows_body<F2, G, 2, kModeStore, 1, XR>(p2, (int)blockIdx.x - g1, (int)gridDim.x - g1);
 }
 
 }  // namespace qmv

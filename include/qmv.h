@@ -142,6 +142,19 @@ qmv_status qmv_fused_rows(qmv_type t, const void *blocks, int64_t K, const float
                           int32_t nseg, const int64_t *seg_rows, float *const *y_seg,
                           hipStream_t stream);
 
+/* ---- two row stacks of different formats in one launch ------------------
+ * FlareLLM page, section "推理层面的深度优化" (fused QKV) with the BebeLM
+ * page, section "量化格式支持" (Q4_K_M keeps the attention V projection in
+ * Q6_K while Q and K are Q4_K).  Each group (t_i, blocks_i, nseg_i,
+ * seg_rows_i, y_seg_i) is what qmv_fused_rows takes, both with K columns and
+ * the same x; every output equals, bit for bit, what qmv_fused_rows (and so
+ * the single-token call) returns for its group.  t1 != t2, both among Q4_K,
+ * Q5_K and Q6_K (the formats with 64-weight lane steps); others QMV_EINVAL. */
+qmv_status qmv_fused_rows2(qmv_type t1, const void *blocks1, int32_t nseg1,
+                           const int64_t *seg_rows1, float *const *y_seg1, qmv_type t2,
+                           const void *blocks2, int32_t nseg2, const int64_t *seg_rows2,
+                           float *const *y_seg2, int64_t K, const float *x, hipStream_t stream);
+
 /* ---- fused gate/up with the gated product: h[j] = silu(g_j) * u_j --------
  * BebeLM page, section "核心算子" (the gated FFN: h = silu(g) * u feeds the
  * down projection) and FlareLLM page, section "推理层面的深度优化" (gate and

@@ -88,6 +88,14 @@ def test_pointer_and_type_errors():
     assert status_of(q.qmv_fused_rows, "q4_k", A16, 256, A16, [], []) == "QMV_EINVAL"
     assert status_of(q.qmv_gate_up_silu, "q4_k", A16, 8, 256, A16, 0) == "QMV_EINVAL"
     assert status_of(q.qmv_gate_up_silu, 11, A16, 8, 256, A16, A16) == "QMV_EINVAL"
+    # two stacks: distinct formats among Q4_K, Q5_K, Q6_K
+    two = ([4], [A16], A16, [4], [A16], 256, A16)
+    assert status_of(q.qmv_fused_rows2, "q4_k", A16, *two[:2], "q4_k", *two[2:]) == "QMV_EINVAL"
+    assert status_of(q.qmv_fused_rows2, "q8_0", A16, *two[:2], "q6_k", *two[2:]) == "QMV_EINVAL"
+    assert status_of(q.qmv_fused_rows2, "q4_k", A16, [0], [A16], "q6_k", A16, [4], [A16], 256,
+                     A16) == "QMV_ESHAPE"
+    assert status_of(q.qmv_fused_rows2, "q4_k", A16, [4], [A16], "q6_k", A16, [4], [A16], 256,
+                     A16 + 4) == "QMV_EALIGN"
 
 
 def test_alignment_errors():
