@@ -351,6 +351,30 @@ def extras(torch, q, synth, step, progress):
         del Y
     progress("extras: prefill done")
 
+    # a Q4_K_M-style QKV (Q and K in Q4_K, V in Q6_K) as one two-format
+    # launch, and as two launches (fused Q4_K rows, then the Q6_K V), over 32
+    # layers' weights in turn
+    qk_rows = [step.qkv_rows[0], step.qkv_rows[1]]
+    v_rows = step.qkv_rows[2]
+    mixed = [(make("q4_k", sum(qk_rows), Hs, synth.T_W, 20 + l), make("q6_k", v_rows, Hs, synth.T_W, 60 + l))
+             for l in range(len(step.layers))]
+    yqk = [torch.empty(m, device=dev) for m in qk_rows]
+    yv = [torch.empty(v_rows, device=dev)]
+    one = [lambda P=P: q.qmv_fused_rows2("q4_k", P[0], qk_rows, yqk, "q6_k", P[1], [v_rows], yv,
+                                         Hs, step.x_h) for P in mixed]
+    two = []
+    for P in mixed:
+        two.append(lambda P=P: q.qmv_fused_rows("q4_k", P[0], Hs, step.x_h, qk_rows, yqk))
+        two.append(lambda P=P: q.qmv_q6_k(P[1], v_rows, Hs, step.x_h, yv[0]))
+    us1 = graph_time_us(torch, one, reps=5)
+    us2 = graph_time_us(torch, two, reps=5) * 2
+    mbytes = mixed[0][0].numel() + mixed[0][1].numel()
+    r = rec(us1, mbytes + 4 * Hs + 4 * sum(step.qkv_rows), per="call (32 layers in turn)")
+    r["two_launches_us"] = round(us2, 3)
+    out["qkv_q4_k_m_mixed_one_launch"] = r
+    del mixed
+    progress("extras: mixed-format QKV done")
+
     # gate+up with the gated product h = silu(g) * u in the same launch, over
     # the 32 layers' gate+up stacks (2.1 GB, cold by rotation); the plain
     # fused gate+up over the same stacks for comparison
