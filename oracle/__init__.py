@@ -27,16 +27,18 @@ Q5_0 = 6
 Q5_1 = 7
 Q8_0 = 8
 Q8_1 = 9
+Q2_K = 10
+Q3_K = 11
 Q4_K = 12
 Q5_K = 13
 Q6_K = 14
 TYPES = {"q4_0": Q4_0, "q4_1": Q4_1, "q5_0": Q5_0, "q5_1": Q5_1, "q8_0": Q8_0, "q8_1": Q8_1,
-         "q4_k": Q4_K, "q5_k": Q5_K, "q6_k": Q6_K}
+         "q2_k": Q2_K, "q3_k": Q3_K, "q4_k": Q4_K, "q5_k": Q5_K, "q6_k": Q6_K}
 
 BLOCK_WEIGHTS = {Q4_0: 32, Q4_1: 32, Q5_0: 32, Q5_1: 32, Q8_0: 32, Q8_1: 32,
-                 Q4_K: 256, Q5_K: 256, Q6_K: 256}
+                 Q2_K: 256, Q3_K: 256, Q4_K: 256, Q5_K: 256, Q6_K: 256}
 BLOCK_BYTES = {Q4_0: 18, Q4_1: 20, Q5_0: 22, Q5_1: 24, Q8_0: 34, Q8_1: 36,
-               Q4_K: 144, Q5_K: 176, Q6_K: 210}
+               Q2_K: 84, Q3_K: 110, Q4_K: 144, Q5_K: 176, Q6_K: 210}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "qmv_oracle.c")

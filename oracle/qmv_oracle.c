@@ -20,7 +20,8 @@
  *  - More block formats from the pages' lists: FlareLLM page, section
  *    "量化技术的全面支持" names the standard 4- to 8-bit quantisations (Q4_0
  *    through Q8_1) and the K-quants; the BebeLM page, section "局限与未来",
- *    wants Q5_K_M.  Their layouts again follow the standard GGUF reading,
+ *    wants Q5_K_M; the K-quants include Q2_K and Q3_K.  Their layouts again
+ *    follow the standard GGUF reading,
  *    written out at each decoder below.
  *  - The matvec itself is the plain definition y = dequant(W) x, each product
  *    formed exactly in f64 and summed in order k = 0..K-1.
@@ -51,6 +52,8 @@
 #define T_Q5_1 7
 #define T_Q8_0 8
 #define T_Q8_1 9
+#define T_Q2_K 10
+#define T_Q3_K 11
 #define T_Q4_K 12
 #define T_Q5_K 13
 #define T_Q6_K 14
@@ -118,7 +121,7 @@ int oracle_block_weights(int type)
 {
     switch (type) {
     case T_Q4_0: case T_Q4_1: case T_Q5_0: case T_Q5_1: case T_Q8_0: case T_Q8_1: return 32;
-    case T_Q4_K: case T_Q5_K: case T_Q6_K: return 256;
+    case T_Q2_K: case T_Q3_K: case T_Q4_K: case T_Q5_K: case T_Q6_K: return 256;
     default: return 0;
     }
 }
@@ -132,6 +135,8 @@ int oracle_block_bytes(int type)
     case T_Q5_1: return 24;   /* fp16 d, fp16 m, 4 B high bits, 16 B nibbles */
     case T_Q8_0: return 34;   /* fp16 d + 32 int8 */
     case T_Q8_1: return 36;   /* fp16 d, fp16 s + 32 int8 */
+    case T_Q2_K: return 84;   /* 16 B 4-bit scale/min pairs, 64 B 2-bit codes, fp16 d, fp16 dmin */
+    case T_Q3_K: return 110;  /* 32 B high bits, 64 B 2-bit codes, 12 B 6-bit scales, fp16 d */
     case T_Q4_K: return 144;  /* fp16 d, fp16 dmin, 12 B scales, 128 B nibbles */
     case T_Q5_K: return 176;  /* fp16 d, fp16 dmin, 12 B scales, 32 B high bits, 128 B nibbles */
     case T_Q6_K: return 210;  /* 128 B low nibbles, 64 B high pairs, 16 int8 scales, fp16 d */
@@ -309,9 +314,59 @@ static void decode_q5_k(const uint8_t *b, float *w)
     }
 }
 
+/* Q2_K: scale/min bytes S at [0,16) (sub-block j of 16 weights: scale =
+ * low nibble of S[j], min = high nibble), 2-bit codes Q at [16,80), d at
+ * [80,82), dmin at [82,84).  Weight i: half n = i/128, r = i%128, plane
+ * p = r/32, l = r%32; q = bits 2p..2p+1 of Q[32n + l]; sub-block
+ * j = 8n + 2p + l/16 (= i/16).  Weight value (d*sc_j)*q - (dmin*m_j). */
+static void decode_q2_k(const uint8_t *b, float *w)
+{
+    const uint8_t *S = b, *Q = b + 16;
+    float d = oracle_half_to_float(rd16(b + 80));
+    float dmin = oracle_half_to_float(rd16(b + 82));
+    for (int i = 0; i < 256; i++) {
+        int n = i / 128, r = i % 128, p = r / 32, l = r % 32;
+        int q = (Q[32 * n + l] >> (2 * p)) & 3;
+        int j = i / 16;
+        float s = d * (float)(S[j] & 15);
+        float o = dmin * (float)(S[j] >> 4);
+        w[i] = s * (float)q - o;
+    }
+}
+
+/* Q3_K 6-bit scale of sub-block j (0..15) from the 12 packed bytes S: low
+ * four bits from the low (j < 8) or high (j >= 8) nibble of S[j % 8], top
+ * two bits from bits 2*(j/4)..+1 of S[8 + j%4]; the value is that minus 32. */
+static int q3k_scale(const uint8_t *S, int j)
+{
+    int lo = j < 8 ? (S[j] & 15) : (S[j - 8] >> 4);
+    int hi = (S[8 + j % 4] >> (2 * (j / 4))) & 3;
+    return (lo | (hi << 4)) - 32;
+}
+
+/* Q3_K: high bits H at [0,32), 2-bit codes Q at [32,96), packed scales S at
+ * [96,108), d at [108,110).  Weight i: half n = i/128, r = i%128, plane
+ * p = r/32, l = r%32; low = bits 2p..2p+1 of Q[32n + l]; the code is
+ * low - 4 when bit 4n + p of H[l] is clear, low when it is set (so -4..3);
+ * sub-block j = i/16.  Weight value (d*sc_j)*q, exact. */
+static void decode_q3_k(const uint8_t *b, float *w)
+{
+    const uint8_t *H = b, *Q = b + 32, *S = b + 96;
+    float d = oracle_half_to_float(rd16(b + 108));
+    for (int i = 0; i < 256; i++) {
+        int n = i / 128, r = i % 128, p = r / 32, l = r % 32;
+        int low = (Q[32 * n + l] >> (2 * p)) & 3;
+        int q = low - (((H[l] >> (4 * n + p)) & 1) ? 0 : 4);
+        float s = d * (float)q3k_scale(S, i / 16);
+        w[i] = s * (float)q;
+    }
+}
+
 static void decode_block(int type, const uint8_t *b, float *w)
 {
     switch (type) {
+    case T_Q2_K: decode_q2_k(b, w); break;
+    case T_Q3_K: decode_q3_k(b, w); break;
     case T_Q4_0: decode_q4_0(b, w); break;
     case T_Q4_1: decode_q4_1(b, w); break;
     case T_Q5_0: decode_q5_0(b, w); break;
@@ -456,6 +511,115 @@ static void encode_q5_k(const float *w, uint8_t *b)
         Q[32 * c + l] |= (uint8_t)((codes[i] & 15) << (4 * h));
         QH[l] |= (uint8_t)((codes[i] >> 4) << (2 * c + h));
     }
+}
+
+/* Q2_K, per 16-weight sub-block j with lo_j = min(0, min w), hi_j = max w:
+ *   dmin = max_j(-lo_j)/15 -> fp16; m_j = min(15, ceil(-lo_j/dmin16));
+ *   L_j = -dmin16*m_j; s_j = (hi_j - L_j)/3; d = max_j s_j / 15 -> fp16;
+ *   sc_j = min(15, ceil(s_j/d16)); q = clamp(round((w - L_j)/(d16*sc_j)), 0, 3). */
+static void encode_q2_k(const float *w, uint8_t *b)
+{
+    float lo[16], hi[16], L[16], s[16];
+    int sc[16], m[16];
+    float maxneg = 0.0f, maxs = 0.0f;
+    for (int j = 0; j < 16; j++) {
+        float mn = 0.0f, mx = -INFINITY;
+        for (int t = 0; t < 16; t++) {
+            float v = w[16 * j + t];
+            if (v < mn) mn = v;
+            if (v > mx) mx = v;
+        }
+        lo[j] = mn;
+        hi[j] = mx;
+        if (-mn > maxneg) maxneg = -mn;
+    }
+    uint16_t dmin_h = oracle_float_to_half(maxneg / 15.0f);
+    float dmin16 = oracle_half_to_float(dmin_h);
+    for (int j = 0; j < 16; j++) {
+        int mj = 0;
+        if (dmin16 > 0.0f) {
+            float t = ceilf(-lo[j] / dmin16);
+            mj = t > 15.0f ? 15 : (int)t;
+        }
+        m[j] = mj;
+        L[j] = -(dmin16 * (float)mj);
+        s[j] = (hi[j] - L[j]) / 3.0f;
+        if (s[j] > maxs) maxs = s[j];
+    }
+    uint16_t d_h = oracle_float_to_half(maxs / 15.0f);
+    float d16 = oracle_half_to_float(d_h);
+    for (int j = 0; j < 16; j++) {
+        int sj = 0;
+        if (d16 > 0.0f) {
+            float t = ceilf(s[j] / d16);
+            sj = t > 15.0f ? 15 : (int)t;
+        }
+        sc[j] = sj;
+        b[j] = (uint8_t)(sj | (m[j] << 4));
+    }
+    memset(b + 16, 0, 64);
+    for (int i = 0; i < 256; i++) {
+        int j = i / 16, q = 0;
+        if (sc[j] > 0) {
+            float t = roundf((w[i] - L[j]) / (d16 * (float)sc[j]));
+            if (t < 0.0f) t = 0.0f;
+            if (t > 3.0f) t = 3.0f;
+            q = (int)t;
+        }
+        int n = i / 128, r = i % 128, p = r / 32, l = r % 32;
+        b[16 + 32 * n + l] |= (uint8_t)(q << (2 * p));
+    }
+    wr16(b + 80, d_h);
+    wr16(b + 82, dmin_h);
+}
+
+/* Q3_K, per 16-weight sub-block j: v_j = the weight of largest magnitude
+ * (first one on ties), s_j = -v_j/4 so that v_j sits on code -4 (the end
+ * of -4..3 that reaches furthest); d = max_j |s_j| / 31 -> fp16;
+ * sc_j = sign(s_j) * min(31, ceil(|s_j|/d16)) (stored + 32);
+ * q = clamp(round(w/(d16*sc_j)), -4, 3). */
+static void encode_q3_k(const float *w, uint8_t *b)
+{
+    float s[16], maxs = 0.0f;
+    int sc[16];
+    for (int j = 0; j < 16; j++) {
+        float v = 0.0f;
+        for (int t = 0; t < 16; t++)
+            if (fabsf(w[16 * j + t]) > fabsf(v)) v = w[16 * j + t];
+        s[j] = -v / 4.0f;
+        if (fabsf(s[j]) > maxs) maxs = fabsf(s[j]);
+    }
+    uint16_t d_h = oracle_float_to_half(maxs / 31.0f);
+    float d16 = oracle_half_to_float(d_h);
+    memset(b, 0, 110);
+    uint8_t *H = b, *Q = b + 32, *S = b + 96;
+    for (int j = 0; j < 16; j++) {
+        int sj = 0;
+        if (d16 > 0.0f) {
+            float t = ceilf(fabsf(s[j]) / d16);
+            sj = t > 31.0f ? 31 : (int)t;
+            if (s[j] < 0.0f) sj = -sj;
+        }
+        sc[j] = sj;
+        int u = sj + 32;  /* 6-bit stored value, 1..63 */
+        if (j < 8) S[j] |= (uint8_t)(u & 15);
+        else S[j - 8] |= (uint8_t)((u & 15) << 4);
+        S[8 + j % 4] |= (uint8_t)((u >> 4) << (2 * (j / 4)));
+    }
+    for (int i = 0; i < 256; i++) {
+        int j = i / 16, q = 0;
+        if (sc[j] != 0) {
+            float t = roundf(w[i] / (d16 * (float)sc[j]));
+            if (t < -4.0f) t = -4.0f;
+            if (t > 3.0f) t = 3.0f;
+            q = (int)t;
+        }
+        int n = i / 128, r = i % 128, p = r / 32, l = r % 32;
+        int code = q + 4;  /* 0..7: bit 2 set means the code is not lowered by 4 */
+        Q[32 * n + l] |= (uint8_t)((code & 3) << (2 * p));
+        H[l] |= (uint8_t)((code >> 2) << (4 * n + p));
+    }
+    wr16(b + 108, d_h);
 }
 
 /* 32-weight formats.  Symmetric ones (Q4_0, Q5_0, Q8_1): d = max|w| / half
@@ -623,6 +787,8 @@ int oracle_quantize(int type, const float *w, int64_t M, int64_t K, uint8_t *blo
         const float *src = w + t * bw;
         uint8_t *dst = blocks_out + t * bb;
         switch (type) {
+        case T_Q2_K: encode_q2_k(src, dst); break;
+        case T_Q3_K: encode_q3_k(src, dst); break;
         case T_Q4_0: encode_q4_0(src, dst); break;
         case T_Q4_1: encode_q4_1(src, dst); break;
         case T_Q5_0: encode_q5_0(src, dst); break;

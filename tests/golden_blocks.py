@@ -9,9 +9,9 @@ from fractions import Fraction
 import numpy as np
 
 BLOCK_BYTES = {"q4_0": 18, "q4_1": 20, "q5_0": 22, "q5_1": 24, "q8_0": 34, "q8_1": 36,
-               "q4_k": 144, "q5_k": 176, "q6_k": 210}
+               "q2_k": 84, "q3_k": 110, "q4_k": 144, "q5_k": 176, "q6_k": 210}
 BLOCK_WEIGHTS = {"q4_0": 32, "q4_1": 32, "q5_0": 32, "q5_1": 32, "q8_0": 32, "q8_1": 32,
-                 "q4_k": 256, "q5_k": 256, "q6_k": 256}
+                 "q2_k": 256, "q3_k": 256, "q4_k": 256, "q5_k": 256, "q6_k": 256}
 
 PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "handbuilt_blocks.txt")
 

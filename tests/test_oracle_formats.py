@@ -228,3 +228,87 @@ def test_new_formats_reach_the_extreme_codes(t, lo, hi):
     assert np.all(np.abs(wh.max(axis=1) - ws.max(axis=1)) <= span / (hi - lo) * 1.01)
     assert np.all(np.abs(wh.min(axis=1) - ws.min(axis=1)) <= span / (hi - lo) * 1.01 +
                   (np.abs(ws).max(axis=1) / (hi // 2) if t in ("q4_0", "q5_0") else 0))
+
+
+# ---------------------------------------------------------------------------
+# Q2_K and Q3_K (FlareLLM page, section "量化技术的全面支持": the K-quant
+# series runs from Q2K to Q6K)
+# ---------------------------------------------------------------------------
+
+def test_q2_k_round_trip():
+    """Per 16-weight sub-block the codes 0..3 span [L, L + 3 step] with
+    L = -dmin16*m >= lo - dmin16 and step = d16*sc >= s = (hi - L)/3: every
+    weight is within half a step of a level, the step at most s + d16."""
+    w = synth.weights(18, 64, 4096)
+    wh = oracle.dequant("q2_k", oracle.quantize("q2_k", w), 64, 4096)
+    ws = w.reshape(-1, 16, 16).astype(np.float64)
+    whs = wh.reshape(-1, 16, 16).astype(np.float64)
+    lo = np.minimum(0.0, ws.min(axis=2))
+    hi = ws.max(axis=2)
+    dmin16 = (-lo).max(axis=1, keepdims=True) / 15.0 * (1 + EPS16)
+    s = (hi - lo + dmin16) / 3.0
+    d16 = s.max(axis=1, keepdims=True) / 15.0 * (1 + EPS16)
+    step = s + d16
+    slack = (np.abs(lo).max(axis=1, keepdims=True) + hi) * 4 * EPS16
+    bound = (0.5 * step + slack)[:, :, None]
+    err = np.abs(ws - whs)
+    assert np.all(err <= bound), float((err - bound).max())
+    # coarser than Q4_K on the same data (3 levels above the min instead of 15)
+    e4 = np.abs(w - oracle.dequant("q4_k", oracle.quantize("q4_k", w), 64, 4096)).mean()
+    assert err.mean() > 2.0 * e4
+
+
+def test_q3_k_round_trip():
+    """The weight of largest magnitude in each sub-block lands on code -4 of
+    a step d16*sc with |step| >= |v|/4: it is reproduced within half a step
+    and every other weight within one step (the far side of -4..3 stops at
+    3 steps, |w| <= 4 steps)."""
+    w = synth.weights(19, 64, 4096)
+    wh = oracle.dequant("q3_k", oracle.quantize("q3_k", w), 64, 4096)
+    ws = w.reshape(-1, 16, 16).astype(np.float64)
+    whs = wh.reshape(-1, 16, 16).astype(np.float64)
+    amax = np.abs(ws).max(axis=2)
+    d16 = (amax / 4).max(axis=1, keepdims=True) / 31.0 * (1 + EPS16)
+    step = amax / 4 + d16
+    err = np.abs(ws - whs)
+    assert np.all(err <= (step * (1 + 4 * EPS16))[:, :, None])
+    arg = np.abs(ws).argmax(axis=2)
+    e_ext = np.take_along_axis(err, arg[:, :, None], axis=2)[:, :, 0]
+    assert np.all(e_ext <= 0.5 * step * (1 + 4 * EPS16))
+    # the extreme is decoded with its own sign
+    v = np.take_along_axis(ws, arg[:, :, None], axis=2)[:, :, 0]
+    vh = np.take_along_axis(whs, arg[:, :, None], axis=2)[:, :, 0]
+    assert np.all(np.sign(vh) == np.sign(v))
+    # between Q2_K and Q4_K on the same data
+    e2 = np.abs(w - oracle.dequant("q2_k", oracle.quantize("q2_k", w), 64, 4096)).mean()
+    e4 = np.abs(w - oracle.dequant("q4_k", oracle.quantize("q4_k", w), 64, 4096)).mean()
+    assert e4 < err.mean() < e2
+
+
+@pytest.mark.parametrize("t", ["q2_k", "q3_k"])
+def test_low_bit_k_zero_and_constant(t):
+    K = 512
+    z = np.zeros((2, K), dtype=np.float32)
+    assert not oracle.dequant(t, oracle.quantize(t, z), 2, K).any()
+    c = np.full((1, K), 0.0125, dtype=np.float32)
+    wh = oracle.dequant(t, oracle.quantize(t, c), 1, K)
+    assert np.allclose(wh, 0.0125, rtol=0, atol=0.0125 / 20)
+
+
+def test_q3_k_uses_both_scale_signs_and_all_codes():
+    """A sub-block whose extreme is positive gets a negative scale, one whose
+    extreme is negative a positive scale; the decoded sub-block values then
+    take the 8 levels sc*d*(-4..3), read back as integers."""
+    w = synth.weights(20, 8, 1024)
+    b = oracle.quantize("q3_k", w)
+    wh = oracle.dequant("q3_k", b, 8, 1024).reshape(-1, 16).astype(np.float64)
+    ws = w.reshape(-1, 16).astype(np.float64)
+    v = ws[np.arange(ws.shape[0]), np.abs(ws).argmax(axis=1)]
+    assert (v > 0).any() and (v < 0).any()
+    seen = set()
+    for row, vv in zip(wh, v):
+        step = -np.abs(row).max() / 4 * np.sign(vv)   # the extreme decodes to -4*step
+        q = row / step
+        assert np.allclose(q, np.round(q), atol=1e-6)
+        seen.update(np.round(q).astype(int).tolist())
+    assert seen == set(range(-4, 4))

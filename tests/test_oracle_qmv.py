@@ -16,7 +16,7 @@ import oracle
 import synth
 from tests import golden_blocks
 
-TYPES = ["q8_0", "q4_k", "q6_k", "q4_0", "q4_1", "q5_0", "q5_1", "q8_1", "q5_k"]
+TYPES = ["q8_0", "q4_k", "q6_k", "q4_0", "q4_1", "q5_0", "q5_1", "q8_1", "q5_k", "q2_k", "q3_k"]
 
 
 def _matrix(t, M, K, seed):
@@ -51,7 +51,8 @@ def test_all_ones_integer_blocks_give_integer_row_sums():
 
 @pytest.mark.parametrize("t,K", [("q8_0", 64), ("q4_k", 256), ("q4_k", 512), ("q6_k", 256),
                                  ("q6_k", 512), ("q4_0", 64), ("q4_1", 64), ("q5_0", 64),
-                                 ("q5_1", 64), ("q8_1", 64), ("q5_k", 256)])
+                                 ("q5_1", 64), ("q8_1", 64), ("q5_k", 256), ("q2_k", 256),
+                                 ("q3_k", 512)])
 def test_exact_rational_brute_force(t, K):
     M = 4
     b = _matrix(t, M, K, 22)
