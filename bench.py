@@ -399,7 +399,7 @@ def extras(torch, q, synth, step, progress):
     # (and its min to -2^-6) -- the rate does not depend on the values
     M, K = 14336, 4096
     fields = {"q5_k": (0, 2), "q4_0": (0,), "q4_1": (0, 2), "q5_0": (0,), "q5_1": (0, 2),
-              "q8_1": (0, 2)}
+              "q8_1": (0, 2), "q2_k": (80, 82), "q3_k": (108,)}
     xk = synth.normal_device(7, synth.T_X, (K,), 1.0, dev)
     yk = torch.empty(M, device=dev)
     for t, offs in fields.items():

@@ -21,15 +21,17 @@ Q5_0 = 6
 Q5_1 = 7
 Q8_0 = 8
 Q8_1 = 9
+Q2_K = 10
+Q3_K = 11
 Q4_K = 12
 Q5_K = 13
 Q6_K = 14
 TYPES = {"q4_0": Q4_0, "q4_1": Q4_1, "q5_0": Q5_0, "q5_1": Q5_1, "q8_0": Q8_0, "q8_1": Q8_1,
-         "q4_k": Q4_K, "q5_k": Q5_K, "q6_k": Q6_K}
+         "q2_k": Q2_K, "q3_k": Q3_K, "q4_k": Q4_K, "q5_k": Q5_K, "q6_k": Q6_K}
 BLOCK_WEIGHTS = {Q4_0: 32, Q4_1: 32, Q5_0: 32, Q5_1: 32, Q8_0: 32, Q8_1: 32,
-                 Q4_K: 256, Q5_K: 256, Q6_K: 256}
+                 Q2_K: 256, Q3_K: 256, Q4_K: 256, Q5_K: 256, Q6_K: 256}
 BLOCK_BYTES = {Q4_0: 18, Q4_1: 20, Q5_0: 22, Q5_1: 24, Q8_0: 34, Q8_1: 36,
-               Q4_K: 144, Q5_K: 176, Q6_K: 210}
+               Q2_K: 84, Q3_K: 110, Q4_K: 144, Q5_K: 176, Q6_K: 210}
 
 OP_ARGMAX = 1
 OP_MOE = 2
@@ -47,8 +49,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmv.so")
 
 # every symbol include/qmv.h declares
 EXPORTS = ["qmv_q8_0", "qmv_q4_k", "qmv_q6_k", "qmv_q4_0", "qmv_q4_1", "qmv_q5_0", "qmv_q5_1",
-           "qmv_q8_1", "qmv_q5_k", "qmv_fused_rows", "qmv_fused_rows2", "qmv_gate_up_silu",
-           "qmv_short_conv", "qmv_argmax", "moe_qmv_topk", "qmv_gemm_n", "qmv_gemm", "qmv_dequant",
+           "qmv_q8_1", "qmv_q5_k", "qmv_q2_k", "qmv_q3_k", "qmv_fused_rows", "qmv_fused_rows2",
+           "qmv_gate_up_silu", "qmv_short_conv", "qmv_argmax", "moe_qmv_topk", "qmv_gemm_n", "qmv_gemm", "qmv_dequant",
            "qmv_quantize", "qmv_row_bytes", "qmv_workspace_bytes", "qmv_last_hip_error",
            "qmv_status_str", "qmv_probe_stream_read", "qmv_time_next_launch"]
 
@@ -88,6 +90,8 @@ def load():
         "qmv_q5_1": [P, i64, i64, P, P, P],
         "qmv_q8_1": [P, i64, i64, P, P, P],
         "qmv_q5_k": [P, i64, i64, P, P, P],
+        "qmv_q2_k": [P, i64, i64, P, P, P],
+        "qmv_q3_k": [P, i64, i64, P, P, P],
         "qmv_fused_rows": [ci, P, i64, P, i32, P, P, P],
         "qmv_fused_rows2": [ci, P, i32, P, P, ci, P, i32, P, P, i64, P, P],
         "qmv_gate_up_silu": [ci, P, i64, i64, P, P, P],
@@ -200,6 +204,14 @@ def qmv_q8_1(blocks, M, K, x, y, stream=None):
 
 def qmv_q5_k(blocks, M, K, x, y, stream=None):
     _call("qmv_q5_k", _ptr(blocks), M, K, _ptr(x), _ptr(y), _stream(stream))
+
+
+def qmv_q2_k(blocks, M, K, x, y, stream=None):
+    _call("qmv_q2_k", _ptr(blocks), M, K, _ptr(x), _ptr(y), _stream(stream))
+
+
+def qmv_q3_k(blocks, M, K, x, y, stream=None):
+    _call("qmv_q3_k", _ptr(blocks), M, K, _ptr(x), _ptr(y), _stream(stream))
 
 
 def qmv_fused_rows(t, blocks, K, x, seg_rows, y_seg, stream=None):

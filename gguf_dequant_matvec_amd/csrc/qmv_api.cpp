@@ -163,6 +163,14 @@ qmv_status qmv_q5_k(const void *blocks, int64_t M, int64_t K, const float *x, fl
                     hipStream_t stream) {
     return single(kQ5K, blocks, M, K, x, y, stream);
 }
+qmv_status qmv_q2_k(const void *blocks, int64_t M, int64_t K, const float *x, float *y,
+                    hipStream_t stream) {
+    return single(kQ2K, blocks, M, K, x, y, stream);
+}
+qmv_status qmv_q3_k(const void *blocks, int64_t M, int64_t K, const float *x, float *y,
+                    hipStream_t stream) {
+    return single(kQ3K, blocks, M, K, x, y, stream);
+}
 qmv_status qmv_q4_0(const void *blocks, int64_t M, int64_t K, const float *x, float *y,
                     hipStream_t stream) {
     return single(kQ40, blocks, M, K, x, y, stream);

@@ -102,6 +102,47 @@ __global__ void dequant_q5_k(const uint8_t *W, int64_t ngroups, float *out) {
     store16(out + t * 16, v);
 }
 
+// Q2_K: thread t writes sub-block j = t & 15 of block t >> 4; weight
+// 16j + i sits at plane p = (j / 2) & 3 of code byte 32n + 16(j & 1) + i
+// (n = j / 8).  w = (d*sc)*q - dmin*m.
+__global__ void dequant_q2_k(const uint8_t *W, int64_t ngroups, float *out) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= ngroups) return;
+    const uint8_t *blk = W + (t >> 4) * 84;
+    const int j = (int)(t & 15), n = j >> 3, p = (j >> 1) & 3, l0 = 16 * (j & 1);
+    const float s = half_bits_to_float(load2(blk + 80)) * (float)(blk[j] & 15);
+    const float o = half_bits_to_float(load2(blk + 82)) * (float)(blk[j] >> 4);
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        const int q = (blk[16 + 32 * n + l0 + i] >> (2 * p)) & 3;
+        v[i] = s * (float)q - o;
+    }
+    store16(out + t * 16, v);
+}
+
+// Q3_K: as Q2_K for the code position; bit 4n + p of H[16(j & 1) + i] set
+// keeps the code, clear lowers it by 4; 6-bit scale minus 32.  w = (d*sc)*q.
+__global__ void dequant_q3_k(const uint8_t *W, int64_t ngroups, float *out) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= ngroups) return;
+    const uint8_t *blk = W + (t >> 4) * 110;
+    const int j = (int)(t & 15), n = j >> 3, p = (j >> 1) & 3, l0 = 16 * (j & 1);
+    const uint8_t *S = blk + 96;
+    const int lo4 = (S[j & 7] >> (4 * (j >> 3))) & 15;
+    const int top = (S[8 + (j & 3)] >> (2 * (j >> 2))) & 3;
+    const float s = half_bits_to_float(load2(blk + 108)) * (float)((lo4 | (top << 4)) - 32);
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        const int l = l0 + i;
+        const int low = (blk[32 + 32 * n + l] >> (2 * p)) & 3;
+        const int q = low - (((blk[l] >> (4 * n + p)) & 1) ? 0 : 4);
+        v[i] = s * (float)q;
+    }
+    store16(out + t * 16, v);
+}
+
 // 32-weight nibble formats: thread t writes half h = t & 1 of block t >> 1,
 // i.e. the low (h = 0) or high (h = 1) nibbles of the 16 code bytes.
 // w = d * (q - kOff), or d * q + m (kMin; the product is exact, so the one
@@ -329,6 +370,8 @@ hipError_t launch_dequant(int type, const uint8_t *W, int64_t M, int64_t K, floa
     case kQ4K: hipLaunchKernelGGL(dequant_q4_k, dim3(grid), dim3(256), 0, s, W, ngroups, out); break;
     case kQ6K: hipLaunchKernelGGL(dequant_q6_k, dim3(grid), dim3(256), 0, s, W, ngroups, out); break;
     case kQ5K: hipLaunchKernelGGL(dequant_q5_k, dim3(grid), dim3(256), 0, s, W, ngroups, out); break;
+    case kQ2K: hipLaunchKernelGGL(dequant_q2_k, dim3(grid), dim3(256), 0, s, W, ngroups, out); break;
+    case kQ3K: hipLaunchKernelGGL(dequant_q3_k, dim3(grid), dim3(256), 0, s, W, ngroups, out); break;
     case kQ40:
         hipLaunchKernelGGL((dequant_nib32<18, false, 0, 2, 8>), dim3(grid), dim3(256), 0, s, W, ngroups, out);
         break;

@@ -382,6 +382,151 @@ struct Q5K {
 };
 
 // ---------------------------------------------------------------------------
+// Q2_K and Q3_K (FlareLLM page, section "量化技术的全面支持": K-quants from
+// Q2K up).  Both store 256 weights as 2-bit codes Q[64], byte 32n + l
+// holding weight 128n + 32p + l in bits 2p..2p+1, with 16-weight sub-blocks
+// j = i / 16.  The unit is the Q6_K one: half n = (u >> 1) & 1, h = u & 1,
+// weights 128n + 32p + 16h + t for p, t in 0..3 x 0..15, i.e. the 16 code
+// bytes Q[32n + 16h ..) and sub-blocks 8n + 2p + h.  Plane p of a code dword
+// is masked in place, so its bytes are a power-of-two multiple of the code;
+// that power is undone with the sub-block scale.
+// ---------------------------------------------------------------------------
+struct LowBitK {
+    static constexpr int kBlockWeights = 256;
+    static constexpr int kUnitWeights = 64;
+    static constexpr int kSumGroup = 16;
+    static constexpr int kPadEvery = 128;
+    __device__ static __forceinline__ uint32_t half_of(int u) { return (u >> 1) & 1; }
+    __device__ static __forceinline__ void load_x(const float *xs, int u, float *xv) {
+        Q6K::load_x(xs, u, xv);
+    }
+    // A[p] += sum over the 16 weights of plane p of (2^e c) 2^-24 x, where
+    // code bytes c come from `plane(i, p)` (dword i = weights t = 4i..4i+3).
+    template <class Plane>
+    __device__ static __forceinline__ void planes(const float *xv, Plane plane, float *A) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+#pragma unroll
+            for (int p = 0; p < 4; p++) {
+                const uint32_t c = plane(i, p);
+                const f16x2_t c01 = as_f16x2(bytes01_to_halves(c));
+                const f16x2_t c23 = as_f16x2(bytes23_to_halves(c));
+                A[p] = fmaf((float)c01.x, xv[16 * p + 4 * i + 0], A[p]);
+                A[p] = fmaf((float)c01.y, xv[16 * p + 4 * i + 1], A[p]);
+                A[p] = fmaf((float)c23.x, xv[16 * p + 4 * i + 2], A[p]);
+                A[p] = fmaf((float)c23.y, xv[16 * p + 4 * i + 3], A[p]);
+            }
+        }
+    }
+};
+
+// Q2_K, 84 B: S[16] (scale in the low, min in the high nibble of sub-block
+// j's byte) | Q[64] | fp16 d | fp16 dmin.  w = d*sc_j*q - dmin*m_j.
+struct Q2K : LowBitK {
+    static constexpr int kBlockBytes = 84;
+    struct Regs {
+        uint4 q;
+        uint2 sm;     // S[8n .. 8n + 8)
+        uint32_t dd;  // d | dmin << 16
+    };
+    __device__ static __forceinline__ uint32_t unit_offset(int u) {
+        return (uint32_t)(u >> 2) * kBlockBytes;
+    }
+    __device__ static __forceinline__ Regs load(const BufSrc &src, uint32_t off, int u) {
+        const uint32_t n = half_of(u), h = u & 1;
+        Regs r;
+        r.q = src.ld16(off + 16 + 32 * n + 16 * h);
+        r.sm = src.ld8(off + 8 * n);
+        r.dd = src.ld4(off + 80);
+        return r;
+    }
+    __device__ static __forceinline__ void dot(const Regs &r, const float *xv, const float *sums,
+                                               int u, float &acc) {
+        const uint32_t qw[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
+        float A[4] = {0.f, 0.f, 0.f, 0.f};
+        planes(xv, [&](int i, int p) { return qw[i] & (0x03030303u << (2 * p)); }, A);
+        // sub-block of plane p is 8n + 2p + h: byte 2p + h of S[8n ..)
+        const int h = u & 1;
+        const int sbase = 16 * (u >> 2) + 8 * (int)half_of(u) + h;
+        const uint32_t w0 = r.sm.x >> (8 * h), w1 = r.sm.y >> (8 * h);
+        const uint32_t b[4] = {w0, w0 >> 16, w1, w1 >> 16};
+        float t = 0.f, mm = 0.f;
+#pragma unroll
+        for (int p = 0; p < 4; p++) {
+            // A[p] 2^24 / 4^p is the code sum exactly (power-of-two scaling)
+            const float sc = (float)(b[p] & 15u) * (kTwo24 / (float)(1 << (2 * p)));
+            t = fmaf(sc, A[p], t);
+            mm = fmaf((float)((b[p] >> 4) & 15u), sums[sbase + 2 * p], mm);
+        }
+        acc = fmaf(half_bits_to_float(r.dd), t, acc);
+        acc = fmaf(-half_bits_to_float(r.dd >> 16), mm, acc);
+    }
+};
+
+// Q3_K, 110 B: H[32] | Q[64] | S[12] (6-bit scales, stored + 32) | fp16 d.
+// Weight 128n + 32p + l: low bits from Q, bit 4n + p of H[l] set keeps the
+// code, clear lowers it by 4.  With c = low | hbit << 2 (0..7) the code is
+// c - 4; the -4 is applied through the sub-block activation sums.
+// Scale of sub-block j: low four bits from nibble j / 8 of S[j % 8], top two
+// from bits 2(j / 4).. of S[8 + j % 4]; for this unit's j = 8n + 2p + h that
+// is nibble n of S[2p + h] and bits 2(2n + p / 2) of S[8 + 2(p & 1) + h].
+struct Q3K : LowBitK {
+    static constexpr int kBlockBytes = 110;
+    struct Regs {
+        uint4 q, hb;
+        uint2 slo;     // S[0 .. 8)
+        uint32_t shi;  // S[8 .. 12)
+        uint32_t d;
+    };
+    __device__ static __forceinline__ uint32_t unit_offset(int u) {
+        return (uint32_t)(u >> 2) * kBlockBytes;
+    }
+    __device__ static __forceinline__ Regs load(const BufSrc &src, uint32_t off, int u) {
+        const uint32_t n = half_of(u), h = u & 1;
+        Regs r;
+        r.q = src.ld16(off + 32 + 32 * n + 16 * h);
+        r.hb = src.ld16(off + 16 * h);
+        r.slo = src.ld8(off + 96);
+        r.shi = src.ld4(off + 104);
+        r.d = src.ld2(off + 108);
+        return r;
+    }
+    __device__ static __forceinline__ void dot(const Regs &r, const float *xv, const float *sums,
+                                               int u, float &acc) {
+        const int n = (int)half_of(u), h = u & 1;
+        const uint32_t qw[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
+        // high bits of this half moved to bits 0..3 of each byte
+        const uint32_t hw[4] = {r.hb.x >> (4 * n), r.hb.y >> (4 * n), r.hb.z >> (4 * n),
+                                r.hb.w >> (4 * n)};
+        // Plane p's 3-bit code is kept at bits e..e+2 of its byte, e = 2p for
+        // p < 3; plane 3 would reach bit 8, so its low bits are shifted down
+        // to bits 4..5 (e = 4).
+        float A[4] = {0.f, 0.f, 0.f, 0.f};
+        planes(xv, [&](int i, int p) {
+            if (p < 3)
+                return (qw[i] & (0x03030303u << (2 * p))) |
+                       ((hw[i] & (0x01010101u << p)) << (p + 2));
+            return ((qw[i] >> 2) & 0x30303030u) | ((hw[i] & 0x08080808u) << 3);
+        }, A);
+        const int sbase = 16 * (u >> 2) + 8 * n + h;
+        const uint32_t lo0 = r.slo.x >> (8 * h + 4 * n), lo1 = r.slo.y >> (8 * h + 4 * n);
+        const uint32_t lo[4] = {lo0, lo0 >> 16, lo1, lo1 >> 16};
+        const uint32_t hi = r.shi >> (8 * h);
+        float t = 0.f;
+#pragma unroll
+        for (int p = 0; p < 4; p++) {
+            const uint32_t top = (hi >> (16 * (p & 1) + 2 * (2 * n + (p >> 1)))) & 3u;
+            const int sc = (int)((lo[p] & 15u) | (top << 4)) - 32;
+            // sum (c - 4) x over the sub-block, exact power-of-two scalings
+            const float cx = fmaf(A[p], kTwo24 / (float)(1 << (p < 3 ? 2 * p : 4)),
+                                  -4.f * sums[sbase + 2 * p]);
+            t = fmaf((float)sc, cx, t);
+        }
+        acc = fmaf(half_bits_to_float(r.d), t, acc);
+    }
+};
+
+// ---------------------------------------------------------------------------
 // 32-weight nibble formats, one block per unit (FlareLLM page, section
 // "量化技术的全面支持": the standard 4- and 5-bit quantisations).  Code byte l
 // (0..15) holds weight l in its low nibble and weight l + 16 in its high

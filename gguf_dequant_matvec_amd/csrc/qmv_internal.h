@@ -10,14 +10,17 @@ namespace qmv {
 
 struct SegTable;
 
-enum { kQ40 = 2, kQ41 = 3, kQ50 = 6, kQ51 = 7, kQ80 = 8, kQ81 = 9, kQ4K = 12, kQ5K = 13, kQ6K = 14 };
+enum {
+    kQ40 = 2, kQ41 = 3, kQ50 = 6, kQ51 = 7, kQ80 = 8, kQ81 = 9,
+    kQ2K = 10, kQ3K = 11, kQ4K = 12, kQ5K = 13, kQ6K = 14
+};
 
 constexpr int kMaxGrid = 2048;  // largest persistent grid (argmax partial slots)
 
 inline int block_weights_of(int type) {
     switch (type) {
     case kQ40: case kQ41: case kQ50: case kQ51: case kQ80: case kQ81: return 32;
-    case kQ4K: case kQ5K: case kQ6K: return 256;
+    case kQ2K: case kQ3K: case kQ4K: case kQ5K: case kQ6K: return 256;
     default: return 0;
     }
 }
@@ -29,6 +32,8 @@ inline int block_bytes_of(int type) {
     case kQ51: return 24;
     case kQ80: return 34;
     case kQ81: return 36;
+    case kQ2K: return 84;
+    case kQ3K: return 110;
     case kQ4K: return 144;
     case kQ5K: return 176;
     case kQ6K: return 210;

@@ -58,7 +58,8 @@ extern "C" {
 /* Block formats, numbered with their GGUF tensor type ids.  Q8_0, Q4_K and
  * Q6_K are the formats of the pages' models; Q4_0, Q4_1, Q5_0, Q5_1, Q8_1
  * (FlareLLM page, section "量化技术的全面支持": the standard 4- to 8-bit
- * quantisations) and Q5_K (BebeLM page, section "局限与未来": Q5_K_M) are
+ * quantisations), Q2_K and Q3_K (same section: K-quants from Q2K up) and
+ * Q5_K (BebeLM page, section "局限与未来": Q5_K_M) are
  * served by the single-token, fused-row, gated gate/up, argmax, MoE and
  * dequantisation calls; qmv_gemm_n and qmv_quantize take the first three
  * only.  Blocks (standard GGUF layouts, little-endian):
@@ -69,6 +70,14 @@ extern "C" {
  *   Q8_1 36 B: fp16 d, fp16 s (unused for weights), 32 int8; w = d * q
  *   Q5_K 176 B: Q4_K's d, dmin and 12 scale bytes, 32 bytes of fifth bits,
  *     128 nibble bytes; w = d * sc_j * q - dmin * m_j, q in 0..31
+ *   Q2_K 84 B: 16 bytes (scale low / min high nibble of each 16-weight
+ *     sub-block j), 64 bytes of 2-bit codes, fp16 d, fp16 dmin;
+ *     w = d * sc_j * q - dmin * m_j, q in 0..3
+ *   Q3_K 110 B: 32 bytes of high bits, 64 bytes of 2-bit low codes, 12 bytes
+ *     of 6-bit scales (stored + 32), fp16 d; w = d * sc_j * q, q in -4..3
+ *     (a clear high bit lowers the code by 4)
+ *   (K-quant 2-bit codes: byte 32n + l holds weight 128n + 32p + l in bits
+ *   2p..2p+1; Q3_K's high bit of that weight is bit 4n + p of byte l.)
  * (32-weight formats: code byte l holds weight l in its low nibble and l + 16
  * in its high nibble; bit i of the u32 is the fifth bit of weight i.) */
 typedef enum {
@@ -78,6 +87,8 @@ typedef enum {
     QMV_Q5_1 = 7,
     QMV_Q8_0 = 8,
     QMV_Q8_1 = 9,
+    QMV_Q2_K = 10,
+    QMV_Q3_K = 11,
     QMV_Q4_K = 12,
     QMV_Q5_K = 13,
     QMV_Q6_K = 14
@@ -127,6 +138,10 @@ qmv_status qmv_q5_1(const void *blocks, int64_t M, int64_t K, const float *x, fl
 qmv_status qmv_q8_1(const void *blocks, int64_t M, int64_t K, const float *x, float *y,
                     hipStream_t stream);
 qmv_status qmv_q5_k(const void *blocks, int64_t M, int64_t K, const float *x, float *y,
+                    hipStream_t stream);
+qmv_status qmv_q2_k(const void *blocks, int64_t M, int64_t K, const float *x, float *y,
+                    hipStream_t stream);
+qmv_status qmv_q3_k(const void *blocks, int64_t M, int64_t K, const float *x, float *y,
                     hipStream_t stream);
 
 /* ---- fused row stack: one launch over nseg row segments sharing x --------

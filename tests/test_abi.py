@@ -61,6 +61,8 @@ def test_shape_errors():
     assert status_of(q.qmv_q8_0, A16, 4, 48, A16, A16) == "QMV_ESHAPE"
     assert status_of(q.qmv_q8_0, A16, 4, q.MAX_K + 32, A16, A16) == "QMV_ESHAPE"
     assert status_of(q.qmv_q5_k, A16, 4, 128, A16, A16) == "QMV_ESHAPE"
+    assert status_of(q.qmv_q2_k, A16, 4, 128, A16, A16) == "QMV_ESHAPE"
+    assert status_of(q.qmv_q3_k, A16, 4, 384, A16, A16) == "QMV_ESHAPE"
     assert status_of(q.qmv_q4_0, A16, 4, 48, A16, A16) == "QMV_ESHAPE"
     assert status_of(q.qmv_q5_1, A16, 0, 64, A16, A16) == "QMV_ESHAPE"
     assert status_of(q.qmv_gemm_n, "q4_k", A16, 4, 256, 17, A16, A16, A16, 1 << 20) == "QMV_ESHAPE"
@@ -75,8 +77,9 @@ def test_shape_errors():
 def test_pointer_and_type_errors():
     assert status_of(q.qmv_q4_k, 0, 4, 256, A16, A16) == "QMV_EINVAL"
     assert status_of(q.qmv_q4_k, A16, 4, 256, 0, A16) == "QMV_EINVAL"
-    assert status_of(q.qmv_dequant, 11, A16, 4, 256, A16) == "QMV_EINVAL"   # Q3_K: not served
+    assert status_of(q.qmv_dequant, 5, A16, 4, 256, A16) == "QMV_EINVAL"   # no such GGUF type
     assert status_of(q.qmv_dequant, 4, A16, 4, 256, A16) == "QMV_EINVAL"
+    assert status_of(q.qmv_dequant, 15, A16, 4, 256, A16) == "QMV_EINVAL"  # Q8_K: not served
     # the verify product and the device quantiser take Q8_0, Q4_K and Q6_K only
     assert status_of(q.qmv_gemm_n, "q5_k", A16, 4, 256, 8, A16, A16, A16, 1 << 20) == "QMV_EINVAL"
     assert status_of(q.qmv_quantize, "q4_0", A16, 4, 256, A16) == "QMV_EINVAL"
@@ -87,7 +90,7 @@ def test_pointer_and_type_errors():
     assert status_of(q.qmv_fused_rows, "q4_k", A16, 256, A16, [1] * 9, [A16] * 9) == "QMV_EINVAL"
     assert status_of(q.qmv_fused_rows, "q4_k", A16, 256, A16, [], []) == "QMV_EINVAL"
     assert status_of(q.qmv_gate_up_silu, "q4_k", A16, 8, 256, A16, 0) == "QMV_EINVAL"
-    assert status_of(q.qmv_gate_up_silu, 11, A16, 8, 256, A16, A16) == "QMV_EINVAL"
+    assert status_of(q.qmv_gate_up_silu, 5, A16, 8, 256, A16, A16) == "QMV_EINVAL"
     # two stacks: distinct formats among Q4_K, Q5_K, Q6_K
     two = ([4], [A16], A16, [4], [A16], 256, A16)
     assert status_of(q.qmv_fused_rows2, "q4_k", A16, *two[:2], "q4_k", *two[2:]) == "QMV_EINVAL"

@@ -37,6 +37,9 @@ SHAPES = [
     ("q5_0", 300, 4096), ("q5_0", 37, 224),
     ("q5_1", 129, 2048), ("q5_1", 1, 32),
     ("q8_1", 1536, 576), ("q8_1", 33, 224),
+    # 2- and 3-bit K-quants
+    ("q2_k", 1, 256), ("q2_k", 77, 2048), ("q2_k", 1000, 4096), ("q2_k", 97, 14336),
+    ("q3_k", 1, 256), ("q3_k", 50, 768), ("q3_k", 1000, 4096), ("q3_k", 97, 14336),
 ]
 
 
@@ -77,7 +80,8 @@ def test_qmv_parity(t, M, K):
 @pytest.mark.parametrize("t,M,K", [("q4_k", 40, 4096), ("q6_k", 40, 1536), ("q8_0", 40, 576),
                                    ("q8_0", 9, 224), ("q4_k", 33, 14336), ("q5_k", 40, 4096),
                                    ("q4_0", 40, 576), ("q4_1", 40, 576), ("q5_0", 40, 576),
-                                   ("q5_1", 40, 576), ("q8_1", 40, 576)])
+                                   ("q5_1", 40, 576), ("q8_1", 40, 576), ("q2_k", 40, 4096),
+                                   ("q3_k", 40, 1536)])
 def test_qmv_one_hot_is_exact(t, M, K):
     b, _ = _case(t, M, K, 300)
     W = oracle.dequant(t, b, M, K)
@@ -126,6 +130,8 @@ def test_x_extremes():
     ("q5_k", (512, 128, 128), 2048),
     ("q4_0", (64, 16, 16), 4096),
     ("q5_1", (33, 7), 224),
+    ("q3_k", (512, 128, 128), 2048),
+    ("q2_k", (300, 5), 4096),
 ])
 def test_fused_rows(t, segs, K):
     M = sum(segs)
@@ -157,7 +163,7 @@ def _argmax_gpu(t, bd, M, K, xd):
 @pytest.mark.parametrize("t,M,K", [("q6_k", 5000, 4096), ("q4_k", 777, 2048), ("q8_0", 1536, 576),
                                    ("q6_k", 1, 256), ("q6_k", 3001, 1536), ("q4_k", 300, 14336),
                                    ("q8_0", 70, 8192), ("q5_k", 3000, 4096), ("q4_0", 2000, 2048),
-                                   ("q8_1", 900, 576)])
+                                   ("q8_1", 900, 576), ("q2_k", 2000, 2048), ("q3_k", 1500, 4096)])
 def test_argmax(t, M, K):
     b, x = _case(t, M, K, 500 + M)
     y_ref, a_ref = oracle.qmv(t, b, M, K, x)

@@ -169,6 +169,7 @@ def test_moe_k1_and_tie_to_lower_expert():
     (8, 512, 256, 4, "q5_k", "q4_0"),     # further formats: Q5_K gate/up, Q4_0 down
     (6, 256, 128, 2, "q5_0", "q5_1"),
     (4, 256, 256, 2, "q4_1", "q8_1"),
+    (8, 512, 256, 4, "q3_k", "q2_k"),     # 3- and 2-bit K-quants
 ])
 def test_moe_small_shapes(E, H, I, k, gu_t, dn_t):
     ex = experts((50 + E, E, H, I, gu_t, dn_t))

@@ -70,6 +70,8 @@ SHAPES = [
     ("q5_k", 200, 2048),
     ("q4_0", 96, 4096),
     ("q5_1", 45, 224),
+    ("q3_k", 150, 2048),
+    ("q2_k", 64, 4096),
 ]
 
 
