@@ -337,8 +337,10 @@ def extras(torch, q, synth, step, progress):
         Xh = synth.normal_device(11, synth.T_X, (nn, Hs), 1.0, dev)
         Xi = synth.normal_device(11, synth.T_XN, (nn, Is), 1.0, dev)
         Y = torch.empty(nn * sum(step.gu_rows), device=dev)
+        wsb = max(q.qmv_workspace_bytes(q.OP_GEMM, M_, K_, nn) for _, M_, K_ in mats)
+        wsp = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
         calls = [lambda m=m, M_=M_, K_=K_: q.qmv_gemm("q4_k", m, M_, K_, nn,
-                                                     Xh if K_ == Hs else Xi, Y)
+                                                     Xh if K_ == Hs else Xi, Y, wsp)
                  for m, M_, K_ in mats]
         us = graph_time_us(torch, calls, reps=1) * len(calls)   # per 32-layer pass
         io = sum(4 * nn * (K_ + M_) for _, M_, K_ in mats)
@@ -348,7 +350,7 @@ def extras(torch, q, synth, step, progress):
         r["pct_of_bf16_mfma_peak"] = round(100 * flops / (us * 1e-6) / 2.5e15, 1)
         r["tok_per_s"] = round(nn / (us * 1e-6), 1)
         out[f"prefill_n{nn}_32_layers_q4_k"] = r
-        del Y
+        del Y, wsp
     progress("extras: prefill done")
 
     # a Q4_K_M-style QKV (Q and K in Q4_K, V in Q6_K) as one two-format

@@ -37,6 +37,7 @@ OP_ARGMAX = 1
 OP_MOE = 2
 OP_GEMM_N = 3
 OP_SHORT_CONV = 4
+OP_GEMM = 5
 MAX_K = 32768
 MAX_SEGMENTS = 8
 MAX_N = 16
@@ -99,7 +100,7 @@ def load():
         "qmv_argmax": [ci, P, i64, i64, P, P, P, P, sz, P],
         "moe_qmv_topk": [P, i64, P, P, i32, i32, ci, P, ci, P, i64, P, P, P, P, sz, P],
         "qmv_gemm_n": [ci, P, i64, i64, i32, P, P, P, sz, P],
-        "qmv_gemm": [ci, P, i64, i64, i64, P, P, P],
+        "qmv_gemm": [ci, P, i64, i64, i64, P, P, P, sz, P],
         "qmv_dequant": [ci, P, i64, i64, P, P],
         "qmv_quantize": [ci, P, i64, i64, P, P],
         "qmv_probe_stream_read": [P, sz, P, P],
@@ -271,8 +272,11 @@ def qmv_gemm_n(t, blocks, M, K, n, X, Y, workspace=None, ws_bytes=None, stream=N
           ws_bytes, _stream(stream))
 
 
-def qmv_gemm(t, blocks, M, K, n, X, Y, stream=None):
-    _call("qmv_gemm", _type(t), _ptr(blocks), M, K, n, _ptr(X), _ptr(Y), _stream(stream))
+def qmv_gemm(t, blocks, M, K, n, X, Y, workspace=None, ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _call("qmv_gemm", _type(t), _ptr(blocks), M, K, n, _ptr(X), _ptr(Y), _ptr(workspace),
+          ws_bytes, _stream(stream))
 
 
 def qmv_dequant(t, blocks, M, K, w_out, stream=None):

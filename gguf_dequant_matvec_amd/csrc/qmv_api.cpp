@@ -116,6 +116,10 @@ size_t qmv_workspace_bytes(qmv_op op, int64_t a, int64_t b, int32_t c, int32_t d
         if (a < 1 || b < 1 || c < 1 || c > QMV_MAX_N) return 0;
         return gemm_n_workspace(a, b, c);
     }
+    if (op == QMV_OP_GEMM) {
+        if (a < 1 || b < 1 || c < 1 || c > QMV_MAX_PREFILL_N) return 0;
+        return gemm_workspace(a, b, c);
+    }
     return 0;
 }
 
@@ -339,7 +343,7 @@ qmv_status qmv_gemm_n(qmv_type t, const void *blocks, int64_t M, int64_t K, int3
 }
 
 qmv_status qmv_gemm(qmv_type t, const void *blocks, int64_t M, int64_t K, int64_t n, const float *X,
-                    float *Y, hipStream_t stream) {
+                    float *Y, void *workspace, size_t ws_bytes, hipStream_t stream) {
     if (!core_type(t)) return QMV_EINVAL;
     qmv_status st = check_matrix(t, blocks, M, K);
     if (st != QMV_OK) return st;
@@ -348,7 +352,12 @@ qmv_status qmv_gemm(qmv_type t, const void *blocks, int64_t M, int64_t K, int64_
     if ((uint64_t)n * (uint64_t)K * 4u > 0xFFFFFFFFull) return QMV_ESHAPE;
     if (!X || !Y) return QMV_EINVAL;
     if (!aligned(X, 16) || !aligned(Y, 4)) return QMV_EALIGN;
-    return from_hip(launch_gemm(t, (const uint8_t *)blocks, M, K, n, X, Y, stream));
+    const size_t need = gemm_workspace(M, K, n);
+    if (need > 0) {
+        if (!workspace || ws_bytes < need) return QMV_EWORKSPACE;
+        if (!aligned(workspace, 16)) return QMV_EALIGN;
+    }
+    return from_hip(launch_gemm(t, (const uint8_t *)blocks, M, K, n, X, Y, workspace, stream));
 }
 
 qmv_status qmv_dequant(qmv_type t, const void *blocks, int64_t M, int64_t K, float *w_out,

@@ -478,14 +478,16 @@ hipError_t launch_typed(const GemmParams &p, hipStream_t s) {
 // ---------------------------------------------------------------------------
 // Prefill-size product (n up to thousands of tokens; BebeLM page, section
 // "性能表现": prompts are processed in batches).  With many tokens there is
-// parallelism across token blocks, so K is not split: a workgroup owns 128
-// rows and a block of 16 * TT tokens and walks every 256-weight window of
-// the rows.  Per window it stages X for its tokens (bf16 hi/lo operand
+// parallelism across token blocks, so K is split only when rows and token
+// blocks alone give too few workgroups: a workgroup owns 128 rows, a block
+// of 16 * TT tokens and a slice of consecutive 256-weight windows (all of K
+// unless split).  Per window it stages X for its tokens (bf16 hi/lo operand
 // fragments and per-sub-block sums) in LDS, then multiplies while the next
 // window's weights are in flight in a second register set.  Each weight sub-block's codes and scales are formed
 // once and used by the TT token tiles.  Two workgroups share a compute unit,
 // so one's X staging overlaps the other's multiply.  Every output is one fixed-order sum
-// over the windows, so results are deterministic and need no workspace.
+// over the windows, or over the slices' partial sums added in slice order by
+// a second kernel, so results are deterministic.
 // Workgroups are mapped so that those sharing rows run on the same XCD
 // (workgroups go to XCDs round-robin): their weights come from that XCD's L2.
 // ---------------------------------------------------------------------------
@@ -576,7 +578,7 @@ struct XStagePf {
 
 template <class F, int TT>
 __global__ __launch_bounds__(kThreads, 2) void gemm_pf_kernel(GemmParams p, int token_blocks,
-                                                            int row_groups_pad) {
+                                                            int wps) {
     using L = PfLayout<F, TT>;
     constexpr int kPfTiles = TT, kPfTokens = 16 * TT;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -584,17 +586,21 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_pf_kernel(GemmParams p, int 
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int r = lane & 15, q = lane >> 4;
     // XCD-aware order: workgroups b and b + 8 share an XCD; consecutive
-    // workgroups of one XCD take the token blocks of one row group
+    // workgroups of one XCD take the (token block, K slice) pairs of one row
+    // group
     const int b = (int)blockIdx.x;
     const int local = b / kXcds;
-    const int tb = local % token_blocks;
-    const int rg = (b % kXcds) + kXcds * (local / token_blocks);
+    const int cols = token_blocks * p.slices;
+    const int cb = local % cols;
+    const int tb = cb % token_blocks, slice = cb / token_blocks;
+    const int rg = (b % kXcds) + kXcds * (local / cols);
     if (rg * kRowsPerWG >= p.M) return;  // padding of the row groups
-    (void)row_groups_pad;
     const int row0 = __builtin_amdgcn_readfirstlane(rg * kRowsPerWG + wave * 16);
     const int tok0 = tb * kPfTokens;
     const int nblocks = p.K / 32;
-    const int wtotal = (p.K + kWin - 1) / kWin;
+    // this workgroup's windows [w0, wtotal)
+    const int w0 = slice * wps;
+    const int wtotal = min((p.K + kWin - 1) / kWin, w0 + wps);
 
     const int rows_left = p.M - row0 > 0 ? p.M - row0 : 0;
     const BufSrc src(p.W + (int64_t)row0 * p.row_bytes,
@@ -622,7 +628,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_pf_kernel(GemmParams p, int 
 #pragma unroll
     for (int tt = 0; tt < kPfTiles; tt++) acc[tt] = {0.f, 0.f, 0.f, 0.f};
 
-    typename F::Regs wcur = wload(0);
+    typename F::Regs wcur = wload(w0);
 
     auto multiply = [&](const typename F::Regs &w, const uint8_t *base, int wi) {
         const __bf16 *xhi = reinterpret_cast<const __bf16 *>(base);
@@ -662,7 +668,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_pf_kernel(GemmParams p, int 
     // load latency is hidden by the other workgroup on the compute unit (two
     // fit: one LDS buffer each).  The register sets trade places by a copy,
     // so the loop body exists once.
-    for (int wi = 0; wi < wtotal; wi++) {
+    for (int wi = w0; wi < wtotal; wi++) {
         const int wn = wi + 1 < wtotal ? wi + 1 : wi;
         {
             XStagePf<F, TT> xs;
@@ -677,44 +683,79 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_pf_kernel(GemmParams p, int 
     }
 
     const int row = row0 + r;
+    float *out = p.slices == 1 ? p.Y : p.partial + (int64_t)slice * p.n * p.M;
     if (row < p.M) {
 #pragma unroll
         for (int tt = 0; tt < kPfTiles; tt++)
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 const int t = tok0 + tt * 16 + 4 * q + i;
-                if (t < p.n) p.Y[(int64_t)t * p.M + row] = acc[tt][i];
+                if (t < p.n) out[(int64_t)t * p.M + row] = acc[tt][i];
             }
     }
 }
 
 template <class F, int TT>
-hipError_t launch_pf_tt(GemmParams p, int rg_pad, hipStream_t s) {
+hipError_t launch_pf_tt(GemmParams p, const PfPlan &plan, hipStream_t s) {
     const size_t lds = (size_t)PfLayout<F, TT>::kBytes;
     hipError_t e = ensure_lds((const void *)gemm_pf_kernel<F, TT>, lds);
     if (e != hipSuccess) return e;
-    const int token_blocks = (p.n + 16 * TT - 1) / (16 * TT);
-    const int64_t grid = (int64_t)rg_pad * token_blocks;
+    p.slices = plan.slices;
+    const int64_t grid = (int64_t)plan.rg_pad * plan.token_blocks * plan.slices;
     if (grid > 0x7FFFFFFFll) return hipErrorInvalidValue;
-    return launch_main(gemm_pf_kernel<F, TT>, dim3((unsigned)grid), dim3(kThreads), lds, s, p,
-                       token_blocks, rg_pad);
+    e = launch_main(gemm_pf_kernel<F, TT>, dim3((unsigned)grid), dim3(kThreads), lds, s, p,
+                    plan.token_blocks, plan.wps);
+    if (e != hipSuccess || plan.slices == 1) return e;
+    const int64_t nm = (int64_t)p.n * p.M;
+    hipLaunchKernelGGL(gemm_n_reduce, dim3((unsigned)((nm + 255) / 256)), dim3(256), 0, s,
+                       p.partial, p.slices, nm, p.Y);
+    return hipGetLastError();
 }
 
-// the most tokens per workgroup that still gives two workgroups per compute
-// unit; fewer tokens per workgroup otherwise (more workgroups, each staging
-// X for fewer tokens)
 template <class F>
 hipError_t launch_pf(GemmParams p, hipStream_t s) {
-    const int row_groups = (p.M + kRowsPerWG - 1) / kRowsPerWG;
-    const int rg_pad = (row_groups + kXcds - 1) / kXcds * kXcds;
-    const int64_t want = 2 * (int64_t)device_cu_count();
-    auto wgs = [&](int tt) { return (int64_t)rg_pad * ((p.n + 16 * tt - 1) / (16 * tt)); };
-    if (wgs(4) >= want) return launch_pf_tt<F, 4>(p, rg_pad, s);
-    if (wgs(2) >= want) return launch_pf_tt<F, 2>(p, rg_pad, s);
-    return launch_pf_tt<F, 1>(p, rg_pad, s);
+    const PfPlan plan = pf_plan(p.M, p.K, p.n);
+    switch (plan.tt) {
+    case 4: return launch_pf_tt<F, 4>(p, plan, s);
+    case 2: return launch_pf_tt<F, 2>(p, plan, s);
+    default: return launch_pf_tt<F, 1>(p, plan, s);
+    }
 }
 
 }  // namespace
+
+// Prefill launch plan.  The most tokens per workgroup (TT = 4, 2, 1) that
+// still gives two workgroups per compute unit of a 256-CU part without a K
+// split; failing that, one token tile per workgroup and K split into the
+// fewest slices (2 .. 16, at least two windows each) that reach that count.
+// The plan depends only on (M, K, n), so the workspace size does too.
+PfPlan pf_plan(int64_t M, int64_t K, int64_t n) {
+    constexpr int64_t kWant = 512;
+    PfPlan pl{};
+    const int64_t row_groups = (M + kRowsPerWG - 1) / kRowsPerWG;
+    pl.rg_pad = (int)((row_groups + kXcds - 1) / kXcds * kXcds);
+    const int wtotal = (int)((K + kWin - 1) / kWin);
+    auto tblocks = [&](int tt) { return (int)((n + 16 * tt - 1) / (16 * tt)); };
+    pl.slices = 1;
+    pl.wps = wtotal;
+    for (int tt = 4; tt >= 1; tt >>= 1) {
+        pl.tt = tt;
+        pl.token_blocks = tblocks(tt);
+        if ((int64_t)pl.rg_pad * pl.token_blocks >= kWant) return pl;
+    }
+    // tt = 1 here
+    for (int ks = 2; ks <= 16 && wtotal / ks >= 2; ks *= 2) {
+        pl.wps = (wtotal + ks - 1) / ks;
+        pl.slices = (wtotal + pl.wps - 1) / pl.wps;  // no empty slice
+        if ((int64_t)pl.rg_pad * pl.token_blocks * pl.slices >= kWant) break;
+    }
+    return pl;
+}
+
+size_t gemm_workspace(int64_t M, int64_t K, int64_t n) {
+    const PfPlan pl = pf_plan(M, K, n);
+    return pl.slices > 1 ? (size_t)pl.slices * (size_t)n * (size_t)M * sizeof(float) : 0;
+}
 
 size_t gemm_n_workspace(int64_t M, int64_t K, int32_t n) {
     const int64_t kw = windows_per_slice(M, K);
@@ -723,7 +764,7 @@ size_t gemm_n_workspace(int64_t M, int64_t K, int32_t n) {
 }
 
 hipError_t launch_gemm(int type, const uint8_t *W, int64_t M, int64_t K, int64_t n, const float *X,
-                       float *Y, hipStream_t s) {
+                       float *Y, void *ws, hipStream_t s) {
     GemmParams p{};
     p.W = W;
     p.M = (int32_t)M;
@@ -732,7 +773,7 @@ hipError_t launch_gemm(int type, const uint8_t *W, int64_t M, int64_t K, int64_t
     p.row_bytes = (int32_t)row_bytes_of(type, K);
     p.X = X;
     p.Y = Y;
-    p.partial = nullptr;
+    p.partial = reinterpret_cast<float *>(ws);
     switch (type) {
     case kQ4K: return launch_pf<GQ4K>(p, s);
     case kQ6K: return launch_pf<GQ6K>(p, s);

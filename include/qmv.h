@@ -104,7 +104,13 @@ typedef enum {
 } qmv_status;
 
 /* Operations that need a workspace, for qmv_workspace_bytes(). */
-typedef enum { QMV_OP_ARGMAX = 1, QMV_OP_MOE = 2, QMV_OP_GEMM_N = 3, QMV_OP_SHORT_CONV = 4 } qmv_op;
+typedef enum {
+    QMV_OP_ARGMAX = 1,
+    QMV_OP_MOE = 2,
+    QMV_OP_GEMM_N = 3,
+    QMV_OP_SHORT_CONV = 4,
+    QMV_OP_GEMM = 5
+} qmv_op;
 
 /* Largest K (columns) any entry point accepts: x is staged whole in LDS. */
 #define QMV_MAX_K 32768
@@ -258,11 +264,15 @@ qmv_status qmv_gemm_n(qmv_type t, const void *blocks, int64_t M, int64_t K, int3
  * row-major, 1 <= n <= QMV_MAX_PREFILL_N and n * K * 4 < 2^32.  Formats
  * Q8_0, Q4_K, Q6_K.  Same arithmetic as qmv_gemm_n (bf16 MFMA on the exact
  * codes, X as bf16 hi + lo, f32 scales per sub-block), so within 1e-5 *
- * sum_k |w_ik x_k| per output; K is not split (a workgroup covers 64 tokens
- * by 128 rows and walks all of K), so each output is one fixed-order sum:
- * deterministic, no workspace. */
+ * sum_k |w_ik x_k| per output.  A workgroup covers up to 64 tokens by 128
+ * rows; K is split into slices only when rows and tokens alone give too few
+ * workgroups (few rows, few tokens, long K), and the slices' partial sums
+ * are added in a fixed order, so results are deterministic either way.
+ * workspace: device, >= qmv_workspace_bytes(QMV_OP_GEMM, M, K, n, 0) bytes
+ * (0 when K is not split; then NULL is allowed), 16-byte aligned, no initial
+ * contents needed; QMV_EWORKSPACE if it is missing or too small. */
 qmv_status qmv_gemm(qmv_type t, const void *blocks, int64_t M, int64_t K, int64_t n, const float *X,
-                    float *Y, hipStream_t stream);
+                    float *Y, void *workspace, size_t ws_bytes, hipStream_t stream);
 
 /* ---- dequantise to f32 (verification surface): w_out[M][K] --------------
  * Bit-exact block decoding, the values every matvec above is defined on. */

@@ -42,6 +42,17 @@ def test_row_bytes_and_workspace():
     assert q.qmv_row_bytes("q5_k", 512) == 352
     assert q.qmv_workspace_bytes(q.OP_ARGMAX, 128000, 4096) >= 8 * 2048
     assert q.qmv_workspace_bytes(q.OP_MOE, 2048, 1536, 32, 4) == 256 + 3 * 4 * 1536 * 4
+    # prefill product: no workspace when rows and token blocks fill the chip,
+    # else whole n x M f32 slices (2 to 16 of them)
+    assert q.qmv_workspace_bytes(q.OP_GEMM, 28672, 4096, 512) == 0
+    assert q.qmv_workspace_bytes(q.OP_GEMM, 4096, 4096, 4096) == 0
+    for M, K, n in [(4096, 14336, 64), (4096, 4096, 16), (300, 14336, 20), (256, 512, 1)]:
+        w = q.qmv_workspace_bytes(q.OP_GEMM, M, K, n)
+        slices = w // (4 * n * M)
+        assert w % (4 * n * M) == 0 and (slices == 0 or 2 <= slices <= 16), (M, K, n, w)
+    assert q.qmv_workspace_bytes(q.OP_GEMM, 4096, 14336, 64) > 0
+    assert q.qmv_workspace_bytes(q.OP_GEMM, 256, 512, 1) == 0   # 2 windows: no split
+    assert q.qmv_workspace_bytes(q.OP_GEMM, 4096, 4096, q.MAX_PREFILL_N + 1) == 0
     assert q.load().qmv_status_str(3) == b"pointer misaligned"
 
 
@@ -87,6 +98,14 @@ def test_pointer_and_type_errors():
     assert status_of(q.qmv_gemm, "q4_k", A16, 4, 256, 0, A16, A16) == "QMV_ESHAPE"
     assert status_of(q.qmv_gemm, "q4_k", A16, 4, 256, q.MAX_PREFILL_N + 1, A16, A16) == "QMV_ESHAPE"
     assert status_of(q.qmv_gemm, "q4_k", A16, 4, 256, 64, A16 + 4, A16) == "QMV_EALIGN"
+    # a K-split plan needs its workspace
+    need = q.qmv_workspace_bytes(q.OP_GEMM, 256, 14336, 32)
+    assert need > 0
+    assert status_of(q.qmv_gemm, "q4_k", A16, 256, 14336, 32, A16, A16, 0, 0) == "QMV_EWORKSPACE"
+    assert status_of(q.qmv_gemm, "q4_k", A16, 256, 14336, 32, A16, A16, A16,
+                     need - 1) == "QMV_EWORKSPACE"
+    assert status_of(q.qmv_gemm, "q4_k", A16, 256, 14336, 32, A16, A16, A16 + 4,
+                     need) == "QMV_EALIGN"
     assert status_of(q.qmv_fused_rows, "q4_k", A16, 256, A16, [1] * 9, [A16] * 9) == "QMV_EINVAL"
     assert status_of(q.qmv_fused_rows, "q4_k", A16, 256, A16, [], []) == "QMV_EINVAL"
     assert status_of(q.qmv_gate_up_silu, "q4_k", A16, 8, 256, A16, 0) == "QMV_EINVAL"

@@ -5,7 +5,8 @@ against the oracle's f64 product (the same definition as the small batch).
 Bound: as the verify product (exact codes on the matrix cores, X as bf16
 hi + lo, f32 scales), within 1e-5 * sum_k |w_ik X[j][k]| per output.
 Also: permuting X's rows permutes Y's rows bit for bit (tokens are
-independent MFMA rows) and two runs are identical (K is not split).
+independent MFMA rows) and two runs are identical (K slices, when there
+are several, are added in a fixed order).
 """
 import numpy as np
 import pytest
@@ -26,7 +27,9 @@ import gguf_dequant_matvec_amd as q  # noqa: E402
 def gemm_gpu(t, bd, M, K, X):
     n = X.shape[0]
     Y = empty(n * M)
-    q.qmv_gemm(t, bd, M, K, n, dev(X), Y)
+    wsb = q.qmv_workspace_bytes(q.OP_GEMM, M, K, n)
+    ws = empty(wsb, "uint8") if wsb else None
+    q.qmv_gemm(t, bd, M, K, n, dev(X), Y, ws)
     return host(Y).reshape(n, M)
 
 
@@ -39,6 +42,11 @@ SHAPES = [
     ("q8_0", 77, 224, 130),      # a partial last window of Q8_0 blocks
     ("q8_0", 200, 576, 65),
     ("q4_k", 33, 512, 1),
+    # few rows and tokens, long K: K split into slices
+    ("q4_k", 300, 14336, 20),
+    ("q6_k", 129, 4096, 70),
+    ("q8_0", 200, 4000, 40),     # slices, the last one ending in a partial window
+    ("q4_k", 1000, 4096, 16),
 ]
 
 
@@ -76,3 +84,19 @@ def test_gemm_llama8b_gate_up_n512_sampled():
     for j in [0, 1, 63, 64, 200, 511]:
         yr, ar = oracle.qmv_rows(t, b, M, K, X[j], rows)
         assert_rel(Y[j, rows], yr, ar, what=f"token {j}")
+
+
+def test_gemm_split_k_is_deterministic_and_within_bound():
+    """A K-split call (few rows and tokens) is deterministic and agrees with
+    the oracle; its workspace is a whole number of n x M f32 slices."""
+    t, M, K, n = "q4_k", 256, 14336, 32
+    wsb = q.qmv_workspace_bytes(q.OP_GEMM, M, K, n)
+    assert wsb > 0 and wsb % (4 * n * M) == 0 and wsb // (4 * n * M) <= 16
+    b = quantized(t, M, K, 1130)
+    X = synth.activations(1131, K, n=n)
+    bd = dev(b)
+    Y = gemm_gpu(t, bd, M, K, X)
+    Y2 = gemm_gpu(t, bd, M, K, X)
+    assert np.array_equal(Y.view(np.uint32), Y2.view(np.uint32))
+    Yr, Ar = oracle.gemm_n(t, b, M, K, X)
+    assert_rel(Y.ravel(), Yr.ravel(), Ar.ravel(), what="split K")
