@@ -76,8 +76,11 @@ int resident_blocks(const void *kernel, int threads, size_t lds) {
     auto it = g_occ.find(key);
     if (it != g_occ.end()) return it->second;
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, lds) != hipSuccess || n < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, lds) != hipSuccess) {
+        (void)hipGetLastError();  // handled here: do not report it with the next launch
         n = 1;
+    }
+    if (n < 1) n = 1;
     g_occ[key] = n;
     return n;
 }

@@ -113,6 +113,8 @@ hipError_t launch_typed(const RowsParams &p_in, hipStream_t s, int *grid_out) {
 template <int MODE>
 hipError_t launch_fmt(int type, const RowsParams &p, hipStream_t s, int *grid_out) {
     switch (type) {
+    case kQ2K: return launch_typed<Q2K, MODE>(p, s, grid_out);
+    case kQ3K: return launch_typed<Q3K, MODE>(p, s, grid_out);
     case kQ4K: return launch_typed<Q4K, MODE>(p, s, grid_out);
     case kQ5K: return launch_typed<Q5K, MODE>(p, s, grid_out);
     case kQ6K: return launch_typed<Q6K, MODE>(p, s, grid_out);
