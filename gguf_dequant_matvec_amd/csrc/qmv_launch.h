@@ -44,9 +44,8 @@ constexpr int rows_per_lane() {
     return MODE == kModeMoeDown ? 1 : MODE == kModeShortConv ? 3 : kR;
 }
 
-template <class F, int MODE, int KS, bool XR>
+template <class F, int MODE, int KS, bool XR, int R = rows_per_lane<MODE>()>
 KernelPtr<F, MODE> kernel_for_ks(int G) {
-    constexpr int R = rows_per_lane<MODE>();
     switch (G) {
     case 4: return rows_kernel<F, 4, R, MODE, KS, XR>;
     case 8: return rows_kernel<F, 8, R, MODE, KS, XR>;
@@ -64,12 +63,24 @@ hipError_t launch_typed(const RowsParams &p_in, hipStream_t s, int *grid_out) {
     // the MoE down launch needs unit steps that never straddle two experts
     const int G = MODE == kModeMoeDown ? pow2_divisor(p.moe.units_per_mat) : pick_group(U);
     const int iters = (U + G - 1) / G;
+    const int waves = kBlockThreads / kWave;
+    // Plain and argmax launches take one row slot instead of two when two
+    // would leave at most one tile per wave of a full grid (no next item to
+    // overlap), and always for the argmax (its vocabulary-sized matrix ran
+    // 6% faster with one; row slots do not change any row's arithmetic).
+    constexpr bool kOneSlotModes = MODE == kModeStore || MODE == kModeArgmax;
+    bool one_slot = false;
+    if (kOneSlotModes) {
+        const int64_t tiles2 = ((int64_t)p.M + 2 * (kWave / G) - 1) / (2 * (kWave / G));
+        one_slot = MODE == kModeArgmax ||
+                   tiles2 <= (int64_t)device_cu_count() * kMaxBlocksPerCU * waves;
+    }
     // stacked modes: the row slots hold rows M apart (gate/up; B/C/x)
     const int64_t rows_per_tile =
-        (MODE == kModeSiluUp || MODE == kModeShortConv ? 1 : (int64_t)rows_per_lane<MODE>()) *
+        (MODE == kModeSiluUp || MODE == kModeShortConv || one_slot ? 1
+                                                                   : (int64_t)rows_per_lane<MODE>()) *
         (kWave / G);
     const int64_t ntiles = ((int64_t)p.M + rows_per_tile - 1) / rows_per_tile;
-    const int waves = kBlockThreads / kWave;
     const size_t lds =
         ((size_t)lds_x_floats<F>(p.K) + (F::kSumGroup ? (size_t)p.K / F::kSumGroup : 0)) * 4;
     // Tiles of one wave each.  The MoE down launch (few rows, long rows)
@@ -82,6 +93,11 @@ hipError_t launch_typed(const RowsParams &p_in, hipStream_t s, int *grid_out) {
                               MODE == kModeShortConv;
     KernelPtr<F, MODE> k = iters == 1 ? kernel_for_ks<F, MODE, 1, kXrModes>(G)
                                       : kernel_for_ks<F, MODE, 1, false>(G);
+    if constexpr (kOneSlotModes) {
+        if (one_slot)
+            k = iters == 1 ? kernel_for_ks<F, MODE, 1, kXrModes, 1>(G)
+                           : kernel_for_ks<F, MODE, 1, false, 1>(G);
+    }
     hipError_t e = ensure_lds((const void *)k, lds);
     if (e != hipSuccess) return e;
     int per_cu = resident_blocks((const void *)k, kBlockThreads, lds);

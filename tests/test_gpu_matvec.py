@@ -132,6 +132,8 @@ def test_x_extremes():
     ("q5_1", (33, 7), 224),
     ("q3_k", (512, 128, 128), 2048),
     ("q2_k", (300, 5), 4096),
+    # the stack takes two row slots per lane, each segment alone one
+    ("q4_k", (4096, 4096), 4096),
 ])
 def test_fused_rows(t, segs, K):
     M = sum(segs)
