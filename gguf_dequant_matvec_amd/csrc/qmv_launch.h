@@ -5,6 +5,8 @@
 #include "qmv_internal.h"
 #include "qmv_rows.h"
 
+#include <type_traits>
+
 namespace qmv {
 
 constexpr int kR = 2;  // row slots per lane
@@ -44,6 +46,14 @@ constexpr int rows_per_lane() {
     return MODE == kModeMoeDown ? 1 : MODE == kModeShortConv ? 3 : kR;
 }
 
+// Formats whose plain launches run faster with one row slot at every size
+// (measured at 14336-128000 rows: Q6_K 15% faster, Q8_0 in two-block units
+// 1.5%; every other format is 6-35% slower with one).
+template <class F>
+constexpr bool prefers_one_slot() {
+    return std::is_same<F, Q6K>::value || std::is_same<F, Q80x2>::value;
+}
+
 template <class F, int MODE, int KS, bool XR, int R = rows_per_lane<MODE>()>
 KernelPtr<F, MODE> kernel_for_ks(int G) {
     switch (G) {
@@ -66,13 +76,14 @@ hipError_t launch_typed(const RowsParams &p_in, hipStream_t s, int *grid_out) {
     const int waves = kBlockThreads / kWave;
     // Plain and argmax launches take one row slot instead of two when two
     // would leave at most one tile per wave of a full grid (no next item to
-    // overlap), and always for the argmax (its vocabulary-sized matrix ran
-    // 6% faster with one; row slots do not change any row's arithmetic).
+    // overlap), always for the argmax (its vocabulary-sized matrix ran 6%
+    // faster with one) and always for the formats that prefer one.  Row
+    // slots do not change any row's arithmetic.
     constexpr bool kOneSlotModes = MODE == kModeStore || MODE == kModeArgmax;
     bool one_slot = false;
     if (kOneSlotModes) {
         const int64_t tiles2 = ((int64_t)p.M + 2 * (kWave / G) - 1) / (2 * (kWave / G));
-        one_slot = MODE == kModeArgmax ||
+        one_slot = MODE == kModeArgmax || prefers_one_slot<F>() ||
                    tiles2 <= (int64_t)device_cu_count() * kMaxBlocksPerCU * waves;
     }
     // stacked modes: the row slots hold rows M apart (gate/up; B/C/x)

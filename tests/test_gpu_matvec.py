@@ -186,6 +186,27 @@ def test_argmax(t, M, K):
     assert i == int(np.argmax(yh)) and np.float32(v) == yh[i]
 
 
+def test_argmax_workspace_reuse_across_grid_sizes():
+    """One workspace serves calls of different sizes (so different grids)
+    back to back, without a synchronisation between them: every call's result
+    matches the argmax of its own matvec."""
+    ws = empty(q.qmv_workspace_bytes(q.OP_ARGMAX, 1, 256), "uint8")
+    cases = [("q6_k", 3000, 1536), ("q4_k", 5, 256), ("q8_0", 70000, 576), ("q6_k", 1, 256),
+             ("q4_k", 777, 2048), ("q6_k", 3000, 1536)]
+    outs = []
+    for n, (t, M, K) in enumerate(cases):
+        b, x = _case(t, M, K, 700 + n)
+        bd, xd = dev(b), dev(x)
+        idx, mx, y = empty(1, "int32"), empty(1), empty(M)
+        q.qmv_argmax(t, bd, M, K, xd, idx, mx, ws)
+        q.qmv(t, bd, M, K, xd, y)
+        outs.append((idx, mx, y, bd, xd))
+    for (t, M, K), (idx, mx, y, _, _) in zip(cases, outs):
+        yh = host(y)
+        i = int(host(idx)[0])
+        assert i == int(np.argmax(yh)) and np.float32(host(mx)[0]) == yh[i], (t, M, K)
+
+
 def test_argmax_ties_go_low():
     t, M, K = "q6_k", 4000, 1536
     b, x = _case(t, M, K, 600)
