@@ -17,13 +17,14 @@
 //   supplies A[l%16][kpl*(l/16) + t], B[kpl*(l/16) + t][l%16] and holds
 //   C[4*(l/16) + i][l%16].
 //
-// Work split: a workgroup of 8 waves owns 128 rows (16 per wave, one MFMA
-// tile) and one K-slice of KW windows of 256 weights (KW = 1, 2 or 4, chosen
-// so that there are enough workgroups).  Each wave issues the loads of all
-// its windows at once, then the workgroup stages X for the slice once in LDS
-// (bf16 hi/lo in the MFMA operand layout plus per-sub-block sums), so the
-// staging is shared by 128 rows.  With more than one slice, each writes its
-// partial sums to the workspace and a second kernel adds them in slice order
+// Work split: K is cut into slices of KW windows of 256 weights (KW = 1, 2
+// or 4, chosen so that there are enough (128-row group, slice) pairs).  An
+// 8-wave workgroup, one per compute unit, is bound to one slice: it stages X
+// for the slice once in LDS (bf16 hi/lo in the MFMA operand layout plus
+// per-sub-block sums), then each wave streams 16-row tiles (one MFMA tile)
+// of the slice, the next tile's weights in flight while the current one is
+// multiplied.  With more than one slice, each writes its partial sums to
+// the workspace and a second kernel adds them in slice order
 // (deterministic, no atomics).
 #include "qmv_device.h"
 #include "qmv_internal.h"
@@ -326,24 +327,25 @@ struct XStage {
     }
 };
 
+// A workgroup is bound to one K-slice: it stages X for the slice once, then
+// each wave walks 16-row tiles of the matrix (tile_first, tile_first +
+// stride, ...) with two register sets in turn, so the next tile's weights are
+// in flight while the current one is multiplied.  Tiles past the last row
+// read through an empty view (zeros, no memory traffic).
 template <class F, int KW>
-__global__ __launch_bounds__(kThreads) void gemm_n_kernel(GemmParams p) {
+__global__ __launch_bounds__(kThreads) void gemm_n_kernel(GemmParams p, int wg_per_slice) {
     using L = WinLayout<F>;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    constexpr int kWaves = kThreads / kWave;
     const int r = lane & 15, q = lane >> 4;
-    const int rg = (int)blockIdx.x % p.row_groups, slice = (int)blockIdx.x / p.row_groups;
-    const int row0 = __builtin_amdgcn_readfirstlane(rg * kRowsPerWG + wave * 16);
+    const int slice = (int)blockIdx.x % p.slices, gidx = (int)blockIdx.x / p.slices;
     const int nblocks = p.K / 32;                // Q8_0 blocks per row (last window)
     const int wtotal = (p.K + kWin - 1) / kWin;  // windows in a row
     const int wfirst = slice * KW;
-
-    // view from this wave's first row to the end of the matrix: rows past M
-    // read zeros
-    const int rows_left = p.M - row0 > 0 ? p.M - row0 : 0;
-    const BufSrc src(p.W + (int64_t)row0 * p.row_bytes,
-                     (uint64_t)rows_left * (uint64_t)(uint32_t)p.row_bytes);
+    const int row_tiles = (p.M + 15) / 16;
+    const int stride = wg_per_slice * kWaves;
     const uint32_t lane_off = (uint32_t)r * (uint32_t)p.row_bytes;
 
     auto nvalid_of = [&](int wi) {
@@ -354,16 +356,24 @@ __global__ __launch_bounds__(kThreads) void gemm_n_kernel(GemmParams p) {
             return F::kNSub;
         }
     };
-
-    // every window's weights in flight at once (windows past the row's end
-    // repeat the last one and are skipped below)
-    typename F::Regs wr[KW];
+    // every window of the slice for one tile (windows past the row's end
+    // repeat the last one and are skipped by the multiply)
+    auto load_tile = [&](typename F::Regs(&wr)[KW], int tile) {
+        const int row0 = __builtin_amdgcn_readfirstlane(tile * 16);
+        const int rows_left = p.M - row0 > 0 ? p.M - row0 : 0;
+        const BufSrc src(p.W + (int64_t)row0 * p.row_bytes,
+                         (uint64_t)rows_left * (uint64_t)(uint32_t)p.row_bytes);
 #pragma unroll
-    for (int i = 0; i < KW; i++) {
-        int wi = wfirst + i < wtotal ? wfirst + i : wtotal - 1;
-        wi = __builtin_amdgcn_readfirstlane(wi);
-        wr[i] = F::load(src, lane_off + (uint32_t)wi * F::kWinBytes, q, nvalid_of(wi));
-    }
+        for (int i = 0; i < KW; i++) {
+            int wi = wfirst + i < wtotal ? wfirst + i : wtotal - 1;
+            wi = __builtin_amdgcn_readfirstlane(wi);
+            wr[i] = F::load(src, lane_off + (uint32_t)wi * F::kWinBytes, q, nvalid_of(wi));
+        }
+    };
+
+    const int t0 = __builtin_amdgcn_readfirstlane(gidx * kWaves + wave);
+    typename F::Regs bufA[KW], bufB[KW];
+    load_tile(bufA, t0);
     {
         const BufSrc xview(reinterpret_cast<const uint8_t *>(p.X),
                            (uint64_t)p.n * (uint32_t)p.K * 4u);
@@ -377,45 +387,57 @@ __global__ __launch_bounds__(kThreads) void gemm_n_kernel(GemmParams p) {
     const uint32_t kmask = __builtin_amdgcn_readfirstlane(0x000F000Fu);
     uint32_t kbias;
     asm("v_mov_b32 %0, %1" : "=v"(kbias) : "i"(kB16));
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < KW; i++) {
-        const int wi = wfirst + i;
-        if (wi >= wtotal) break;
-        const uint8_t *base = smem + (size_t)i * L::kBytes;
-        const __bf16 *xhi = reinterpret_cast<const __bf16 *>(base);
-        const __bf16 *xlo = xhi + L::kVals;
-        const float *xs = reinterpret_cast<const float *>(base + 4 * L::kVals);
-        const int nsub = nvalid_of(wi);
-#pragma unroll
-        for (int j = 0; j < F::kNSub; j++) {
-            if (j >= nsub) break;
-            const int fo = ((j * 4 + q) * kTok + r) * F::kKpl;
-            const Frag<F> ah = *reinterpret_cast<const Frag<F> *>(xhi + fo);
-            const Frag<F> al = *reinterpret_cast<const Frag<F> *>(xlo + fo);
-            const Frag<F> b = F::codes(wr[i], j, kmask, kbias);
-            f32x4 c = {0.f, 0.f, 0.f, 0.f};
-            c = mfma<F>(ah, b, c);
-            c = mfma<F>(al, b, c);
-            float scale, corr;
-            F::scales(wr[i], j, scale, corr);
-            const float4 sx = *reinterpret_cast<const float4 *>(xs + j * kTok + 4 * q);
-            acc[0] = fmaf(scale, c[0], fmaf(-corr, sx.x, acc[0]));
-            acc[1] = fmaf(scale, c[1], fmaf(-corr, sx.y, acc[1]));
-            acc[2] = fmaf(scale, c[2], fmaf(-corr, sx.z, acc[2]));
-            acc[3] = fmaf(scale, c[3], fmaf(-corr, sx.w, acc[3]));
-        }
-    }
+    float *out = p.slices == 1 ? p.Y : p.partial + (int64_t)slice * p.n * p.M;
 
-    // tokens 4q .. 4q+3 of this lane's row
-    const int row = row0 + r;
-    if (row < p.M) {
-        float *out = p.slices == 1 ? p.Y : p.partial + (int64_t)slice * p.n * p.M;
+    auto multiply_store = [&](const typename F::Regs(&wr)[KW], int tile) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int t = 4 * q + i;
-            if (t < p.n) out[(int64_t)t * p.M + row] = acc[i];
+        for (int i = 0; i < KW; i++) {
+            const int wi = wfirst + i;
+            if (wi >= wtotal) break;
+            const uint8_t *base = smem + (size_t)i * L::kBytes;
+            const __bf16 *xhi = reinterpret_cast<const __bf16 *>(base);
+            const __bf16 *xlo = xhi + L::kVals;
+            const float *xs = reinterpret_cast<const float *>(base + 4 * L::kVals);
+            const int nsub = nvalid_of(wi);
+#pragma unroll
+            for (int j = 0; j < F::kNSub; j++) {
+                if (j >= nsub) break;
+                const int fo = ((j * 4 + q) * kTok + r) * F::kKpl;
+                const Frag<F> ah = *reinterpret_cast<const Frag<F> *>(xhi + fo);
+                const Frag<F> al = *reinterpret_cast<const Frag<F> *>(xlo + fo);
+                const Frag<F> b = F::codes(wr[i], j, kmask, kbias);
+                f32x4 c = {0.f, 0.f, 0.f, 0.f};
+                c = mfma<F>(ah, b, c);
+                c = mfma<F>(al, b, c);
+                float scale, corr;
+                F::scales(wr[i], j, scale, corr);
+                const float4 sx = *reinterpret_cast<const float4 *>(xs + j * kTok + 4 * q);
+                acc[0] = fmaf(scale, c[0], fmaf(-corr, sx.x, acc[0]));
+                acc[1] = fmaf(scale, c[1], fmaf(-corr, sx.y, acc[1]));
+                acc[2] = fmaf(scale, c[2], fmaf(-corr, sx.z, acc[2]));
+                acc[3] = fmaf(scale, c[3], fmaf(-corr, sx.w, acc[3]));
+            }
         }
+        // tokens 4q .. 4q+3 of this lane's row
+        const int row = tile * 16 + r;
+        if (row < p.M) {
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int t = 4 * q + i;
+                if (t < p.n) out[(int64_t)t * p.M + row] = acc[i];
+            }
+        }
+    };
+
+    // two register sets in turn: the set just multiplied receives the tile
+    // after next
+    for (int t = t0; t < row_tiles; t += 2 * stride) {
+        load_tile(bufB, t + stride);
+        multiply_store(bufA, t);
+        if (t + stride >= row_tiles) break;
+        load_tile(bufA, t + 2 * stride);
+        multiply_store(bufB, t + stride);
     }
 }
 
@@ -449,6 +471,8 @@ int windows_per_slice(int64_t M, int64_t K) {
     return 1;
 }
 
+// One 8-wave workgroup per compute unit; each slice gets an equal share of
+// the workgroups (at most one per 8 row tiles).
 template <class F, int KW>
 hipError_t launch_kw(GemmParams p, hipStream_t s) {
     const int wtotal = (p.K + kWin - 1) / kWin;
@@ -457,8 +481,15 @@ hipError_t launch_kw(GemmParams p, hipStream_t s) {
     const size_t lds = gemm_lds_bytes<F>(KW);
     hipError_t e = ensure_lds((const void *)gemm_n_kernel<F, KW>, lds);
     if (e != hipSuccess) return e;
-    const int64_t grid = (int64_t)p.row_groups * p.slices;
-    e = launch_main(gemm_n_kernel<F, KW>, dim3((unsigned)grid), dim3(kThreads), lds, s, p);
+    const int row_tiles = (p.M + 15) / 16;
+    const int waves = kThreads / kWave;
+    int per_slice = device_cu_count() / p.slices;
+    const int most = (row_tiles + waves - 1) / waves;
+    if (per_slice > most) per_slice = most;
+    if (per_slice < 1) per_slice = 1;
+    const int64_t grid = (int64_t)per_slice * p.slices;
+    e = launch_main(gemm_n_kernel<F, KW>, dim3((unsigned)grid), dim3(kThreads), lds, s, p,
+                    per_slice);
     if (e != hipSuccess || p.slices == 1) return e;
     const int64_t nm = (int64_t)p.n * p.M;
     hipLaunchKernelGGL(gemm_n_reduce, dim3((unsigned)((nm + 255) / 256)), dim3(256), 0, s,
