@@ -29,6 +29,8 @@ bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 bool valid_type(int t) { return block_weights_of(t) != 0; }
 // formats with a verify-product kernel and a device quantiser
 bool core_type(int t) { return t == kQ80 || t == kQ4K || t == kQ6K; }
+// formats of the matrix-core products (verify and prefill)
+bool mfma_type(int t) { return core_type(t) || t == kQ5K; }
 
 qmv_status check_matrix(int t, const void *blocks, int64_t M, int64_t K) {
     if (!valid_type(t)) return QMV_EINVAL;
@@ -333,7 +335,7 @@ qmv_status moe_qmv_topk(const float *x, int64_t H, const float *router, const fl
 qmv_status qmv_gemm_n(qmv_type t, const void *blocks, int64_t M, int64_t K, int32_t n,
                       const float *X, float *Y, void *workspace, size_t ws_bytes,
                       hipStream_t stream) {
-    if (!core_type(t)) return QMV_EINVAL;
+    if (!mfma_type(t)) return QMV_EINVAL;
     qmv_status st = check_matrix(t, blocks, M, K);
     if (st != QMV_OK) return st;
     if (n < 1 || n > QMV_MAX_N) return QMV_ESHAPE;
@@ -347,7 +349,7 @@ qmv_status qmv_gemm_n(qmv_type t, const void *blocks, int64_t M, int64_t K, int3
 
 qmv_status qmv_gemm(qmv_type t, const void *blocks, int64_t M, int64_t K, int64_t n, const float *X,
                     float *Y, void *workspace, size_t ws_bytes, hipStream_t stream) {
-    if (!core_type(t)) return QMV_EINVAL;
+    if (!mfma_type(t)) return QMV_EINVAL;
     qmv_status st = check_matrix(t, blocks, M, K);
     if (st != QMV_OK) return st;
     if (n < 1 || n > QMV_MAX_PREFILL_N) return QMV_ESHAPE;

@@ -105,7 +105,10 @@ struct GQ4K {
     // and 8-11 (min); 4-7 the low / high nibble of bytes 12-15 plus the top
     // two bits of bytes 4-7 / 8-11.
     __device__ static void scales(const Regs &r, int j, float &scale, float &corr) {
-        const uint32_t s0 = r.hdr.y, s1 = r.hdr.z, s2 = r.hdr.w;
+        scales_of(r.hdr, j, scale, corr);
+    }
+    __device__ static void scales_of(const uint4 &hdr, int j, float &scale, float &corr) {
+        const uint32_t s0 = hdr.y, s1 = hdr.z, s2 = hdr.w;
         const int sh = 8 * (j & 3);
         int sc, m;
         if (j < 4) {
@@ -115,9 +118,47 @@ struct GQ4K {
             sc = ((s2 >> sh) & 15) | ((((s0 >> sh) >> 6) & 3) << 4);
             m = (((s2 >> sh) >> 4) & 15) | ((((s1 >> sh) >> 6) & 3) << 4);
         }
-        const float d = half_bits_to_float(r.hdr.x), dmin = half_bits_to_float(r.hdr.x >> 16);
+        const float d = half_bits_to_float(hdr.x), dmin = half_bits_to_float(hdr.x >> 16);
         scale = d * (float)sc;
         corr = fmaf(128.0f, scale, dmin * (float)m);
+    }
+};
+
+// Q5_K (BebeLM page, section "局限与未来": Q5_K_M): the Q4_K super-block plus
+// 32 bytes of fifth bits; bit 2c + h of high byte l is the fifth bit of
+// weight 64c + 32h + l, i.e. bit j of byte l for sub-block j.  Lane group q
+// takes high bytes 8q .. 8q + 8 (the same l as its nibble bytes), and each
+// code dword gets its two fifth bits or-ed in at bit 4 of both halves, so
+// the bf16 codes are 128 + q with q in 0..31 (exact).
+struct GQ5K {
+    static constexpr int kSub = 32, kNSub = 8, kKpl = 8, kWinBytes = 176;
+    struct Regs {
+        uint4 hdr;
+        uint2 qh;        // high bytes 8q .. 8q + 8
+        uint2 piece[4];  // nibble bytes 32c + 8q .. +8, c = 0..3
+    };
+    __device__ static constexpr int perm(int b) { return GQ4K::perm(b); }
+    __device__ static void slot(int i, int &j, int &q) { GQ4K::slot(i, j, q); }
+    __device__ static Regs load(const BufSrc &src, uint32_t off, int q, int) {
+        Regs r;
+        r.hdr = src.ld16(off);
+        r.qh = src.ld8(off + 16 + 8 * q);
+#pragma unroll
+        for (int c = 0; c < 4; c++) r.piece[c] = src.ld8(off + 48 + 32 * c + 8 * q);
+        return r;
+    }
+    __device__ static bf16x8 codes(const Regs &r, int j, uint32_t mask, uint32_t bias) {
+        const uint2 p = r.piece[j >> 1];
+        const int sh = (j & 1) * 4;
+        uint32_t d[4];
+        d[0] = ((p.x >> sh) & mask) | bias | (((r.qh.x >> j) & 0x00010001u) << 4);
+        d[1] = ((p.x >> (sh + 8)) & mask) | bias | (((r.qh.x >> (j + 8)) & 0x00010001u) << 4);
+        d[2] = ((p.y >> sh) & mask) | bias | (((r.qh.y >> j) & 0x00010001u) << 4);
+        d[3] = ((p.y >> (sh + 8)) & mask) | bias | (((r.qh.y >> (j + 8)) & 0x00010001u) << 4);
+        return __builtin_bit_cast(bf16x8, d);
+    }
+    __device__ static void scales(const Regs &r, int j, float &scale, float &corr) {
+        GQ4K::scales_of(r.hdr, j, scale, corr);
     }
 };
 
@@ -807,6 +848,7 @@ hipError_t launch_gemm(int type, const uint8_t *W, int64_t M, int64_t K, int64_t
     p.partial = reinterpret_cast<float *>(ws);
     switch (type) {
     case kQ4K: return launch_pf<GQ4K>(p, s);
+    case kQ5K: return launch_pf<GQ5K>(p, s);
     case kQ6K: return launch_pf<GQ6K>(p, s);
     case kQ80: return launch_pf<GQ80>(p, s);
     default: return hipErrorInvalidValue;
@@ -826,6 +868,7 @@ hipError_t launch_gemm_n(int type, const uint8_t *W, int64_t M, int64_t K, int32
     p.partial = reinterpret_cast<float *>(ws);
     switch (type) {
     case kQ4K: return launch_typed<GQ4K>(p, s);
+    case kQ5K: return launch_typed<GQ5K>(p, s);
     case kQ6K: return launch_typed<GQ6K>(p, s);
     case kQ80: return launch_typed<GQ80>(p, s);
     default: return hipErrorInvalidValue;

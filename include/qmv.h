@@ -61,8 +61,9 @@ extern "C" {
  * quantisations), Q2_K and Q3_K (same section: K-quants from Q2K up) and
  * Q5_K (BebeLM page, section "局限与未来": Q5_K_M) are
  * served by the single-token, fused-row, gated gate/up, argmax, MoE and
- * dequantisation calls; qmv_gemm_n and qmv_quantize take the first three
- * only.  Blocks (standard GGUF layouts, little-endian):
+ * dequantisation calls; the matrix-core products qmv_gemm_n and qmv_gemm
+ * take the first three and Q5_K, qmv_quantize the first three only.  Blocks
+ * (standard GGUF layouts, little-endian):
  *   Q4_0 18 B: fp16 d, 16 code bytes;                w = d * (q - 8)
  *   Q4_1 20 B: fp16 d, fp16 m, 16 code bytes;        w = d * q + m
  *   Q5_0 22 B: fp16 d, u32 fifth bits, 16 code bytes; w = d * (q - 16)
@@ -247,7 +248,8 @@ qmv_status moe_qmv_topk(const float *x, int64_t H, const float *router, const fl
 /* ---- small batch (speculative verify): Y[n][M] = X[n][K] . dequant(W)^T ----
  * FlareLLM page, section "推理层面的深度优化" (n-gram speculative decoding
  * checks several drafted tokens against the same weights).  X: f32 n x K
- * row-major, Y: f32 n x M row-major, 1 <= n <= QMV_MAX_N.  Runs on the matrix
+ * row-major, Y: f32 n x M row-major, 1 <= n <= QMV_MAX_N.  Formats Q8_0,
+ * Q4_K, Q5_K, Q6_K.  Runs on the matrix
  * cores (bf16 MFMA on the exact integer codes, X split into bf16 hi + lo, f32
  * scales), within 1e-5 * sum_k |w_ik x_k| of the exact result like the
  * matvecs.  workspace: device, >= qmv_workspace_bytes(QMV_OP_GEMM_N, M, K, n,
@@ -262,7 +264,7 @@ qmv_status qmv_gemm_n(qmv_type t, const void *blocks, int64_t M, int64_t K, int3
  * BebeLM page, section "性能表现" (prompt tokens are processed as a batch,
  * unlike the one-token decode).  X: f32 n x K row-major, Y: f32 n x M
  * row-major, 1 <= n <= QMV_MAX_PREFILL_N and n * K * 4 < 2^32.  Formats
- * Q8_0, Q4_K, Q6_K.  Same arithmetic as qmv_gemm_n (bf16 MFMA on the exact
+ * Q8_0, Q4_K, Q5_K, Q6_K.  Same arithmetic as qmv_gemm_n (bf16 MFMA on the exact
  * codes, X as bf16 hi + lo, f32 scales per sub-block), so within 1e-5 *
  * sum_k |w_ik x_k| per output.  A workgroup covers up to 64 tokens by 128
  * rows; K is split into slices only when rows and tokens alone give too few

@@ -91,10 +91,13 @@ def test_pointer_and_type_errors():
     assert status_of(q.qmv_dequant, 5, A16, 4, 256, A16) == "QMV_EINVAL"   # no such GGUF type
     assert status_of(q.qmv_dequant, 4, A16, 4, 256, A16) == "QMV_EINVAL"
     assert status_of(q.qmv_dequant, 15, A16, 4, 256, A16) == "QMV_EINVAL"  # Q8_K: not served
-    # the verify product and the device quantiser take Q8_0, Q4_K and Q6_K only
-    assert status_of(q.qmv_gemm_n, "q5_k", A16, 4, 256, 8, A16, A16, A16, 1 << 20) == "QMV_EINVAL"
+    # the matrix-core products take Q8_0, Q4_K, Q5_K and Q6_K, the device
+    # quantiser Q8_0, Q4_K and Q6_K
+    assert status_of(q.qmv_gemm_n, "q4_0", A16, 4, 256, 8, A16, A16, A16, 1 << 20) == "QMV_EINVAL"
+    assert status_of(q.qmv_gemm_n, "q3_k", A16, 4, 256, 8, A16, A16, A16, 1 << 20) == "QMV_EINVAL"
+    assert status_of(q.qmv_quantize, "q5_k", A16, 4, 256, A16) == "QMV_EINVAL"
     assert status_of(q.qmv_quantize, "q4_0", A16, 4, 256, A16) == "QMV_EINVAL"
-    assert status_of(q.qmv_gemm, "q5_k", A16, 4, 256, 64, A16, A16) == "QMV_EINVAL"
+    assert status_of(q.qmv_gemm, "q2_k", A16, 4, 256, 64, A16, A16) == "QMV_EINVAL"
     assert status_of(q.qmv_gemm, "q4_k", A16, 4, 256, 0, A16, A16) == "QMV_ESHAPE"
     assert status_of(q.qmv_gemm, "q4_k", A16, 4, 256, q.MAX_PREFILL_N + 1, A16, A16) == "QMV_ESHAPE"
     assert status_of(q.qmv_gemm, "q4_k", A16, 4, 256, 64, A16 + 4, A16) == "QMV_EALIGN"

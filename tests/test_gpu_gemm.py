@@ -38,6 +38,7 @@ SHAPES = [
     ("q4_k", 1000, 14336, 16), ("q4_k", 4096, 4096, 16),
     ("q6_k", 200, 1536, 16), ("q6_k", 77, 4096, 3), ("q6_k", 500, 4096, 8),
     ("q8_0", 100, 576, 16), ("q8_0", 37, 224, 5), ("q8_0", 300, 4096, 16), ("q8_0", 17, 32, 2),
+    ("q5_k", 300, 4096, 16), ("q5_k", 129, 2048, 7), ("q5_k", 1000, 14336, 16),
 ]
 
 
@@ -64,7 +65,7 @@ def test_gemm_n_one_column_matches_matvec():
     assert np.all(np.abs(Y[0].astype(np.float64) - host(y)) <= 2e-5 * ar)
 
 
-@pytest.mark.parametrize("t", ["q4_k", "q6_k", "q8_0"])
+@pytest.mark.parametrize("t", ["q4_k", "q5_k", "q6_k", "q8_0"])
 def test_gemm_n_token_permutation_and_determinism(t):
     M, K, n = 333, 4096, 16
     b = quantized(t, M, K, 820)

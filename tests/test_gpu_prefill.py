@@ -47,6 +47,8 @@ SHAPES = [
     ("q6_k", 129, 4096, 70),
     ("q8_0", 200, 4000, 40),     # slices, the last one ending in a partial window
     ("q4_k", 1000, 4096, 16),
+    ("q5_k", 300, 4096, 100),    # Q5_K: the Q4_K policy plus fifth bits
+    ("q5_k", 129, 14336, 20),    # and with K slices
 ]
 
 
@@ -60,7 +62,7 @@ def test_gemm_parity(t, M, K, n):
     print(f"{t} {M}x{K} n={n}: worst |dY|/sum|wx| = {worst:.2e}")
 
 
-@pytest.mark.parametrize("t", ["q4_k", "q6_k", "q8_0"])
+@pytest.mark.parametrize("t", ["q4_k", "q5_k", "q6_k", "q8_0"])
 def test_gemm_token_permutation_and_determinism(t):
     M, K, n = 260, 1024, 150
     b = quantized(t, M, K, 1110)
