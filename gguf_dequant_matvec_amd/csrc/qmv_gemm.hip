@@ -4,9 +4,11 @@
 //
 // Exactness plan (the result stays within the f32 matvec's 1e-5 sum|w x|):
 //  - the MFMA's weight operand holds the raw integer codes, which bf16
-//    represents exactly (written 0x43uu = 128 + u, the +128 folded into a
-//    per-sub-block correction); the f32 scales d*sc and mins are applied to
-//    the f32 MFMA result once per sub-block;
+//    represents exactly (written 0x43uu = 128 + u); the f32 scale d*sc is
+//    applied to the f32 MFMA result once per sub-block, and the per-sub-block
+//    correction (the +128 and the min) times the activation sums is itself a
+//    small product, sums[token][j] x corr[j][row], done by one f32 MFMA
+//    (16x16x4) per four sub-blocks straight into the accumulator;
 //  - X is split into bf16 hi + lo (two MFMAs into one accumulator), so the
 //    only representation error is |x - hi - lo| <= 2^-18 |x|.
 // Operand roles: tokens are the MFMA M side (A = X fragment), weight rows the
@@ -104,23 +106,25 @@ struct GQ4K {
     // Scale bytes: sub-blocks 0-3 take the low 6 bits of bytes 4-7 (scale)
     // and 8-11 (min); 4-7 the low / high nibble of bytes 12-15 plus the top
     // two bits of bytes 4-7 / 8-11.
-    __device__ static void scales(const Regs &r, int j, float &scale, float &corr) {
-        scales_of(r.hdr, j, scale, corr);
-    }
-    __device__ static void scales_of(const uint4 &hdr, int j, float &scale, float &corr) {
-        const uint32_t s0 = hdr.y, s1 = hdr.z, s2 = hdr.w;
+    static constexpr bool kCorr = true;
+    __device__ static float scale_of(const Regs &r, int j) { return hdr_scale(r.hdr, j); }
+    __device__ static float corr_of(const Regs &r, int j) { return hdr_corr(r.hdr, j); }
+    __device__ static int hdr_sc(const uint4 &hdr, int j) {
         const int sh = 8 * (j & 3);
-        int sc, m;
-        if (j < 4) {
-            sc = (s0 >> sh) & 63;
-            m = (s1 >> sh) & 63;
-        } else {
-            sc = ((s2 >> sh) & 15) | ((((s0 >> sh) >> 6) & 3) << 4);
-            m = (((s2 >> sh) >> 4) & 15) | ((((s1 >> sh) >> 6) & 3) << 4);
-        }
-        const float d = half_bits_to_float(hdr.x), dmin = half_bits_to_float(hdr.x >> 16);
-        scale = d * (float)sc;
-        corr = fmaf(128.0f, scale, dmin * (float)m);
+        return j < 4 ? (int)((hdr.y >> sh) & 63)
+                     : (int)(((hdr.w >> sh) & 15) | ((((hdr.y >> sh) >> 6) & 3) << 4));
+    }
+    __device__ static int hdr_m(const uint4 &hdr, int j) {
+        const int sh = 8 * (j & 3);
+        return j < 4 ? (int)((hdr.z >> sh) & 63)
+                     : (int)((((hdr.w >> sh) >> 4) & 15) | ((((hdr.z >> sh) >> 6) & 3) << 4));
+    }
+    __device__ static float hdr_scale(const uint4 &hdr, int j) {
+        return half_bits_to_float(hdr.x) * (float)hdr_sc(hdr, j);
+    }
+    __device__ static float hdr_corr(const uint4 &hdr, int j) {
+        const float dmin = half_bits_to_float(hdr.x >> 16);
+        return fmaf(128.0f, hdr_scale(hdr, j), dmin * (float)hdr_m(hdr, j));
     }
 };
 
@@ -157,9 +161,9 @@ struct GQ5K {
         d[3] = ((p.y >> (sh + 8)) & mask) | bias | (((r.qh.y >> (j + 8)) & 0x00010001u) << 4);
         return __builtin_bit_cast(bf16x8, d);
     }
-    __device__ static void scales(const Regs &r, int j, float &scale, float &corr) {
-        GQ4K::scales_of(r.hdr, j, scale, corr);
-    }
+    static constexpr bool kCorr = true;
+    __device__ static float scale_of(const Regs &r, int j) { return GQ4K::hdr_scale(r.hdr, j); }
+    __device__ static float corr_of(const Regs &r, int j) { return GQ4K::hdr_corr(r.hdr, j); }
 };
 
 struct GQ6K {
@@ -205,11 +209,12 @@ struct GQ6K {
         return __builtin_bit_cast(s16x4, d);
     }
     // w = d*sc*(u - 32) and the codes are u + 128: y += d*sc*C - 160*d*sc*sum(x)
-    __device__ static void scales(const Regs &r, int j, float &scale, float &corr) {
+    static constexpr bool kCorr = true;
+    __device__ static float scale_of(const Regs &r, int j) {
         const uint32_t w = j < 4 ? r.sc.x : j < 8 ? r.sc.y : j < 12 ? r.sc.z : r.sc.w;
-        scale = half_bits_to_float(r.d) * (float)(int32_t)(int8_t)((w >> (8 * (j & 3))) & 0xFFu);
-        corr = 160.0f * scale;
+        return half_bits_to_float(r.d) * (float)(int32_t)(int8_t)((w >> (8 * (j & 3))) & 0xFFu);
     }
+    __device__ static float corr_of(const Regs &r, int j) { return 160.0f * scale_of(r, j); }
 };
 
 struct GQ80 {
@@ -250,16 +255,26 @@ struct GQ80 {
         }
         return __builtin_bit_cast(bf16x8, d);
     }
-    __device__ static void scales(const Regs &r, int j, float &scale, float &corr) {
-        scale = half_bits_to_float(r.d[j]);
-        corr = 0.f;
-    }
+    static constexpr bool kCorr = false;  // signed codes, no offset, no min
+    __device__ static float scale_of(const Regs &r, int j) { return half_bits_to_float(r.d[j]); }
+    __device__ static float corr_of(const Regs &, int) { return 0.f; }
 };
 
 template <class F>
 using Frag = typename std::conditional<F::kKpl == 8, bf16x8, s16x4>::type;
 template <class F>
 using BFrag = typename std::conditional<F::kKpl == 8, bf16x8, bf16x4>::type;
+
+// acc[token][row] -= sum over four sub-blocks of sums[token][j] * corr[j][row]:
+// an f32 MFMA with K = 4, lane (r, q) supplying the sum of token r and the
+// correction of its row for sub-block j0 + q.
+template <class F, class Regs>
+__device__ __forceinline__ f32x4 corr_mfma(const Regs &w, const float *sums, int stride, int tok,
+                                           int j0, int r, int q, f32x4 acc) {
+    const float a = -sums[(j0 + q) * stride + tok + r];
+    const float b = F::corr_of(w, j0 + q);
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+}
 
 template <class F>
 __device__ __forceinline__ f32x4 mfma(const Frag<F> &a, const Frag<F> &b, f32x4 c) {
@@ -441,6 +456,11 @@ __global__ __launch_bounds__(kThreads) void gemm_n_kernel(GemmParams p, int wg_p
             const __bf16 *xlo = xhi + L::kVals;
             const float *xs = reinterpret_cast<const float *>(base + 4 * L::kVals);
             const int nsub = nvalid_of(wi);
+            if constexpr (F::kCorr) {
+#pragma unroll
+                for (int j0 = 0; j0 < F::kNSub; j0 += 4)
+                    acc = corr_mfma<F>(wr[i], xs, kTok, 0, j0, r, q, acc);
+            }
 #pragma unroll
             for (int j = 0; j < F::kNSub; j++) {
                 if (j >= nsub) break;
@@ -451,13 +471,11 @@ __global__ __launch_bounds__(kThreads) void gemm_n_kernel(GemmParams p, int wg_p
                 f32x4 c = {0.f, 0.f, 0.f, 0.f};
                 c = mfma<F>(ah, b, c);
                 c = mfma<F>(al, b, c);
-                float scale, corr;
-                F::scales(wr[i], j, scale, corr);
-                const float4 sx = *reinterpret_cast<const float4 *>(xs + j * kTok + 4 * q);
-                acc[0] = fmaf(scale, c[0], fmaf(-corr, sx.x, acc[0]));
-                acc[1] = fmaf(scale, c[1], fmaf(-corr, sx.y, acc[1]));
-                acc[2] = fmaf(scale, c[2], fmaf(-corr, sx.z, acc[2]));
-                acc[3] = fmaf(scale, c[3], fmaf(-corr, sx.w, acc[3]));
+                const float scale = F::scale_of(wr[i], j);
+                acc[0] = fmaf(scale, c[0], acc[0]);
+                acc[1] = fmaf(scale, c[1], acc[1]);
+                acc[2] = fmaf(scale, c[2], acc[2]);
+                acc[3] = fmaf(scale, c[3], acc[3]);
             }
         }
         // tokens 4q .. 4q+3 of this lane's row
@@ -707,12 +725,18 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_pf_kernel(GemmParams p, int 
         const __bf16 *xlo = xhi + L::kVals;
         const float *xsum = reinterpret_cast<const float *>(base + 4 * L::kVals);
         const int nsub = nvalid_of(wi);
+        if constexpr (F::kCorr) {
+#pragma unroll
+            for (int j0 = 0; j0 < F::kNSub; j0 += 4)
+#pragma unroll
+                for (int tt = 0; tt < kPfTiles; tt++)
+                    acc[tt] = corr_mfma<F>(w, xsum, kPfTokens, tt * 16, j0, r, q, acc[tt]);
+        }
 #pragma unroll
         for (int j = 0; j < F::kNSub; j++) {
             if (j >= nsub) break;
             const Frag<F> bcode = F::codes(w, j, kmask, kbias);
-            float scale, corr;
-            F::scales(w, j, scale, corr);
+            const float scale = F::scale_of(w, j);
 #pragma unroll
             for (int tt = 0; tt < kPfTiles; tt++) {
                 const int fo = ((j * 4 + q) * kPfTokens + tt * 16 + r) * F::kKpl;
@@ -721,11 +745,10 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_pf_kernel(GemmParams p, int 
                 f32x4 c = {0.f, 0.f, 0.f, 0.f};
                 c = mfma<F>(ah, bcode, c);
                 c = mfma<F>(al, bcode, c);
-                const float4 sx = *reinterpret_cast<const float4 *>(xsum + j * kPfTokens + tt * 16 + 4 * q);
-                acc[tt][0] = fmaf(scale, c[0], fmaf(-corr, sx.x, acc[tt][0]));
-                acc[tt][1] = fmaf(scale, c[1], fmaf(-corr, sx.y, acc[tt][1]));
-                acc[tt][2] = fmaf(scale, c[2], fmaf(-corr, sx.z, acc[tt][2]));
-                acc[tt][3] = fmaf(scale, c[3], fmaf(-corr, sx.w, acc[tt][3]));
+                acc[tt][0] = fmaf(scale, c[0], acc[tt][0]);
+                acc[tt][1] = fmaf(scale, c[1], acc[tt][1]);
+                acc[tt][2] = fmaf(scale, c[2], acc[tt][2]);
+                acc[tt][3] = fmaf(scale, c[3], acc[tt][3]);
                 // keep each tile's operand reads and epilogue next to its
                 // MFMAs (hoisting or sinking them across tiles would need
                 // more registers than a wave has)
