@@ -101,7 +101,7 @@ hipError_t launch_typed(const RowsParams &p_in, hipStream_t s, int *grid_out) {
     // and fused rows and the argmax stay bit-identical to the plain matvec.
     // a row of one unit step keeps its activations in registers
     constexpr bool kXrModes = MODE == kModeStore || MODE == kModeArgmax || MODE == kModeSiluUp ||
-                              MODE == kModeShortConv;
+                              MODE == kModeShortConv || MODE == kModeMoeGateUp;
     KernelPtr<F, MODE> k = iters == 1 ? kernel_for_ks<F, MODE, 1, kXrModes>(G)
                                       : kernel_for_ks<F, MODE, 1, false>(G);
     if constexpr (kOneSlotModes) {

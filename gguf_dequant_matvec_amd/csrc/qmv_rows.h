@@ -224,7 +224,7 @@ __device__ __forceinline__ void moe_select(const MoeArgs &m, int32_t *sel, float
 // wave order, so the result is still fixed by (format, K, G, KS).
 // XR: a row is a single unit step, so every lane keeps the same unit for the
 // whole launch and reads its activations from LDS once, after staging, into
-// registers (plain and argmax modes only).
+// registers (modes whose x is one vector: not the MoE down launch).
 // The body takes its workgroup index `bid` among `nblk` workgroups, so one
 // launch can run two bodies side by side on separate workgroup ranges.
 template <class F, int G, int R, int MODE, int KS, bool XR>
@@ -457,6 +457,7 @@ __device__ __forceinline__ void rows_body(const RowsParams &p, const int bid, co
             moe_select(p.moe, sel, wsel);
             issue(bufA, tA, itA);
         });
+        if constexpr (XR) F::load_x(xs, g < U ? g : 0, xr);
     } else if (MODE == kModeMoeDown) {
         if ((int)threadIdx.x < p.moe.k) {
             sel[threadIdx.x] = p.moe.topk_idx[threadIdx.x];
