@@ -471,24 +471,37 @@ __device__ __forceinline__ void rows_body(const RowsParams &p, const int bid, co
         const int I = p.moe.I, K = p.K;
         const int nt = blockDim.x;
         const BufSrc gv(reinterpret_cast<const uint8_t *>(p.moe.gu), (uint64_t)p.moe.k * 2 * I * 4);
-        auto pass = [&](int base0, bool first) {
-            const int base = base0 + (int)threadIdx.x * 4;
-            const int sl = base < K ? base / I : 0, j = base - sl * I;
-            const uint32_t off = (uint32_t)(sl * 2 * I + j) * 4u;
-            const float4 gg = __builtin_bit_cast(float4, gv.ld16(off));
-            const float4 uu = __builtin_bit_cast(float4, gv.ld16(off + (uint32_t)I * 4u));
+        // kNB passes of 4 values per thread at a time: all their loads are
+        // issued before any is used, so the batch pays one load latency
+        constexpr int kNB = 4;
+        auto batch = [&](int base0, bool first) {
+            float4 gg[kNB], uu[kNB];
+            int base[kNB], sl[kNB];
+#pragma unroll
+            for (int i = 0; i < kNB; i++) {
+                base[i] = base0 + i * nt * 4 + (int)threadIdx.x * 4;
+                sl[i] = base[i] < K ? base[i] / I : 0;
+                const int j = base[i] < K ? base[i] - sl[i] * I : 0;
+                const uint32_t off = (uint32_t)(sl[i] * 2 * I + j) * 4u;
+                gg[i] = __builtin_bit_cast(float4, gv.ld16(off));
+                uu[i] = __builtin_bit_cast(float4, gv.ld16(off + (uint32_t)I * 4u));
+            }
             if (first) {
                 issue(bufA, tA, itA);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            const float4 h = make_float4(siluf(gg.x) * uu.x, siluf(gg.y) * uu.y,
-                                         siluf(gg.z) * uu.z, siluf(gg.w) * uu.w);
-            if (bid == 0 && base < K) *reinterpret_cast<float4 *>(p.moe.h + base) = h;
-            const float w = wsel[sl];
-            put_x4<F>(xs, sums, base, base < K, make_float4(w * h.x, w * h.y, w * h.z, w * h.w));
+#pragma unroll
+            for (int i = 0; i < kNB; i++) {
+                const float4 h = make_float4(siluf(gg[i].x) * uu[i].x, siluf(gg[i].y) * uu[i].y,
+                                             siluf(gg[i].z) * uu[i].z, siluf(gg[i].w) * uu[i].w);
+                if (bid == 0 && base[i] < K) *reinterpret_cast<float4 *>(p.moe.h + base[i]) = h;
+                const float w = wsel[sl[i]];
+                put_x4<F>(xs, sums, base[i], base[i] < K,
+                          make_float4(w * h.x, w * h.y, w * h.z, w * h.w));
+            }
         };
-        pass(0, true);
-        for (int base0 = nt * 4; base0 < K; base0 += nt * 4) pass(base0, false);
+        batch(0, true);
+        for (int base0 = nt * 4 * kNB; base0 < K; base0 += nt * 4 * kNB) batch(base0, false);
         __syncthreads();
     } else {
         // the first item's weights are requested right after the first
