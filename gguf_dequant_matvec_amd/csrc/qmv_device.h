@@ -8,6 +8,8 @@ namespace qmv {
 
 constexpr int kWave = 64;          // CDNA wavefront
 constexpr int kBlockThreads = 256;  // 4 waves per workgroup
+constexpr int kWideBlockThreads = 512;  // 8 waves: one workgroup per CU (long rows)
+constexpr int kMaxBlockThreads = 512;
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 

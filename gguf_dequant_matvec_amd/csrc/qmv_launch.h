@@ -54,14 +54,15 @@ constexpr bool prefers_one_slot() {
     return std::is_same<F, Q6K>::value || std::is_same<F, Q80x2>::value;
 }
 
-template <class F, int MODE, int KS, bool XR, int R = rows_per_lane<MODE>()>
+template <class F, int MODE, int KS, bool XR, int R = rows_per_lane<MODE>(),
+          int BT = kBlockThreads>
 KernelPtr<F, MODE> kernel_for_ks(int G) {
     switch (G) {
-    case 4: return rows_kernel<F, 4, R, MODE, KS, XR>;
-    case 8: return rows_kernel<F, 8, R, MODE, KS, XR>;
-    case 16: return rows_kernel<F, 16, R, MODE, KS, XR>;
-    case 32: return rows_kernel<F, 32, R, MODE, KS, XR>;
-    default: return rows_kernel<F, 64, R, MODE, KS, XR>;
+    case 4: return rows_kernel<F, 4, R, MODE, KS, XR, BT>;
+    case 8: return rows_kernel<F, 8, R, MODE, KS, XR, BT>;
+    case 16: return rows_kernel<F, 16, R, MODE, KS, XR, BT>;
+    case 32: return rows_kernel<F, 32, R, MODE, KS, XR, BT>;
+    default: return rows_kernel<F, 64, R, MODE, KS, XR, BT>;
     }
 }
 
@@ -73,7 +74,17 @@ hipError_t launch_typed(const RowsParams &p_in, hipStream_t s, int *grid_out) {
     // the MoE down launch needs unit steps that never straddle two experts
     const int G = MODE == kModeMoeDown ? pow2_divisor(p.moe.units_per_mat) : pick_group(U);
     const int iters = (U + G - 1) / G;
-    const int waves = kBlockThreads / kWave;
+    // Plain launches with long rows (K >= 8192: x of 32 KB or more, staged in
+    // LDS) use one 8-wave workgroup per compute unit instead of two 4-wave
+    // ones, so each compute unit stages x once, not twice (4096 x 14336
+    // Q4_K: 11.4 -> 9.9 us).  Shorter rows keep two 4-wave workgroups
+    // (gate+up 28672 x 4096 was slower with one 8-wave, and Q8_0 1536 x 576
+    // went from 4.2 to 5.7 us with half as many workgroups).
+    const bool wide = MODE == kModeStore && iters > 1 && p.K >= 8192;
+    const int bt = wide ? kWideBlockThreads : kBlockThreads;
+    const int waves = bt / kWave;
+    const int64_t total_waves =
+        (int64_t)device_cu_count() * kMaxBlocksPerCU * (kBlockThreads / kWave);
     // Plain and argmax launches take one row slot instead of two when two
     // would leave at most one tile per wave of a full grid (no next item to
     // overlap), always for the argmax (its vocabulary-sized matrix ran 6%
@@ -83,8 +94,7 @@ hipError_t launch_typed(const RowsParams &p_in, hipStream_t s, int *grid_out) {
     bool one_slot = false;
     if (kOneSlotModes) {
         const int64_t tiles2 = ((int64_t)p.M + 2 * (kWave / G) - 1) / (2 * (kWave / G));
-        one_slot = MODE == kModeArgmax || prefers_one_slot<F>() ||
-                   tiles2 <= (int64_t)device_cu_count() * kMaxBlocksPerCU * waves;
+        one_slot = MODE == kModeArgmax || prefers_one_slot<F>() || tiles2 <= total_waves;
     }
     // stacked modes: the row slots hold rows M apart (gate/up; B/C/x)
     const int64_t rows_per_tile =
@@ -109,9 +119,14 @@ hipError_t launch_typed(const RowsParams &p_in, hipStream_t s, int *grid_out) {
             k = iters == 1 ? kernel_for_ks<F, MODE, 1, kXrModes, 1>(G)
                            : kernel_for_ks<F, MODE, 1, false, 1>(G);
     }
+    if constexpr (MODE == kModeStore) {
+        if (wide)
+            k = one_slot ? kernel_for_ks<F, MODE, 1, false, 1, kWideBlockThreads>(G)
+                         : kernel_for_ks<F, MODE, 1, false, kR, kWideBlockThreads>(G);
+    }
     hipError_t e = ensure_lds((const void *)k, lds);
     if (e != hipSuccess) return e;
-    int per_cu = resident_blocks((const void *)k, kBlockThreads, lds);
+    int per_cu = resident_blocks((const void *)k, bt, lds);
     const bool split = MODE == kModeMoeDown && iters >= waves &&
                        ntiles < 2 * (int64_t)device_cu_count();
     if (split) {
@@ -126,6 +141,7 @@ hipError_t launch_typed(const RowsParams &p_in, hipStream_t s, int *grid_out) {
     // start late and end the launch late, so at most two are used (measured
     // faster at every decode shape).
     if (per_cu > kMaxBlocksPerCU) per_cu = kMaxBlocksPerCU;
+    if (wide) per_cu = 1;
     // persistent grid: at most the workgroups that are resident at once, so
     // no workgroup waits for a second round while compute units idle
     int64_t grid = split ? ntiles : (ntiles + waves - 1) / waves;
@@ -134,7 +150,7 @@ hipError_t launch_typed(const RowsParams &p_in, hipStream_t s, int *grid_out) {
     if (grid > kMaxGrid) grid = kMaxGrid;
     if (grid < 1) grid = 1;
     if (grid_out) *grid_out = (int)grid;
-    return launch_main(k, dim3((unsigned)grid), dim3(kBlockThreads), lds, s, p);
+    return launch_main(k, dim3((unsigned)grid), dim3((unsigned)bt), lds, s, p);
 }
 
 template <int MODE>

@@ -548,7 +548,7 @@ __device__ __forceinline__ void rows_body(const RowsParams &p, const int bid, co
     }
 
     if (MODE == kModeArgmax) {
-        __shared__ uint64_t wave_best[kBlockThreads / kWave];
+        __shared__ uint64_t wave_best[kMaxBlockThreads / kWave];
         uint64_t key = best_i < p.M ? argmax_key(best_v, best_i) : 0ull;
         for (int o = kWave / 2; o > 0; o >>= 1) {
             const uint64_t other = __shfl_xor(key, o, kWave);
@@ -564,8 +564,8 @@ __device__ __forceinline__ void rows_body(const RowsParams &p, const int bid, co
     }
 }
 
-template <class F, int G, int R, int MODE, int KS, bool XR>
-__global__ __launch_bounds__(kBlockThreads) void rows_kernel(RowsParams p) {
+template <class F, int G, int R, int MODE, int KS, bool XR, int BT = kBlockThreads>
+__global__ __launch_bounds__(BT) void rows_kernel(RowsParams p) {
     rows_body<F, G, R, MODE, KS, XR>(p, (int)blockIdx.x, (int)gridDim.x);
 }
 
