@@ -31,7 +31,7 @@ HBM_PEAK_GBS = 8000.0    # MI355X HBM3E peak, 8 TB/s
 # The dominant kernel: the Q4_K row kernel instantiated for K = 4096 (64-lane
 # row groups, 2 row slots, store mode) -- the QKV and gate+up launches (the
 # O launch, 4096 rows, takes the one-slot instantiation).
-DOMINANT = "rows_kernel<qmv::Q4K, 64, 2, 0, 1, true>"
+DOMINANT = "rows_kernel<qmv::Q4K, 64, 2, 0, 1, true, 256>"
 DOMINANT_KINDS = ("qkv", "gate_up")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "rows_kernel_q4k_k4096_decode_step_traffic.txt")
 PROBE_KERNEL = "probe_read"          # streaming-read probe: known bytes read
