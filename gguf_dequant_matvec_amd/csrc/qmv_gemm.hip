@@ -666,11 +666,15 @@ struct XStagePf {
     }
 };
 
-template <class F, int TT>
-__global__ __launch_bounds__(kThreads, 2) void gemm_pf_kernel(GemmParams p, int token_blocks,
+// RT 16-row tiles per wave (a workgroup owns 128 * RT rows): each X
+// fragment read from LDS feeds RT row tiles' MFMAs, and the staged X of a
+// window is shared by 128 * RT rows.
+template <class F, int TT, int RT>
+__global__ __launch_bounds__(kThreads, 4) void gemm_pf_kernel(GemmParams p, int token_blocks,
                                                             int wps) {
     using L = PfLayout<F, TT>;
     constexpr int kPfTiles = TT, kPfTokens = 16 * TT;
+    constexpr int kRows = kRowsPerWG * RT;  // rows per workgroup
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -684,8 +688,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_pf_kernel(GemmParams p, int 
     const int cb = local % cols;
     const int tb = cb % token_blocks, slice = cb / token_blocks;
     const int rg = (b % kXcds) + kXcds * (local / cols);
-    if (rg * kRowsPerWG >= p.M) return;  // padding of the row groups
-    const int row0 = __builtin_amdgcn_readfirstlane(rg * kRowsPerWG + wave * 16);
+    if (rg * kRows >= p.M) return;  // padding of the row groups
+    const int row0 = __builtin_amdgcn_readfirstlane(rg * kRows + wave * 16 * RT);
     const int tok0 = tb * kPfTokens;
     const int nblocks = p.K / 32;
     // this workgroup's windows [w0, wtotal)
@@ -695,7 +699,6 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_pf_kernel(GemmParams p, int 
     const int rows_left = p.M - row0 > 0 ? p.M - row0 : 0;
     const BufSrc src(p.W + (int64_t)row0 * p.row_bytes,
                      (uint64_t)rows_left * (uint64_t)(uint32_t)p.row_bytes);
-    const uint32_t lane_off = (uint32_t)r * (uint32_t)p.row_bytes;
     const BufSrc xview(reinterpret_cast<const uint8_t *>(p.X), (uint64_t)p.n * (uint32_t)p.K * 4u);
 
     auto nvalid_of = [&](int wi) {
@@ -706,21 +709,29 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_pf_kernel(GemmParams p, int 
             return F::kNSub;
         }
     };
-    auto wload = [&](int wi) {
+    using Set = typename F::Regs[RT];
+    auto wload = [&](Set &dst, int wi) {
         wi = __builtin_amdgcn_readfirstlane(wi < wtotal ? wi : wtotal - 1);
-        return F::load(src, lane_off + (uint32_t)wi * F::kWinBytes, q, nvalid_of(wi));
+#pragma unroll
+        for (int rt = 0; rt < RT; rt++)
+            dst[rt] = F::load(src, (uint32_t)(rt * 16 + r) * (uint32_t)p.row_bytes +
+                                       (uint32_t)wi * F::kWinBytes,
+                              q, nvalid_of(wi));
     };
 
     const uint32_t kmask = __builtin_amdgcn_readfirstlane(0x000F000Fu);
     uint32_t kbias;
     asm("v_mov_b32 %0, %1" : "=v"(kbias) : "i"(kB16));
-    f32x4 acc[kPfTiles];
+    f32x4 acc[RT][kPfTiles];
 #pragma unroll
-    for (int tt = 0; tt < kPfTiles; tt++) acc[tt] = {0.f, 0.f, 0.f, 0.f};
+    for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+        for (int tt = 0; tt < kPfTiles; tt++) acc[rt][tt] = {0.f, 0.f, 0.f, 0.f};
 
-    typename F::Regs wcur = wload(w0);
+    Set wcur;
+    wload(wcur, w0);
 
-    auto multiply = [&](const typename F::Regs &w, const uint8_t *base, int wi) {
+    auto multiply = [&](const Set &w, const uint8_t *base, int wi) {
         const __bf16 *xhi = reinterpret_cast<const __bf16 *>(base);
         const __bf16 *xlo = xhi + L::kVals;
         const float *xsum = reinterpret_cast<const float *>(base + 4 * L::kVals);
@@ -730,25 +741,36 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_pf_kernel(GemmParams p, int 
             for (int j0 = 0; j0 < F::kNSub; j0 += 4)
 #pragma unroll
                 for (int tt = 0; tt < kPfTiles; tt++)
-                    acc[tt] = corr_mfma<F>(w, xsum, kPfTokens, tt * 16, j0, r, q, acc[tt]);
+#pragma unroll
+                    for (int rt = 0; rt < RT; rt++)
+                        acc[rt][tt] = corr_mfma<F>(w[rt], xsum, kPfTokens, tt * 16, j0, r, q,
+                                                   acc[rt][tt]);
         }
 #pragma unroll
         for (int j = 0; j < F::kNSub; j++) {
             if (j >= nsub) break;
-            const Frag<F> bcode = F::codes(w, j, kmask, kbias);
-            const float scale = F::scale_of(w, j);
+            Frag<F> bcode[RT];
+            float scale[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; rt++) {
+                bcode[rt] = F::codes(w[rt], j, kmask, kbias);
+                scale[rt] = F::scale_of(w[rt], j);
+            }
 #pragma unroll
             for (int tt = 0; tt < kPfTiles; tt++) {
                 const int fo = ((j * 4 + q) * kPfTokens + tt * 16 + r) * F::kKpl;
                 const Frag<F> ah = *reinterpret_cast<const Frag<F> *>(xhi + fo);
                 const Frag<F> al = *reinterpret_cast<const Frag<F> *>(xlo + fo);
-                f32x4 c = {0.f, 0.f, 0.f, 0.f};
-                c = mfma<F>(ah, bcode, c);
-                c = mfma<F>(al, bcode, c);
-                acc[tt][0] = fmaf(scale, c[0], acc[tt][0]);
-                acc[tt][1] = fmaf(scale, c[1], acc[tt][1]);
-                acc[tt][2] = fmaf(scale, c[2], acc[tt][2]);
-                acc[tt][3] = fmaf(scale, c[3], acc[tt][3]);
+#pragma unroll
+                for (int rt = 0; rt < RT; rt++) {
+                    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+                    c = mfma<F>(ah, bcode[rt], c);
+                    c = mfma<F>(al, bcode[rt], c);
+                    acc[rt][tt][0] = fmaf(scale[rt], c[0], acc[rt][tt][0]);
+                    acc[rt][tt][1] = fmaf(scale[rt], c[1], acc[rt][tt][1]);
+                    acc[rt][tt][2] = fmaf(scale[rt], c[2], acc[rt][tt][2]);
+                    acc[rt][tt][3] = fmaf(scale[rt], c[3], acc[rt][tt][3]);
+                }
                 // keep each tile's operand reads and epilogue next to its
                 // MFMAs (hoisting or sinking them across tiles would need
                 // more registers than a wave has)
@@ -771,34 +793,39 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_pf_kernel(GemmParams p, int 
             xs.store(smem, wi, p.K);
         }
         __syncthreads();
-        typename F::Regs wnext = wload(wn);
+        Set wnext;
+        wload(wnext, wn);
         multiply(wcur, smem, wi);
         __syncthreads();
-        wcur = wnext;
+#pragma unroll
+        for (int rt = 0; rt < RT; rt++) wcur[rt] = wnext[rt];
     }
 
-    const int row = row0 + r;
     float *out = p.slices == 1 ? p.Y : p.partial + (int64_t)slice * p.n * p.M;
-    if (row < p.M) {
 #pragma unroll
-        for (int tt = 0; tt < kPfTiles; tt++)
+    for (int rt = 0; rt < RT; rt++) {
+        const int row = row0 + rt * 16 + r;
+        if (row < p.M) {
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int t = tok0 + tt * 16 + 4 * q + i;
-                if (t < p.n) out[(int64_t)t * p.M + row] = acc[tt][i];
-            }
+            for (int tt = 0; tt < kPfTiles; tt++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int t = tok0 + tt * 16 + 4 * q + i;
+                    if (t < p.n) out[(int64_t)t * p.M + row] = acc[rt][tt][i];
+                }
+        }
     }
 }
 
-template <class F, int TT>
+template <class F, int TT, int RT>
 hipError_t launch_pf_tt(GemmParams p, const PfPlan &plan, hipStream_t s) {
     const size_t lds = (size_t)PfLayout<F, TT>::kBytes;
-    hipError_t e = ensure_lds((const void *)gemm_pf_kernel<F, TT>, lds);
+    hipError_t e = ensure_lds((const void *)gemm_pf_kernel<F, TT, RT>, lds);
     if (e != hipSuccess) return e;
     p.slices = plan.slices;
     const int64_t grid = (int64_t)plan.rg_pad * plan.token_blocks * plan.slices;
     if (grid > 0x7FFFFFFFll) return hipErrorInvalidValue;
-    e = launch_main(gemm_pf_kernel<F, TT>, dim3((unsigned)grid), dim3(kThreads), lds, s, p,
+    e = launch_main(gemm_pf_kernel<F, TT, RT>, dim3((unsigned)grid), dim3(kThreads), lds, s, p,
                     plan.token_blocks, plan.wps);
     if (e != hipSuccess || plan.slices == 1) return e;
     const int64_t nm = (int64_t)p.n * p.M;
@@ -807,13 +834,26 @@ hipError_t launch_pf_tt(GemmParams p, const PfPlan &plan, hipStream_t s) {
     return hipGetLastError();
 }
 
+// formats whose two-tile waves fit the register budget of two workgroups
+// per compute unit
+template <class F>
+constexpr bool two_tiles() {
+    return std::is_same<F, GQ4K>::value || std::is_same<F, GQ5K>::value;
+}
+
 template <class F>
 hipError_t launch_pf(GemmParams p, hipStream_t s) {
-    const PfPlan plan = pf_plan(p.M, p.K, p.n);
+    PfPlan plan = pf_plan(p.M, p.K, p.n);
+    if (plan.rt == 2) {
+        if constexpr (two_tiles<F>()) return launch_pf_tt<F, 4, 2>(p, plan, s);
+        // the same plan with one-tile waves: twice the workgroups, same slices
+        plan.rt = 1;
+        plan.rg_pad = (int)(((p.M + kRowsPerWG - 1) / kRowsPerWG + kXcds - 1) / kXcds * kXcds);
+    }
     switch (plan.tt) {
-    case 4: return launch_pf_tt<F, 4>(p, plan, s);
-    case 2: return launch_pf_tt<F, 2>(p, plan, s);
-    default: return launch_pf_tt<F, 1>(p, plan, s);
+    case 4: return launch_pf_tt<F, 4, 1>(p, plan, s);
+    case 2: return launch_pf_tt<F, 2, 1>(p, plan, s);
+    default: return launch_pf_tt<F, 1, 1>(p, plan, s);
     }
 }
 
@@ -827,12 +867,20 @@ hipError_t launch_pf(GemmParams p, hipStream_t s) {
 PfPlan pf_plan(int64_t M, int64_t K, int64_t n) {
     constexpr int64_t kWant = 512;
     PfPlan pl{};
-    const int64_t row_groups = (M + kRowsPerWG - 1) / kRowsPerWG;
-    pl.rg_pad = (int)((row_groups + kXcds - 1) / kXcds * kXcds);
     const int wtotal = (int)((K + kWin - 1) / kWin);
     auto tblocks = [&](int tt) { return (int)((n + 16 * tt - 1) / (16 * tt)); };
     pl.slices = 1;
     pl.wps = wtotal;
+    // two row tiles per wave (256-row workgroups) when that still gives
+    // enough workgroups with 64 tokens each
+    pl.rt = 2;
+    pl.tt = 4;
+    pl.token_blocks = tblocks(4);
+    pl.rg_pad = (int)(((M + 2 * kRowsPerWG - 1) / (2 * kRowsPerWG) + kXcds - 1) / kXcds * kXcds);
+    if ((int64_t)pl.rg_pad * pl.token_blocks >= kWant) return pl;
+    pl.rt = 1;
+    const int64_t row_groups = (M + kRowsPerWG - 1) / kRowsPerWG;
+    pl.rg_pad = (int)((row_groups + kXcds - 1) / kXcds * kXcds);
     for (int tt = 4; tt >= 1; tt >>= 1) {
         pl.tt = tt;
         pl.token_blocks = tblocks(tt);

@@ -95,10 +95,10 @@ hipError_t launch_moe(const float *x, int64_t H, const float *router, const floa
                       int32_t E, int32_t k, int gu_t, const uint8_t *gate_up, int dn_t,
                       const uint8_t *down, int64_t I, float *y, int32_t *topk_idx,
                       float *topk_w, uint8_t *ws, hipStream_t s);
-// Prefill product plan: tokens per workgroup (16 tt), token blocks, padded
-// row groups, K slices and windows per slice.
+// Prefill product plan: tokens per workgroup (16 tt), 16-row tiles per wave
+// (rt), token blocks, padded row groups, K slices and windows per slice.
 struct PfPlan {
-    int tt, token_blocks, rg_pad, slices, wps;
+    int tt, rt, token_blocks, rg_pad, slices, wps;
 };
 PfPlan pf_plan(int64_t M, int64_t K, int64_t n);
 size_t gemm_workspace(int64_t M, int64_t K, int64_t n);
