@@ -49,6 +49,8 @@ SHAPES = [
     ("q4_k", 1000, 4096, 16),
     ("q5_k", 300, 4096, 100),    # Q5_K: the Q4_K policy plus fifth bits
     ("q5_k", 129, 14336, 20),    # and with K slices
+    ("q4_k", 2048, 256, 4096),   # two 16-row tiles per wave (256-row workgroups)
+    ("q5_k", 2100, 512, 4000),   # the same with a ragged row group and token block
 ]
 
 
