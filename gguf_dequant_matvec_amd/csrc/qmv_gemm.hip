@@ -519,14 +519,15 @@ __global__ __launch_bounds__(256) void gemm_n_reduce(const float *partial, int s
     Y[idx] = s;
 }
 
-// Windows per slice: the largest of 4, 2, 1 that still gives about 1.5
-// workgroups per compute unit of a 256-CU part (the plan depends only on
-// M and K, so the workspace size does too).
+// Windows per slice: the largest of 4, 2, 1 that still gives 512 (128-row
+// group, slice) pairs, two per compute unit of a 256-CU part (measured
+// against 256, 384 and 768: the 32-layer verify pass was 1-3% faster); the
+// plan depends only on M and K, so the workspace size does too.
 int windows_per_slice(int64_t M, int64_t K) {
     const int64_t groups = (M + kRowsPerWG - 1) / kRowsPerWG;
     const int64_t wtotal = (K + kWin - 1) / kWin;
     for (int kw = 4; kw > 1; kw >>= 1)
-        if (groups * ((wtotal + kw - 1) / kw) >= 384) return kw;
+        if (groups * ((wtotal + kw - 1) / kw) >= 512) return kw;
     return 1;
 }
 
@@ -871,13 +872,14 @@ PfPlan pf_plan(int64_t M, int64_t K, int64_t n) {
     auto tblocks = [&](int tt) { return (int)((n + 16 * tt - 1) / (16 * tt)); };
     pl.slices = 1;
     pl.wps = wtotal;
-    // two row tiles per wave (256-row workgroups) when that still gives
-    // enough workgroups with 64 tokens each
+    // two row tiles per wave (256-row workgroups) when that still gives 1.5
+    // workgroups per compute unit with 64 tokens each (n = 256 over the 32
+    // layers: 17.8 ms with a threshold of 2 per compute unit, 16.8 with 1.5)
     pl.rt = 2;
     pl.tt = 4;
     pl.token_blocks = tblocks(4);
     pl.rg_pad = (int)(((M + 2 * kRowsPerWG - 1) / (2 * kRowsPerWG) + kXcds - 1) / kXcds * kXcds);
-    if ((int64_t)pl.rg_pad * pl.token_blocks >= kWant) return pl;
+    if ((int64_t)pl.rg_pad * pl.token_blocks >= kWant * 3 / 4) return pl;
     pl.rt = 1;
     const int64_t row_groups = (M + kRowsPerWG - 1) / kRowsPerWG;
     pl.rg_pad = (int)((row_groups + kXcds - 1) / kXcds * kXcds);
