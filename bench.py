@@ -436,6 +436,18 @@ def extras(torch, q, synth, step, progress):
     us = graph_time_us(torch, [lambda r=r: q.qmv_q8_0(r, M, K, step.x_h, y) for r in reps], reps=5)
     out["q8_0_28672x4096_cold"] = rec(us, b.numel() + 4 * K + 4 * M, replicas=n)
     del reps, b
+    # vocabulary-sized Q8_0 and Q4_K matrices (557 and 295 MB): the per-launch
+    # fixed cost is a few percent of these, so they show the streaming rate
+    M, K = V, Hs
+    y = torch.empty(M, device=dev)
+    for t in ("q8_0", "q4_k"):
+        b = make(t, M, K, synth.T_W, 9)
+        n = max(2, GiB // b.numel() + 1)
+        reps = replicas(b, n)
+        us = graph_time_us(torch, [lambda r=r, t=t: q.qmv(t, r, M, K, step.x_h, y) for r in reps],
+                           reps=3)
+        out[f"{t}_{M}x{K}_cold"] = rec(us, b.numel() + 4 * K + 4 * M, replicas=n)
+        del reps, b
     progress("extras: cold streams done")
     return out
 

@@ -19,8 +19,8 @@
 //   supplies A[l%16][kpl*(l/16) + t], B[kpl*(l/16) + t][l%16] and holds
 //   C[4*(l/16) + i][l%16].
 //
-// Work split: K is cut into slices of KW windows of 256 weights (KW = 1, 2
-// or 4, chosen so that there are enough (128-row group, slice) pairs).  An
+// Work split: K is cut into slices of KW windows of 256 weights (KW = 1 or
+// 2, chosen so that there are enough (128-row group, slice) pairs).  An
 // 8-wave workgroup, one per compute unit, is bound to one slice: it stages X
 // for the slice once in LDS (bf16 hi/lo in the MFMA operand layout plus
 // per-sub-block sums), then each wave streams 16-row tiles (one MFMA tile)
@@ -519,16 +519,17 @@ __global__ __launch_bounds__(256) void gemm_n_reduce(const float *partial, int s
     Y[idx] = s;
 }
 
-// Windows per slice: the largest of 4, 2, 1 that still gives 512 (128-row
-// group, slice) pairs, two per compute unit of a 256-CU part (measured
-// against 256, 384 and 768: the 32-layer verify pass was 1-3% faster); the
+// Windows per slice: 2 if that still gives 512 (128-row group, slice)
+// pairs, two per compute unit of a 256-CU part, else 1 (measured against
+// 256, 384 and 768 pairs: the 32-layer verify pass was 1-3% faster).  Four
+// windows per slice would give fewer slices on large matrices, but their
+// kernel needs 146-227 VGPRs against 64-126 for two: gate+up 28672 x 4096
+// took 32.7-34.5 us with four and 27.5-31.5 us with two (n = 8, 16).  The
 // plan depends only on M and K, so the workspace size does too.
 int windows_per_slice(int64_t M, int64_t K) {
     const int64_t groups = (M + kRowsPerWG - 1) / kRowsPerWG;
     const int64_t wtotal = (K + kWin - 1) / kWin;
-    for (int kw = 4; kw > 1; kw >>= 1)
-        if (groups * ((wtotal + kw - 1) / kw) >= 512) return kw;
-    return 1;
+    return groups * ((wtotal + 1) / 2) >= 512 ? 2 : 1;
 }
 
 // One 8-wave workgroup per compute unit; each slice gets an equal share of
@@ -559,11 +560,7 @@ hipError_t launch_kw(GemmParams p, hipStream_t s) {
 
 template <class F>
 hipError_t launch_typed(const GemmParams &p, hipStream_t s) {
-    switch (windows_per_slice(p.M, p.K)) {
-    case 4: return launch_kw<F, 4>(p, s);
-    case 2: return launch_kw<F, 2>(p, s);
-    default: return launch_kw<F, 1>(p, s);
-    }
+    return windows_per_slice(p.M, p.K) == 2 ? launch_kw<F, 2>(p, s) : launch_kw<F, 1>(p, s);
 }
 
 // ---------------------------------------------------------------------------
