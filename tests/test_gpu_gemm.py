@@ -87,3 +87,36 @@ def test_gemm_n_wide_range_x():
     Yr, Ar = oracle.gemm_n(t, b, M, K, X)
     Y = gemm_gpu(t, dev(b), M, K, X)
     assert_rel(Y.ravel(), Yr.ravel(), Ar.ravel(), what="wide-range X")
+
+
+# Shapes whose plan takes two-window slices (at least 512 (128-row group,
+# slice) pairs): whole windows, an odd window count (the last slice's second
+# window lies past the row's end), a single window, ragged row groups and a
+# Q8_0 row whose last window holds one block.  Checked on sampled rows.
+SHAPES_TWO_WINDOW = [
+    ("q4_k", 16384, 4096, 16), ("q4_k", 65536 + 77, 256, 8), ("q4_k", 16384 + 5, 2304, 3),
+    ("q6_k", 8192, 4096, 8), ("q5_k", 8192 + 100, 4096, 16), ("q8_0", 8192, 4128, 16),
+]
+
+
+def sampled_rows(M, seed, n=300):
+    g = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, 1, M // 2, M - 2, M - 1], g.integers(0, M, n)]))
+
+
+@pytest.mark.parametrize("t,M,K,n", SHAPES_TWO_WINDOW)
+def test_gemm_n_two_window_slices(t, M, K, n):
+    groups, windows = (M + 127) // 128, (K + 255) // 256
+    assert groups * ((windows + 1) // 2) >= 512   # the plan these shapes are chosen for
+    b = quantized(t, M, K, 840 + K)
+    X = synth.activations(841 + K, K, n=n)
+    bd = dev(b)
+    Y = gemm_gpu(t, bd, M, K, X)
+    rows = sampled_rows(M, 842 + K)
+    rb = q.row_bytes(t, K)
+    bs = b.reshape(M, rb)[rows].ravel()
+    Yr, Ar = oracle.gemm_n(t, bs, len(rows), K, X)
+    worst = assert_rel(Y[:, rows].ravel(), Yr.ravel(), Ar.ravel(), what=f"{t} {M}x{K} n={n}")
+    print(f"{t} {M}x{K} n={n} (two-window slices, {len(rows)} rows): worst {worst:.2e}")
+    Y2 = gemm_gpu(t, bd, M, K, X)
+    assert np.array_equal(Y2.view(np.uint32), Y.view(np.uint32))
