@@ -378,7 +378,8 @@ qmv_status qmv_quantize(qmv_type t, const float *w, int64_t M, int64_t K, void *
                         hipStream_t stream) {
     if (!core_type(t)) return QMV_EINVAL;
     if (!w || !blocks_out) return QMV_EINVAL;
-    if (M < 1 || K < 1 || K % block_weights_of(t) != 0) return QMV_ESHAPE;
+    if (M < 1 || K < 1 || K > QMV_MAX_K || K % block_weights_of(t) != 0) return QMV_ESHAPE;
+    if (M > 0x7FFFFFFFll) return QMV_ESHAPE;
     if (!aligned(w, 4)) return QMV_EALIGN;
     return from_hip(launch_quantize(t, w, M, K, (uint8_t *)blocks_out, stream));
 }

@@ -310,9 +310,10 @@ const char *qmv_status_str(qmv_status s);
 qmv_status qmv_time_next_launch(hipEvent_t start, hipEvent_t stop);
 
 /* ---- bandwidth probe (measurement only) -----------------------------------
- * Streams `bytes` (a multiple of 16, buffer 16-byte aligned) with the same
- * 128-bit loads the matvec kernels use and writes one u32 per workgroup into
- * sink (>= 2048 entries); gives the achievable HBM read rate on this device. */
+ * Streams `bytes` (a multiple of 16, buffer 16-byte aligned) in 4 KB chunks
+ * per wave with 128-bit nontemporal loads, the fastest read pattern measured
+ * on this device, and writes one u32 per workgroup into sink (>= 2048
+ * entries); gives the achievable HBM read rate. */
 qmv_status qmv_probe_stream_read(const void *buf, size_t bytes, uint32_t *sink,
                                  hipStream_t stream);
 
