@@ -23,9 +23,9 @@
 // 2, chosen so that there are enough (128-row group, slice) pairs).  An
 // 8-wave workgroup, one per compute unit, is bound to one slice: it stages X
 // for the slice once in LDS (bf16 hi/lo in the MFMA operand layout plus
-// per-sub-block sums), then each wave streams 16-row tiles (one MFMA tile)
-// of the slice, the next tile's weights in flight while the current one is
-// multiplied.  With more than one slice, each writes its partial sums to
+// per-sub-block sums), each wave reads its part of the X fragments into
+// registers once, then streams 16-row tiles (one MFMA tile) of the slice,
+// the next tile's weights in flight while the current one is multiplied.  With more than one slice, each writes its partial sums to
 // the workspace and a second kernel adds them in slice order
 // (deterministic, no atomics).
 #include "qmv_device.h"
@@ -439,6 +439,30 @@ __global__ __launch_bounds__(kThreads) void gemm_n_kernel(GemmParams p, int wg_p
     }
     __syncthreads();
 
+    // The slice's X fragments and activation sums are the same for every row
+    // tile, so each lane reads its part of them from LDS once, into registers
+    // (64 VGPRs per window; one 8-wave workgroup per compute unit is two
+    // waves per SIMD, which leaves room for them: 126-245 VGPRs, no spills),
+    // and the tile loop does no LDS reads.  Gate+up 28672 x 4096 at n = 8, 16:
+    // 27.6 / 30.0 -> 26.6 / 28.7 us per call.
+    Frag<F> xh[KW][F::kNSub], xl[KW][F::kNSub];
+    float xc[KW][F::kNSub / 4];
+#pragma unroll
+    for (int i = 0; i < KW; i++) {
+        const uint8_t *base = smem + (size_t)i * L::kBytes;
+        const __bf16 *xhi = reinterpret_cast<const __bf16 *>(base);
+        const __bf16 *xlo = xhi + L::kVals;
+        const float *xs = reinterpret_cast<const float *>(base + 4 * L::kVals);
+#pragma unroll
+        for (int j = 0; j < F::kNSub; j++) {
+            const int fo = ((j * 4 + q) * kTok + r) * F::kKpl;
+            xh[i][j] = *reinterpret_cast<const Frag<F> *>(xhi + fo);
+            xl[i][j] = *reinterpret_cast<const Frag<F> *>(xlo + fo);
+        }
+#pragma unroll
+        for (int j0 = 0; j0 < F::kNSub; j0 += 4) xc[i][j0 / 4] = -xs[(j0 + q) * kTok + r];
+    }
+
     // code-packing constants in registers (one SGPR, one VGPR)
     const uint32_t kmask = __builtin_amdgcn_readfirstlane(0x000F000Fu);
     uint32_t kbias;
@@ -451,22 +475,17 @@ __global__ __launch_bounds__(kThreads) void gemm_n_kernel(GemmParams p, int wg_p
         for (int i = 0; i < KW; i++) {
             const int wi = wfirst + i;
             if (wi >= wtotal) break;
-            const uint8_t *base = smem + (size_t)i * L::kBytes;
-            const __bf16 *xhi = reinterpret_cast<const __bf16 *>(base);
-            const __bf16 *xlo = xhi + L::kVals;
-            const float *xs = reinterpret_cast<const float *>(base + 4 * L::kVals);
             const int nsub = nvalid_of(wi);
             if constexpr (F::kCorr) {
 #pragma unroll
                 for (int j0 = 0; j0 < F::kNSub; j0 += 4)
-                    acc = corr_mfma<F>(wr[i], xs, kTok, 0, j0, r, q, acc);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                        xc[i][j0 / 4], F::corr_of(wr[i], j0 + q), acc, 0, 0, 0);
             }
 #pragma unroll
             for (int j = 0; j < F::kNSub; j++) {
                 if (j >= nsub) break;
-                const int fo = ((j * 4 + q) * kTok + r) * F::kKpl;
-                const Frag<F> ah = *reinterpret_cast<const Frag<F> *>(xhi + fo);
-                const Frag<F> al = *reinterpret_cast<const Frag<F> *>(xlo + fo);
+                const Frag<F> &ah = xh[i][j], &al = xl[i][j];
                 const Frag<F> b = F::codes(wr[i], j, kmask, kbias);
                 f32x4 c = {0.f, 0.f, 0.f, 0.f};
                 c = mfma<F>(ah, b, c);
