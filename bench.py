@@ -199,7 +199,7 @@ def graph_time_us(torch, fn_list, reps=10):
     return us
 
 
-def extras(torch, q, synth, step, progress):
+def extras(torch, q, synth, step, progress, probe_gbs=None):
     """The other configurations of the path, each cold in HBM: every timed
     loop cycles through >= 1 GiB of distinct weight addresses (replicas), so
     the 256 MiB last-level cache cannot serve them.  Rates are algorithmic
@@ -220,9 +220,10 @@ def extras(torch, q, synth, step, progress):
         return b
 
     def rec(us, nbytes, per="call", **kw):
-        return dict(per=per, us=round(us, 3), bytes=int(nbytes),
-                    gbs=round(nbytes / (us * 1e-6) / 1e9, 1),
-                    pct_of_peak=round(100 * nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1), **kw)
+        gbs = nbytes / (us * 1e-6) / 1e9
+        return dict(per=per, us=round(us, 3), bytes=int(nbytes), gbs=round(gbs, 1),
+                    pct_of_peak=round(100 * gbs / HBM_PEAK_GBS, 1),
+                    pct_of_probe=round(100 * gbs / probe_gbs, 1) if probe_gbs else None, **kw)
 
     # single Q8_0 matvec, 1536 x 576
     c = synth.CONFIG1
@@ -711,7 +712,7 @@ def main():
         },
     }
     if not args.no_extras:
-        rec["extras"] = extras(torch, q, synth, step, progress)
+        rec["extras"] = extras(torch, q, synth, step, progress, probe_gbs)
     if not args.no_cpu_baseline:
         progress("timing the CPU oracle")
         rec["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
