@@ -128,6 +128,7 @@ class DecodeStep:
                 gu=make("q4_k", sum(self.gu_rows), H, 3, l),
                 down=make("q4_k", self.down_shape[0], I, 4, l),
             ))
+        self.out_type = cfg["out_type"]
         self.out = make(cfg["out_type"], self.vocab, H, 5, 0)
         self.x_h = synth.normal_device(seed, 10, (H,), 1.0, dev)
         self.x_i = synth.normal_device(seed, 11, (I,), 1.0, dev)
@@ -308,46 +309,58 @@ def extras(torch, q, synth, step, progress, probe_gbs=None):
     del sets, inp, outp
     progress("extras: short conv done")
 
-    # small-batch verify (n = 8, 16) over the decode-step weights
+    # small-batch verify (n = 8, 16) over the whole decode-step weight set:
+    # the 128 Q4_K layer matrices and the Q6_K 128000 x 4096 output projection
     Hs, Is = step.H, step.I
     mats = []
     for lay in step.layers:
-        mats += [(lay["qkv"], sum(step.qkv_rows), Hs), (lay["o"], step.o_shape[0], Hs),
-                 (lay["gu"], sum(step.gu_rows), Hs), (lay["down"], step.down_shape[0], Is)]
-    wbytes = sum(m.numel() for m, _, _ in mats)
+        mats += [("q4_k", lay["qkv"], sum(step.qkv_rows), Hs), ("q4_k", lay["o"], step.o_shape[0], Hs),
+                 ("q4_k", lay["gu"], sum(step.gu_rows), Hs),
+                 ("q4_k", lay["down"], step.down_shape[0], Is)]
+    mats.append((step.out_type, step.out, step.vocab, Hs))
+    wbytes = sum(m.numel() for _, m, _, _ in mats)
     for nn in (8, 16):
         Xh = synth.normal_device(5, synth.T_X, (nn, Hs), 1.0, dev)
         Xi = synth.normal_device(5, synth.T_XN, (nn, Is), 1.0, dev)
-        Y = torch.empty(nn * sum(step.gu_rows), device=dev)
-        wsb = max(q.qmv_workspace_bytes(q.OP_GEMM_N, M_, K_, nn) for _, M_, K_ in mats)
+        Y = torch.empty(nn * max(M_ for _, _, M_, _ in mats), device=dev)
+        wsb = max(q.qmv_workspace_bytes(q.OP_GEMM_N, M_, K_, nn) for _, _, M_, K_ in mats)
         wsn = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
-        calls = [lambda m=m, M_=M_, K_=K_: q.qmv_gemm_n("q4_k", m, M_, K_, nn,
-                                                       Xh if K_ == Hs else Xi, Y, wsn)
-                 for m, M_, K_ in mats]
-        us = graph_time_us(torch, calls, reps=3) * len(calls)   # per 32-layer pass
-        io = sum(4 * nn * (K_ + M_) for _, M_, K_ in mats)
-        flops = sum(2 * nn * M_ * K_ for _, M_, K_ in mats)
-        r = rec(us, wbytes + io, per=f"32-layer pass ({len(calls)} calls)", n=nn)
+        calls = [lambda t=t, m=m, M_=M_, K_=K_: q.qmv_gemm_n(t, m, M_, K_, nn,
+                                                            Xh if K_ == Hs else Xi, Y, wsn)
+                 for t, m, M_, K_ in mats]
+        us = graph_time_us(torch, calls, reps=3) * len(calls)   # per pass
+        io = sum(4 * nn * (K_ + M_) for _, _, M_, K_ in mats)
+        flops = sum(2 * nn * M_ * K_ for _, _, M_, K_ in mats)
+        r = rec(us, wbytes + io, per=f"decode-step weight set ({len(calls)} calls: 32 layers "
+                                     f"q4_k + q6_k output)", n=nn)
         r["tflops"] = round(flops / (us * 1e-6) / 1e12, 2)
         r["tok_per_s"] = round(nn / (us * 1e-6), 1)
-        out[f"verify_n{nn}_32_layers_q4_k"] = r
+        # per-matrix-kind call times (each kind's calls back to back in a graph)
+        kinds = {}
+        for name, idx in (("qkv", 0), ("o", 1), ("gate_up", 2), ("down", 3)):
+            kinds[name] = round(graph_time_us(torch, calls[idx:-1:4], reps=3), 2)
+        kinds["output_q6_k"] = round(graph_time_us(torch, calls[-1:] * 4, reps=3), 2)
+        r["us_per_call"] = kinds
+        out[f"verify_n{nn}_decode_step_weights"] = r
         del Y, wsn
     progress("extras: verify done")
 
-    # prefill-size product (n = 64, 256, 512) over the same weights
+    # prefill-size product (n = 64, 256, 512) over the 32 layers' weights
+    pmats = [(m, M_, K_) for t, m, M_, K_ in mats if t == "q4_k"]
+    pbytes = sum(m.numel() for m, _, _ in pmats)
     for nn in (64, 256, 512):
         Xh = synth.normal_device(11, synth.T_X, (nn, Hs), 1.0, dev)
         Xi = synth.normal_device(11, synth.T_XN, (nn, Is), 1.0, dev)
         Y = torch.empty(nn * sum(step.gu_rows), device=dev)
-        wsb = max(q.qmv_workspace_bytes(q.OP_GEMM, M_, K_, nn) for _, M_, K_ in mats)
+        wsb = max(q.qmv_workspace_bytes(q.OP_GEMM, M_, K_, nn) for _, M_, K_ in pmats)
         wsp = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
         calls = [lambda m=m, M_=M_, K_=K_: q.qmv_gemm("q4_k", m, M_, K_, nn,
                                                      Xh if K_ == Hs else Xi, Y, wsp)
-                 for m, M_, K_ in mats]
+                 for m, M_, K_ in pmats]
         us = graph_time_us(torch, calls, reps=1) * len(calls)   # per 32-layer pass
-        io = sum(4 * nn * (K_ + M_) for _, M_, K_ in mats)
-        flops = sum(2 * nn * M_ * K_ for _, M_, K_ in mats)
-        r = rec(us, wbytes + io, per=f"32-layer pass ({len(calls)} calls)", n=nn)
+        io = sum(4 * nn * (K_ + M_) for _, M_, K_ in pmats)
+        flops = sum(2 * nn * M_ * K_ for _, M_, K_ in pmats)
+        r = rec(us, pbytes + io, per=f"32-layer pass ({len(calls)} calls)", n=nn)
         r["tflops"] = round(flops / (us * 1e-6) / 1e12, 2)
         r["pct_of_bf16_mfma_peak"] = round(100 * flops / (us * 1e-6) / 2.5e15, 1)
         r["tok_per_s"] = round(nn / (us * 1e-6), 1)

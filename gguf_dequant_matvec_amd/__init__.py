@@ -215,7 +215,14 @@ def qmv_q3_k(blocks, M, K, x, y, stream=None):
     _call("qmv_q3_k", _ptr(blocks), M, K, _ptr(x), _ptr(y), _stream(stream))
 
 
+def _check_segments(seg_rows, y_seg):
+    # the C entry point reads nseg entries of both host arrays
+    if len(seg_rows) != len(y_seg):
+        raise ValueError(f"seg_rows has {len(seg_rows)} entries but y_seg has {len(y_seg)}")
+
+
 def qmv_fused_rows(t, blocks, K, x, seg_rows, y_seg, stream=None):
+    _check_segments(seg_rows, y_seg)
     n = len(seg_rows)
     rows = (ctypes.c_int64 * max(n, 1))(*seg_rows)
     ys = (ctypes.c_void_p * max(len(y_seg), 1))(*[_ptr(y) for y in y_seg])
@@ -226,6 +233,7 @@ def qmv_fused_rows(t, blocks, K, x, seg_rows, y_seg, stream=None):
 def qmv_fused_rows2(t1, blocks1, seg_rows1, y_seg1, t2, blocks2, seg_rows2, y_seg2, K, x,
                     stream=None):
     def arrays(seg_rows, y_seg):
+        _check_segments(seg_rows, y_seg)
         rows = (ctypes.c_int64 * max(len(seg_rows), 1))(*seg_rows)
         ys = (ctypes.c_void_p * max(len(y_seg), 1))(*[_ptr(y) for y in y_seg])
         return rows, ys

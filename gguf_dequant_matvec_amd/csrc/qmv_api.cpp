@@ -21,6 +21,7 @@ thread_local TimingHook g_timing_hook;
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cu_count[kMaxDevices];
 std::mutex g_lds_mutex;
+std::map<std::pair<int, const void *>, size_t> g_lds;  // (device, kernel) -> dynamic LDS limit set
 std::mutex g_occ_mutex;
 std::map<std::pair<const void *, size_t>, int> g_occ;  // (kernel, lds) -> blocks per CU
 
@@ -89,8 +90,15 @@ int resident_blocks(const void *kernel, int threads, size_t lds) {
 
 hipError_t ensure_lds(const void *kernel, size_t bytes) {
     if (bytes <= 64 * 1024) return hipSuccess;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
     std::lock_guard<std::mutex> lock(g_lds_mutex);
-    return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    size_t &done = g_lds[std::make_pair(dev, kernel)];
+    if (done >= bytes) return hipSuccess;
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e == hipSuccess) done = bytes;
+    return e;
 }
 
 }  // namespace qmv
@@ -147,7 +155,7 @@ static qmv_status single(int t, const void *blocks, int64_t M, int64_t K, const 
     qmv_status st = check_matrix(t, blocks, M, K);
     if (st != QMV_OK) return st;
     if (!x || !y) return QMV_EINVAL;
-    if (!aligned(x, 16) || !aligned(y, 4)) return QMV_EALIGN;
+    if (!aligned(x, 4) || !aligned(y, 4)) return QMV_EALIGN;
     SegTable seg{};
     seg.n = 1;
     seg.start[0] = 0;
@@ -240,7 +248,7 @@ qmv_status qmv_fused_rows2(qmv_type t1, const void *blocks1, int32_t nseg1,
     st = check_matrix(t2, blocks2, M2, K);
     if (st != QMV_OK) return st;
     if (!x) return QMV_EINVAL;
-    if (!aligned(x, 16)) return QMV_EALIGN;
+    if (!aligned(x, 4)) return QMV_EALIGN;
     return from_hip(launch_rows_mixed(t1, (const uint8_t *)blocks1, M1, seg1, t2,
                                       (const uint8_t *)blocks2, M2, seg2, K, x, stream));
 }
@@ -255,7 +263,7 @@ qmv_status qmv_fused_rows(qmv_type t, const void *blocks, int64_t K, const float
     st = check_matrix(t, blocks, total, K);
     if (st != QMV_OK) return st;
     if (!x) return QMV_EINVAL;
-    if (!aligned(x, 16)) return QMV_EALIGN;
+    if (!aligned(x, 4)) return QMV_EALIGN;
     return from_hip(launch_rows_store(t, (const uint8_t *)blocks, total, K, x, seg, stream));
 }
 
@@ -267,7 +275,7 @@ qmv_status qmv_gate_up_silu(qmv_type t, const void *blocks, int64_t I, int64_t K
     // the up row of a gate row is addressed by a 32-bit byte offset
     if ((uint64_t)I * row_bytes_of(t, K) > 0x7FFFFFFFull) return QMV_ESHAPE;
     if (!x || !h) return QMV_EINVAL;
-    if (!aligned(x, 16) || !aligned(h, 4)) return QMV_EALIGN;
+    if (!aligned(x, 4) || !aligned(h, 4)) return QMV_EALIGN;
     return from_hip(launch_rows_silu(t, (const uint8_t *)blocks, I, K, x, h, stream));
 }
 
@@ -282,7 +290,7 @@ qmv_status qmv_short_conv(qmv_type in_t, const void *in_proj, int64_t D, int64_t
     // the x row of a channel is 2D rows past its B row (32-bit byte offset)
     if ((uint64_t)2 * D * row_bytes_of(in_t, H) > 0x7FFFFFFFull) return QMV_ESHAPE;
     if (!h || !w_conv || !state || !out) return QMV_EINVAL;
-    if (!aligned(h, 16) || !aligned(w_conv, 4) || !aligned(state, 4) || !aligned(out, 4))
+    if (!aligned(h, 4) || !aligned(w_conv, 4) || !aligned(state, 4) || !aligned(out, 4))
         return QMV_EALIGN;
     if (!workspace || ws_bytes < qmv_workspace_bytes(QMV_OP_SHORT_CONV, D, 0, 0, 0))
         return QMV_EWORKSPACE;
@@ -297,7 +305,7 @@ qmv_status qmv_argmax(qmv_type t, const void *blocks, int64_t M, int64_t K, cons
     qmv_status st = check_matrix(t, blocks, M, K);
     if (st != QMV_OK) return st;
     if (!x || !idx_out || !max_out) return QMV_EINVAL;
-    if (!aligned(x, 16) || !aligned(idx_out, 4) || !aligned(max_out, 4)) return QMV_EALIGN;
+    if (!aligned(x, 4) || !aligned(idx_out, 4) || !aligned(max_out, 4)) return QMV_EALIGN;
     if (!workspace || ws_bytes < qmv_workspace_bytes(QMV_OP_ARGMAX, M, K, 0, 0))
         return QMV_EWORKSPACE;
     if (!aligned(workspace, 8)) return QMV_EALIGN;
@@ -321,7 +329,7 @@ qmv_status moe_qmv_topk(const float *x, int64_t H, const float *router, const fl
     if (st != QMV_OK) return st;
     st = check_matrix(dn_t, down, H, I);
     if (st != QMV_OK) return st;
-    if (!aligned(x, 16) || !aligned(router, 16) || !aligned(bias, 4) || !aligned(y, 4) ||
+    if (!aligned(x, 4) || !aligned(router, 4) || !aligned(bias, 4) || !aligned(y, 4) ||
         !aligned(topk_idx, 4) || !aligned(topk_w, 4))
         return QMV_EALIGN;
     if (!workspace || ws_bytes < qmv_workspace_bytes(QMV_OP_MOE, H, I, E, k))
@@ -340,7 +348,7 @@ qmv_status qmv_gemm_n(qmv_type t, const void *blocks, int64_t M, int64_t K, int3
     if (st != QMV_OK) return st;
     if (n < 1 || n > QMV_MAX_N) return QMV_ESHAPE;
     if (!X || !Y) return QMV_EINVAL;
-    if (!aligned(X, 16) || !aligned(Y, 4)) return QMV_EALIGN;
+    if (!aligned(X, 4) || !aligned(Y, 4)) return QMV_EALIGN;
     const size_t need = gemm_n_workspace(M, K, n);
     if (need > 0 && (!workspace || ws_bytes < need)) return QMV_EWORKSPACE;
     if (need > 0 && !aligned(workspace, 16)) return QMV_EALIGN;
@@ -356,7 +364,7 @@ qmv_status qmv_gemm(qmv_type t, const void *blocks, int64_t M, int64_t K, int64_
     // X is addressed with 32-bit byte offsets
     if ((uint64_t)n * (uint64_t)K * 4u > 0xFFFFFFFFull) return QMV_ESHAPE;
     if (!X || !Y) return QMV_EINVAL;
-    if (!aligned(X, 16) || !aligned(Y, 4)) return QMV_EALIGN;
+    if (!aligned(X, 4) || !aligned(Y, 4)) return QMV_EALIGN;
     const size_t need = gemm_workspace(M, K, n);
     if (need > 0) {
         if (!workspace || ws_bytes < need) return QMV_EWORKSPACE;

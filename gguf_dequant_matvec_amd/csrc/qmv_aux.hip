@@ -378,28 +378,23 @@ hipError_t launch_dequant(int type, const uint8_t *W, int64_t M, int64_t K, floa
     if ((ngroups + 255) / 256 > 0x7FFFFFFFll) return hipErrorInvalidValue;
     const unsigned grid = (unsigned)((ngroups + 255) / 256);
     switch (type) {
-    case kQ80: hipLaunchKernelGGL(dequant_q8_0, dim3(grid), dim3(256), 0, s, W, ngroups, out); break;
-    case kQ4K: hipLaunchKernelGGL(dequant_q4_k, dim3(grid), dim3(256), 0, s, W, ngroups, out); break;
-    case kQ6K: hipLaunchKernelGGL(dequant_q6_k, dim3(grid), dim3(256), 0, s, W, ngroups, out); break;
-    case kQ5K: hipLaunchKernelGGL(dequant_q5_k, dim3(grid), dim3(256), 0, s, W, ngroups, out); break;
-    case kQ2K: hipLaunchKernelGGL(dequant_q2_k, dim3(grid), dim3(256), 0, s, W, ngroups, out); break;
-    case kQ3K: hipLaunchKernelGGL(dequant_q3_k, dim3(grid), dim3(256), 0, s, W, ngroups, out); break;
+    case kQ80: return launch_main(dequant_q8_0, dim3(grid), dim3(256), 0, s, W, ngroups, out);
+    case kQ4K: return launch_main(dequant_q4_k, dim3(grid), dim3(256), 0, s, W, ngroups, out);
+    case kQ6K: return launch_main(dequant_q6_k, dim3(grid), dim3(256), 0, s, W, ngroups, out);
+    case kQ5K: return launch_main(dequant_q5_k, dim3(grid), dim3(256), 0, s, W, ngroups, out);
+    case kQ2K: return launch_main(dequant_q2_k, dim3(grid), dim3(256), 0, s, W, ngroups, out);
+    case kQ3K: return launch_main(dequant_q3_k, dim3(grid), dim3(256), 0, s, W, ngroups, out);
     case kQ40:
-        hipLaunchKernelGGL((dequant_nib32<18, false, 0, 2, 8>), dim3(grid), dim3(256), 0, s, W, ngroups, out);
-        break;
+        return launch_main((dequant_nib32<18, false, 0, 2, 8>), dim3(grid), dim3(256), 0, s, W, ngroups, out);
     case kQ41:
-        hipLaunchKernelGGL((dequant_nib32<20, true, 0, 4, 0>), dim3(grid), dim3(256), 0, s, W, ngroups, out);
-        break;
+        return launch_main((dequant_nib32<20, true, 0, 4, 0>), dim3(grid), dim3(256), 0, s, W, ngroups, out);
     case kQ50:
-        hipLaunchKernelGGL((dequant_nib32<22, false, 2, 6, 16>), dim3(grid), dim3(256), 0, s, W, ngroups, out);
-        break;
+        return launch_main((dequant_nib32<22, false, 2, 6, 16>), dim3(grid), dim3(256), 0, s, W, ngroups, out);
     case kQ51:
-        hipLaunchKernelGGL((dequant_nib32<24, true, 4, 8, 0>), dim3(grid), dim3(256), 0, s, W, ngroups, out);
-        break;
-    case kQ81: hipLaunchKernelGGL(dequant_q8_1, dim3(grid), dim3(256), 0, s, W, ngroups, out); break;
+        return launch_main((dequant_nib32<24, true, 4, 8, 0>), dim3(grid), dim3(256), 0, s, W, ngroups, out);
+    case kQ81: return launch_main(dequant_q8_1, dim3(grid), dim3(256), 0, s, W, ngroups, out);
     default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 hipError_t launch_quantize(int type, const float *w, int64_t M, int64_t K, uint8_t *out,
@@ -408,20 +403,18 @@ hipError_t launch_quantize(int type, const float *w, int64_t M, int64_t K, uint8
     if ((nblocks + 127) / 128 > 0x7FFFFFFFll) return hipErrorInvalidValue;
     const unsigned grid = (unsigned)((nblocks + 127) / 128);
     switch (type) {
-    case kQ80: hipLaunchKernelGGL(quantize_q8_0, dim3(grid), dim3(128), 0, s, w, nblocks, out); break;
-    case kQ4K: hipLaunchKernelGGL(quantize_q4_k, dim3(grid), dim3(128), 0, s, w, nblocks, out); break;
-    case kQ6K: hipLaunchKernelGGL(quantize_q6_k, dim3(grid), dim3(128), 0, s, w, nblocks, out); break;
+    case kQ80: return launch_main(quantize_q8_0, dim3(grid), dim3(128), 0, s, w, nblocks, out);
+    case kQ4K: return launch_main(quantize_q4_k, dim3(grid), dim3(128), 0, s, w, nblocks, out);
+    case kQ6K: return launch_main(quantize_q6_k, dim3(grid), dim3(128), 0, s, w, nblocks, out);
     default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 hipError_t launch_probe(const void *buf, size_t bytes, uint32_t *sink, hipStream_t s) {
     int grid = device_cu_count() * 2;  // two workgroups per compute unit
     if (grid > 2048) grid = 2048;
-    hipLaunchKernelGGL(probe_read, dim3(grid), dim3(256), 0, s, (const uint8_t *)buf, (uint64_t)bytes,
-                       sink);
-    return hipGetLastError();
+    return launch_main(probe_read, dim3(grid), dim3(256), 0, s, (const uint8_t *)buf,
+                       (uint64_t)bytes, sink);
 }
 
 }  // namespace qmv

@@ -572,9 +572,8 @@ hipError_t launch_kw(GemmParams p, hipStream_t s) {
                     per_slice);
     if (e != hipSuccess || p.slices == 1) return e;
     const int64_t nm = (int64_t)p.n * p.M;
-    hipLaunchKernelGGL(gemm_n_reduce, dim3((unsigned)((nm + 255) / 256)), dim3(256), 0, s,
-                       p.partial, p.slices, nm, p.Y);
-    return hipGetLastError();
+    return launch_aux(gemm_n_reduce, dim3((unsigned)((nm + 255) / 256)), dim3(256), 0, s,
+                      (const float *)p.partial, p.slices, nm, p.Y);
 }
 
 template <class F>
@@ -846,9 +845,8 @@ hipError_t launch_pf_tt(GemmParams p, const PfPlan &plan, hipStream_t s) {
                     plan.token_blocks, plan.wps);
     if (e != hipSuccess || plan.slices == 1) return e;
     const int64_t nm = (int64_t)p.n * p.M;
-    hipLaunchKernelGGL(gemm_n_reduce, dim3((unsigned)((nm + 255) / 256)), dim3(256), 0, s,
-                       p.partial, p.slices, nm, p.Y);
-    return hipGetLastError();
+    return launch_aux(gemm_n_reduce, dim3((unsigned)((nm + 255) / 256)), dim3(256), 0, s,
+                      (const float *)p.partial, p.slices, nm, p.Y);
 }
 
 // formats whose two-tile waves fit the register budget of two workgroups

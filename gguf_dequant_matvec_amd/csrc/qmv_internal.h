@@ -6,6 +6,9 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <type_traits>
+
 namespace qmv {
 
 struct SegTable;
@@ -52,17 +55,39 @@ struct TimingHook {
 void set_timing_hook(hipEvent_t start, hipEvent_t stop);
 TimingHook take_timing_hook();
 
-// Launch `kernel`, through hipExtLaunchKernelGGL with the thread's timing
-// events when the hook is armed (the hook is consumed).
+// Enqueue `kernel` and return the status of this enqueue itself (not a
+// sticky error left by an earlier call): the arguments are converted to the
+// kernel's parameter types and passed by address to hipLaunchKernel, or to
+// hipExtLaunchKernel when timing events are given.
+template <typename... KArgs, typename... Args>
+hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds,
+                         hipStream_t s, hipEvent_t start, hipEvent_t stop, Args... args) {
+    static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count");
+    std::tuple<typename std::decay<KArgs>::type...> vals(args...);
+    void *argv[sizeof...(KArgs) > 0 ? sizeof...(KArgs) : 1];
+    std::apply([&](auto &...v) {
+        int i = 0;
+        ((argv[i++] = (void *)&v), ...);
+    }, vals);
+    if (start && stop)
+        return hipExtLaunchKernel((const void *)kernel, grid, block, argv, lds, s, start, stop, 0);
+    return hipLaunchKernel((const void *)kernel, grid, block, argv, lds, s);
+}
+
+// Launch a call's main kernel, with the thread's timing events when the hook
+// is armed (the hook is consumed).
 template <typename Kernel, typename... Args>
 hipError_t launch_main(Kernel kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s,
                        Args... args) {
     TimingHook h = take_timing_hook();
-    if (h.start && h.stop)
-        hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, h.start, h.stop, 0, args...);
-    else
-        hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
-    return hipGetLastError();
+    return launch_kernel(kernel, grid, block, lds, s, h.start, h.stop, args...);
+}
+
+// Launch a helper kernel of a call (never timed).
+template <typename Kernel, typename... Args>
+hipError_t launch_aux(Kernel kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                      Args... args) {
+    return launch_kernel(kernel, grid, block, lds, s, nullptr, nullptr, args...);
 }
 
 // Compute units of the current device (cached per device).

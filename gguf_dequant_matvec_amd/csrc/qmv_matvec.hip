@@ -55,9 +55,8 @@ hipError_t launch_rows_argmax(int type, const uint8_t *W, int64_t M, int64_t K, 
     int grid = 0;
     hipError_t e = launch_fmt<kModeArgmax>(type, p, s, &grid);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(argmax_finalize, dim3(1), dim3(256), 0, s, partials, grid, idx_out,
-                       max_out);
-    return hipGetLastError();
+    return launch_aux(argmax_finalize, dim3(1), dim3(256), 0, s, (const uint64_t *)partials, grid,
+                      idx_out, max_out);
 }
 
 }  // namespace qmv

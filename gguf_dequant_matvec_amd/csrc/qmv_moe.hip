@@ -21,8 +21,10 @@ __global__ __launch_bounds__(256) void router_logits(const float *__restrict__ R
     const float *row = R + (int64_t)e * H;
     float acc = 0.f;
     for (int i = threadIdx.x * 4; i < H; i += 256 * 4) {
-        const float4 r = *reinterpret_cast<const float4 *>(row + i);
-        const float4 v = *reinterpret_cast<const float4 *>(x + i);
+        // x and the router rows need only 4-byte alignment (unaligned
+        // 16-byte global loads are enabled on this device)
+        const float4 r = __builtin_bit_cast(float4, load16(reinterpret_cast<const uint8_t *>(row + i)));
+        const float4 v = __builtin_bit_cast(float4, load16(reinterpret_cast<const uint8_t *>(x + i)));
         acc = fmaf(r.x, v.x, acc);
         acc = fmaf(r.y, v.y, acc);
         acc = fmaf(r.z, v.z, acc);
@@ -45,8 +47,7 @@ hipError_t launch_moe(const float *x, int64_t H, const float *router, const floa
     float *gu = reinterpret_cast<float *>(ws + 256);
     float *h = gu + (int64_t)k * 2 * I;
 
-    hipLaunchKernelGGL(router_logits, dim3(E), dim3(256), 0, s, router, x, (int)H, logits);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_aux(router_logits, dim3(E), dim3(256), 0, s, router, x, (int)H, logits);
     if (e != hipSuccess) return e;
 
     MoeArgs m{};

@@ -34,14 +34,25 @@
  *    stream is synchronised.
  *  - Outputs are overwritten, never accumulated into.  Outputs must not alias
  *    inputs or the workspace.
- *  - Alignment: `x`/`X` must be 16-byte aligned, outputs 4-byte, `blocks`
+ *  - Alignment: activations (`x`, `X`, `h`, the MoE router) and outputs must
+ *    be 4-byte aligned (any f32 element of a tensor may start one), `blocks`
  *    2-byte (so row slices of any matrix are valid; 16-byte-aligned block
- *    buffers stream fastest).
- *  - Errors: every check runs on the host before anything is enqueued; a call
- *    that returns anything but QMV_OK has enqueued nothing.  QMV_EHIP means a
- *    launch failed; qmv_last_hip_error() returns the raw HIP code.  No
- *    exception crosses the ABI.  The library is re-entrant: its only state is
- *    a per-device cache of the compute-unit count and a thread-local error.
+ *    buffers stream fastest), workspaces as stated per call.
+ *  - Errors: every argument check runs on the host before anything is
+ *    enqueued, so a call that returns QMV_EINVAL, QMV_ESHAPE, QMV_EALIGN or
+ *    QMV_EWORKSPACE has enqueued nothing.  QMV_EHIP means that HIP refused a
+ *    launch (each launch's own status is checked); in a call of several
+ *    launches (MoE, argmax, short convolution, split-K products) the
+ *    launches before the failing one may already be enqueued.
+ *    qmv_last_hip_error() returns the raw HIP code.  No exception crosses
+ *    the ABI.
+ *  - Re-entrancy: calls may come from several host threads at once.  The
+ *    library's state is a per-device cache of the compute-unit count, two
+ *    mutex-guarded caches (per-kernel occupancy, and the dynamic-LDS limit
+ *    already raised per kernel and device, so hipFuncSetAttribute runs once
+ *    per kernel and device), and per-thread values (the last HIP error and
+ *    the timing hook below).  Calls on one stream run in order; calls on
+ *    different streams must not share an output or a workspace.
  *  - Shapes: M >= 1, K >= 1, K a multiple of B, K <= QMV_MAX_K.
  */
 #ifndef QMV_H
@@ -277,7 +288,13 @@ qmv_status qmv_gemm(qmv_type t, const void *blocks, int64_t M, int64_t K, int64_
                     float *Y, void *workspace, size_t ws_bytes, hipStream_t stream);
 
 /* ---- dequantise to f32 (verification surface): w_out[M][K] --------------
- * Bit-exact block decoding, the values every matvec above is defined on. */
+ * BebeLM page, section "GGUF加载器" (the loader dequantises Q4_K, Q6_K, F16
+ * and F32 tensors) and section "量化格式支持" (weights are dequantised at run
+ * time, activations stay f32): w_out holds each weight's block decoding,
+ * w = d*q (Q8_0), d*sc*q - dmin*m (Q4_K, one rounding), d*sc*(q - 32) (Q6_K)
+ * and the layouts above for the other formats; every matvec above is defined
+ * on these values.  w_out: f32 M x K row-major (device), 16-byte aligned;
+ * one launch, bit-exact (no f32 rounding except Q4_K's single subtraction). */
 qmv_status qmv_dequant(qmv_type t, const void *blocks, int64_t M, int64_t K, float *w_out,
                        hipStream_t stream);
 

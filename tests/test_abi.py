@@ -100,7 +100,7 @@ def test_pointer_and_type_errors():
     assert status_of(q.qmv_gemm, "q2_k", A16, 4, 256, 64, A16, A16) == "QMV_EINVAL"
     assert status_of(q.qmv_gemm, "q4_k", A16, 4, 256, 0, A16, A16) == "QMV_ESHAPE"
     assert status_of(q.qmv_gemm, "q4_k", A16, 4, 256, q.MAX_PREFILL_N + 1, A16, A16) == "QMV_ESHAPE"
-    assert status_of(q.qmv_gemm, "q4_k", A16, 4, 256, 64, A16 + 4, A16) == "QMV_EALIGN"
+    assert status_of(q.qmv_gemm, "q4_k", A16, 4, 256, 64, A16 + 2, A16) == "QMV_EALIGN"
     # a K-split plan needs its workspace
     need = q.qmv_workspace_bytes(q.OP_GEMM, 256, 14336, 32)
     assert need > 0
@@ -120,14 +120,19 @@ def test_pointer_and_type_errors():
     assert status_of(q.qmv_fused_rows2, "q4_k", A16, [0], [A16], "q6_k", A16, [4], [A16], 256,
                      A16) == "QMV_ESHAPE"
     assert status_of(q.qmv_fused_rows2, "q4_k", A16, [4], [A16], "q6_k", A16, [4], [A16], 256,
-                     A16 + 4) == "QMV_EALIGN"
+                     A16 + 2) == "QMV_EALIGN"
 
 
 def test_alignment_errors():
+    # activations (x, X, h, router) and outputs need 4-byte alignment, blocks 2
     assert status_of(q.qmv_q4_k, A16 + 1, 4, 256, A16, A16) == "QMV_EALIGN"
-    assert status_of(q.qmv_q4_k, A16, 4, 256, A16 + 4, A16) == "QMV_EALIGN"
+    assert status_of(q.qmv_q4_k, A16, 4, 256, A16 + 2, A16) == "QMV_EALIGN"
     assert status_of(q.qmv_q4_k, A16, 4, 256, A16, A16 + 2) == "QMV_EALIGN"
-    assert status_of(q.qmv_gate_up_silu, "q4_k", A16, 8, 256, A16 + 4, A16) == "QMV_EALIGN"
+    assert status_of(q.qmv_gemm_n, "q4_k", A16, 4, 256, 8, A16 + 1, A16, A16, 1 << 20) == \
+        "QMV_EALIGN"
+    assert status_of(q.qmv_argmax, "q6_k", A16, 4, 256, A16 + 2, A16, A16, A16, 1 << 20) == \
+        "QMV_EALIGN"
+    assert status_of(q.qmv_gate_up_silu, "q4_k", A16, 8, 256, A16 + 2, A16) == "QMV_EALIGN"
     assert status_of(q.qmv_gate_up_silu, "q4_k", A16, 8, 256, A16, A16 + 2) == "QMV_EALIGN"
 
 
@@ -154,7 +159,7 @@ def test_workspace_errors():
     # out_proj has D = 100 columns: not a multiple of Q4_K's 256
     assert status_of(q.qmv_short_conv, "q8_0", A16, 100, 256, A16, A16, A16, "q4_k", A16, A16, A16,
                      wc) == "QMV_ESHAPE"
-    assert status_of(q.qmv_short_conv, "q4_k", A16, 2048, 2048, A16 + 4, A16, A16, "q4_k", A16, A16,
+    assert status_of(q.qmv_short_conv, "q4_k", A16, 2048, 2048, A16 + 2, A16, A16, "q4_k", A16, A16,
                      A16, wc) == "QMV_EALIGN"
     assert status_of(q.qmv_short_conv, "q4_k", A16, 2048, 2048, A16, A16, 0, "q4_k", A16, A16, A16,
                      wc) == "QMV_EINVAL"
@@ -162,3 +167,13 @@ def test_workspace_errors():
     assert wg > 0
     assert status_of(q.qmv_gemm_n, "q4_k", A16, 4096, 4096, 16, A16, A16, A16, wg - 4) == \
         "QMV_EWORKSPACE"
+
+
+def test_segment_lists_must_match():
+    # the binding refuses lists of different lengths before calling the library
+    # (it reads nseg entries of both host arrays)
+    with pytest.raises(ValueError):
+        q.qmv_fused_rows("q4_k", A16, 256, A16, [4, 4], [A16], stream=0)
+    with pytest.raises(ValueError):
+        q.qmv_fused_rows2("q4_k", A16, [4], [A16, A16], "q6_k", A16, [4], [A16], 256, A16,
+                          stream=0)

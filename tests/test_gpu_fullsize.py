@@ -124,6 +124,67 @@ def test_llama8b_verify_n16_gate_up():
         assert_rel(Yh[j, rows], yr, ar, what=f"verify column {j}")
 
 
+@pytest.mark.parametrize("n", [8, 16])
+def test_llama8b_verify_output_projection(n):
+    """The Q6_K 128000 x 4096 output projection through the verify product at
+    n = 8 and 16 (the largest matrix of the verify pass), on sampled rows."""
+    V, H = C4["vocab"], C4["hidden"]
+    b, bd = mat("q6_k", V, H, 904)
+    X = synth.activations(930 + n, H, n=n)
+    Y = empty(n * V)
+    ws = empty(max(q.qmv_workspace_bytes(q.OP_GEMM_N, V, H, n), 16), "uint8")
+    q.qmv_gemm_n("q6_k", bd, V, H, n, dev(X), Y, ws)
+    Yh = host(Y).reshape(n, V)
+    rows = sample_rows(V, n=64, seed=940 + n)
+    for j in range(n):
+        yr, ar = oracle.qmv_rows("q6_k", b, V, H, X[j], rows)
+        assert_rel(Yh[j, rows], yr, ar, what=f"q6_k output verify n={n} column {j}")
+
+
+# The largest K the library accepts: x (and its sub-block sums) fill 129-144
+# KB of the 160 KB LDS.  One case per LDS layout of x: Q4_K (64-weight units,
+# sums per 32), Q6_K (sums per 16), Q8_0 in two-block and one-block units
+# (K = 32768 and 32736, an odd block count) and a 32-weight nibble format.
+MAX_K_CASES = [("q4_k", 37, q.MAX_K), ("q6_k", 29, q.MAX_K), ("q8_0", 41, q.MAX_K),
+               ("q8_0", 23, q.MAX_K - 32), ("q4_0", 19, q.MAX_K), ("q5_k", 7, q.MAX_K)]
+
+
+@pytest.mark.parametrize("t,M,K", MAX_K_CASES)
+def test_max_k_single_and_argmax(t, M, K):
+    b, bd = mat(t, M, K, 950 + M)
+    x = synth.activations(951 + M, K)
+    y = empty(M)
+    xd = dev(x)
+    q.qmv(t, bd, M, K, xd, y)
+    yr, ar = oracle.qmv(t, b, M, K, x)                    # every row
+    assert_rel(host(y), yr, ar, what=f"{t} {M}x{K}")
+    idx, mx = empty(1, "int32"), empty(1)
+    ws = empty(q.qmv_workspace_bytes(q.OP_ARGMAX, M, K), "uint8")
+    q.qmv_argmax(t, bd, M, K, xd, idx, mx, ws)
+    yh = host(y)
+    i, v = int(host(idx)[0]), host(mx)[0]
+    # the argmax of the matvec's own row values, bit for bit
+    assert i == int(np.argmax(yh)) and v == yh[i]
+    order = np.argsort(yr)
+    top, second = int(order[-1]), int(order[-2])
+    if yr[top] - yr[second] > 1e-5 * (ar[top] + ar[second]):
+        assert i == top
+
+
+@pytest.mark.parametrize("t,M,n", [("q4_k", 300, 8), ("q6_k", 70, 16), ("q8_0", 50, 5)])
+def test_max_k_verify(t, M, n):
+    K = q.MAX_K
+    b, bd = mat(t, M, K, 960 + M)
+    X = synth.activations(961 + M, K, n=n)
+    Y = empty(n * M)
+    ws = empty(max(q.qmv_workspace_bytes(q.OP_GEMM_N, M, K, n), 16), "uint8")
+    q.qmv_gemm_n(t, bd, M, K, n, dev(X), Y, ws)
+    Yh = host(Y).reshape(n, M)
+    for j in range(n):
+        yr, ar = oracle.qmv(t, b, M, K, X[j])
+        assert_rel(Yh[j], yr, ar, what=f"{t} verify {M}x{K} column {j}")
+
+
 def test_llama1b_decode_matvecs_full():
     H = C2["hidden"]
     check_fused("q4_k", C2["qkv"], H, 910)

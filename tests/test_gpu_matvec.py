@@ -243,3 +243,57 @@ def test_probe_reads_everything():
     q.qmv_probe_stream_read(dev(buf.view(np.uint8)), n, sink)
     got = np.bitwise_xor.reduce(host(sink).view(np.uint32))
     assert got == np.bitwise_xor.reduce(buf)
+
+
+def offset_view(a: np.ndarray):
+    """A device copy of `a` that starts 4 bytes into its allocation: 4-byte but
+    not 16-byte aligned, as a view one f32 into a tensor is."""
+    d = torch.empty(a.size + 1, dtype=torch.float32, device="cuda")
+    v = d[1:]
+    v.copy_(torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32).ravel()))
+    assert v.data_ptr() % 16 != 0 and v.data_ptr() % 4 == 0
+    return v
+
+
+@pytest.mark.parametrize("t,M,K", [("q4_k", 300, 4096), ("q6_k", 97, 1536), ("q8_0", 77, 576),
+                                   ("q8_0", 33, 224), ("q4_0", 40, 14336)])
+def test_activations_at_four_byte_offset(t, M, K):
+    """x needs only 4-byte alignment: the matvec, fused rows and argmax on an
+    x that starts one f32 into its buffer equal the aligned results bit for
+    bit, and match the oracle."""
+    b, x = _case(t, M, K, 700 + M)
+    bd = dev(b)
+    xa, xo = dev(x), offset_view(x)
+    ya, yo = empty(M), empty(M)
+    q.qmv(t, bd, M, K, xa, ya)
+    q.qmv(t, bd, M, K, xo, yo)
+    y_ref, a_ref = oracle.qmv(t, b, M, K, x)
+    assert_rel(host(yo), y_ref, a_ref, what=f"{t} {M}x{K} offset x")
+    assert np.array_equal(host(ya).view(np.uint32), host(yo).view(np.uint32))
+    segs = [M // 2, M - M // 2]
+    ys = [empty(m) for m in segs]
+    q.qmv_fused_rows(t, bd, K, xo, segs, ys)
+    assert np.array_equal(np.concatenate([host(v) for v in ys]).view(np.uint32),
+                          host(ya).view(np.uint32))
+    idx, mx = empty(1, "int32"), empty(1)
+    ws = empty(q.qmv_workspace_bytes(q.OP_ARGMAX, M, K), "uint8")
+    q.qmv_argmax(t, bd, M, K, xo, idx, mx, ws)
+    yh = host(ya)
+    assert int(host(idx)[0]) == int(np.argmax(yh)) and host(mx)[0] == yh.max()
+
+
+def test_verify_and_prefill_at_four_byte_offset():
+    t, M, K = "q4_k", 256, 4096
+    b, _ = _case(t, M, K, 720)
+    bd = dev(b)
+    for n, fn, op in ((8, q.qmv_gemm_n, q.OP_GEMM_N), (40, q.qmv_gemm, q.OP_GEMM)):
+        X = synth.activations(721 + n, K, n=n)
+        Ya, Yo = empty(n * M), empty(n * M)
+        ws = empty(max(q.qmv_workspace_bytes(op, M, K, n), 16), "uint8")
+        fn(t, bd, M, K, n, dev(X), Ya, ws)
+        fn(t, bd, M, K, n, offset_view(X), Yo, ws)
+        assert np.array_equal(host(Ya).view(np.uint32), host(Yo).view(np.uint32)), n
+        Yh = host(Yo).reshape(n, M)
+        for j in (0, n - 1):
+            yr, ar = oracle.qmv(t, b, M, K, X[j])
+            assert_rel(Yh[j], yr, ar, what=f"offset X n={n} column {j}")

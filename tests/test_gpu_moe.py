@@ -177,3 +177,27 @@ def test_moe_small_shapes(E, H, I, k, gu_t, dn_t):
     R = synth.normal(60 + E, synth.T_ROUTER, (E, H), ROUTER_STD)
     b = synth.normal(60 + E, synth.T_BIAS, (E,), synth.BIAS_STD)
     check_moe(ex, x, R, b, k, strict_selection=False)
+
+
+def test_moe_activations_at_four_byte_offset():
+    """x and the router need only 4-byte alignment: inputs that start one f32
+    into their buffers give the aligned call's outputs bit for bit."""
+    ex = experts((3, 32, 2048, 1536, "q4_k", "q6_k"))
+    x, R, b = lfm2_inputs(7)
+    E, H, I, k = ex.E, ex.H, ex.I, 4
+
+    def off(a):
+        d = torch.empty(a.size + 1, dtype=torch.float32, device="cuda")
+        d[1:].copy_(torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32).ravel()))
+        assert d[1:].data_ptr() % 16 == 4
+        return d[1:]
+
+    outs = []
+    for xd, Rd in ((dev(x), dev(R)), (off(x), off(R))):
+        y, idx, w = empty(H), empty(k, "int32"), empty(k)
+        ws = empty(q.qmv_workspace_bytes(q.OP_MOE, H, I, E, k), "uint8")
+        q.moe_qmv_topk(xd, H, Rd, dev(b), E, k, ex.gu_t, ex.gu_d, ex.dn_t, ex.dn_d, I, y, idx, w,
+                       ws)
+        outs.append((host(y).copy(), host(idx).copy(), host(w).copy()))
+    for a, c in zip(*outs):
+        assert np.array_equal(np.asarray(a).view(np.uint32), np.asarray(c).view(np.uint32))
