@@ -51,7 +51,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmv.so")
 # every symbol include/qmv.h declares
 EXPORTS = ["qmv_q8_0", "qmv_q4_k", "qmv_q6_k", "qmv_q4_0", "qmv_q4_1", "qmv_q5_0", "qmv_q5_1",
            "qmv_q8_1", "qmv_q5_k", "qmv_q2_k", "qmv_q3_k", "qmv_fused_rows", "qmv_fused_rows2",
-           "qmv_gate_up_silu", "qmv_short_conv", "qmv_argmax", "moe_qmv_topk", "qmv_gemm_n", "qmv_gemm", "qmv_dequant",
+           "qmv_gate_up_silu", "qmv_short_conv", "qmv_argmax", "qmv_argmax_noalloc", "moe_qmv_topk", "qmv_gemm_n", "qmv_gemm", "qmv_dequant",
            "qmv_quantize", "qmv_row_bytes", "qmv_workspace_bytes", "qmv_last_hip_error",
            "qmv_status_str", "qmv_probe_stream_read", "qmv_time_next_launch"]
 
@@ -98,6 +98,7 @@ def load():
         "qmv_gate_up_silu": [ci, P, i64, i64, P, P, P],
         "qmv_short_conv": [ci, P, i64, i64, P, P, P, ci, P, P, P, sz, P],
         "qmv_argmax": [ci, P, i64, i64, P, P, P, P, sz, P],
+        "qmv_argmax_noalloc": [ci, P, i64, i64, P, P, P, P],
         "moe_qmv_topk": [P, i64, P, P, i32, i32, ci, P, ci, P, i64, P, P, P, P, sz, P],
         "qmv_gemm_n": [ci, P, i64, i64, i32, P, P, P, sz, P],
         "qmv_gemm": [ci, P, i64, i64, i64, P, P, P, sz, P],
@@ -262,6 +263,11 @@ def qmv_argmax(t, blocks, M, K, x, idx_out, max_out, workspace, ws_bytes=None, s
         ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _call("qmv_argmax", _type(t), _ptr(blocks), M, K, _ptr(x), _ptr(idx_out), _ptr(max_out),
           _ptr(workspace), ws_bytes, _stream(stream))
+
+
+def qmv_argmax_noalloc(t, blocks, M, K, x, idx_out, max_out, stream=None):
+    _call("qmv_argmax_noalloc", _type(t), _ptr(blocks), M, K, _ptr(x), _ptr(idx_out),
+          _ptr(max_out), _stream(stream))
 
 
 def moe_qmv_topk(x, H, router, bias, E, k, gu_t, gate_up, dn_t, down, I, y, topk_idx, topk_w,

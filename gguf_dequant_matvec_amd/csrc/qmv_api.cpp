@@ -313,6 +313,17 @@ qmv_status qmv_argmax(qmv_type t, const void *blocks, int64_t M, int64_t K, cons
                                        (uint64_t *)workspace, idx_out, max_out, stream));
 }
 
+qmv_status qmv_argmax_noalloc(qmv_type t, const void *blocks, int64_t M, int64_t K,
+                              const float *x, int32_t *idx_out, float *max_out,
+                              hipStream_t stream) {
+    qmv_status st = check_matrix(t, blocks, M, K);
+    if (st != QMV_OK) return st;
+    if (!x || !idx_out || !max_out) return QMV_EINVAL;
+    if (!aligned(x, 4) || !aligned(idx_out, 4) || !aligned(max_out, 4)) return QMV_EALIGN;
+    return from_hip(launch_rows_argmax_noalloc(t, (const uint8_t *)blocks, M, K, x, idx_out,
+                                               max_out, stream));
+}
+
 qmv_status moe_qmv_topk(const float *x, int64_t H, const float *router, const float *bias,
                         int32_t E, int32_t k, qmv_type gu_t, const void *gate_up,
                         qmv_type dn_t, const void *down, int64_t I, float *y,

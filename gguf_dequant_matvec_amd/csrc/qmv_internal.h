@@ -111,6 +111,10 @@ hipError_t launch_short_conv(int in_t, const uint8_t *in_proj, int64_t D, int64_
 hipError_t launch_rows_argmax(int type, const uint8_t *W, int64_t M, int64_t K, const float *x,
                               uint64_t *partials, int32_t *idx_out, float *max_out,
                               hipStream_t s);
+// qmv_argmax with its per-workgroup keys in a device-global array.
+hipError_t launch_rows_argmax_noalloc(int type, const uint8_t *W, int64_t M, int64_t K,
+                                      const float *x, int32_t *idx_out, float *max_out,
+                                      hipStream_t s);
 hipError_t launch_dequant(int type, const uint8_t *W, int64_t M, int64_t K, float *out,
                           hipStream_t s);
 hipError_t launch_quantize(int type, const float *w, int64_t M, int64_t K, uint8_t *out,

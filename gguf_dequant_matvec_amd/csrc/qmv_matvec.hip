@@ -1,9 +1,24 @@
 // Single-token, fused-row and argmax launches of the row-streaming kernel.
+#include "qmv.h"
 #include "qmv_launch.h"
+
+#include <mutex>
 
 namespace qmv {
 
 namespace {
+
+// Scratch of qmv_argmax_noalloc: the per-workgroup (value, index) keys of one
+// argmax launch, whose grid never exceeds kMaxGrid workgroups.  A device
+// global (16 KiB), so every GPU the library runs on holds its own copy until
+// the process ends and no call allocates.  In host code `scratch` names a
+// host-side stand-in, not device memory: kernels get the device address that
+// hipGetSymbolAddress returns for the current device (scratch_of_device).
+__device__ __align__(256) uint64_t scratch[kMaxGrid];
+
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mutex;
+uint64_t *g_scratch_ptr[kScratchDevices];
 
 __global__ __launch_bounds__(256) void argmax_finalize(const uint64_t *partials, int n,
                                                        int32_t *idx_out, float *max_out) {
@@ -57,6 +72,36 @@ hipError_t launch_rows_argmax(int type, const uint8_t *W, int64_t M, int64_t K, 
     if (e != hipSuccess) return e;
     return launch_aux(argmax_finalize, dim3(1), dim3(256), 0, s, (const uint64_t *)partials, grid,
                       idx_out, max_out);
+}
+
+// Device address of this device's scratch array, looked up once per device
+// (with that device current) and kept.
+static hipError_t scratch_of_device(uint64_t **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = static_cast<uint64_t *>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+hipError_t launch_rows_argmax_noalloc(int type, const uint8_t *W, int64_t M, int64_t K,
+                                      const float *x, int32_t *idx_out, float *max_out,
+                                      hipStream_t s) {
+    // the argmax launch caps its grid at kMaxGrid, one key per workgroup
+    static_assert(sizeof(scratch) == (size_t)kMaxGrid * sizeof(uint64_t), "one key per workgroup");
+    static_assert(kMaxGrid == QMV_ARGMAX_SCRATCH_KEYS, "the documented scratch size");
+    uint64_t *keys = nullptr;
+    hipError_t e = scratch_of_device(&keys);
+    if (e != hipSuccess) return e;
+    return launch_rows_argmax(type, W, M, K, x, keys, idx_out, max_out, s);
 }
 
 }  // namespace qmv

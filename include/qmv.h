@@ -232,6 +232,25 @@ qmv_status qmv_argmax(qmv_type t, const void *blocks, int64_t M, int64_t K, cons
                       int32_t *idx_out, float *max_out, void *workspace, size_t ws_bytes,
                       hipStream_t stream);
 
+/* ---- qmv_argmax without a workspace ---------------------------------------
+ * For callers that cannot allocate device memory at all (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same result as qmv_argmax -- the same kernels, bit for bit -- with the
+ * per-workgroup keys kept in a library-owned device array instead of a
+ * workspace.  That array holds QMV_ARGMAX_SCRATCH_KEYS keys (16 KiB), the
+ * most an argmax launch uses for any M and K; each GPU the library runs on
+ * holds its own copy until the process ends, and its address is looked up
+ * once per device on the first call there.  The call allocates nothing on
+ * the device and needs nothing zeroed (every key the finalising kernel reads
+ * is written by the same call); the array keeps the last call's keys.  All
+ * calls on one GPU share the array: calls that overlap on one GPU (on
+ * different streams without ordering between them) race.  Arguments,
+ * limits and errors as qmv_argmax. */
+#define QMV_ARGMAX_SCRATCH_KEYS 2048
+qmv_status qmv_argmax_noalloc(qmv_type t, const void *blocks, int64_t M, int64_t K,
+                              const float *x, int32_t *idx_out, float *max_out,
+                              hipStream_t stream);
+
 /* ---- sigmoid-routed top-k MoE FFN for one token ---------------------------
  * BebeLM page, section "核心算子" (MoE FFN): router scores are sigmoids
  * (not a softmax); the k experts with the largest score + bias are chosen
