@@ -80,6 +80,7 @@ constexpr int kDppXor1 = 0xB1;          // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;          // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141;   // lane 7 - i within each 8
 constexpr int kDppMirror = 0x140;       // lane 15 - i within each 16
+constexpr int kDppRowRor8 = 0x128;      // lane (i + 8) mod 16 within each 16
 constexpr int kDppBcast15 = 0x142;      // lane 15 of row r to row r + 1
 constexpr int kDppBcast31 = 0x143;      // lane 31 to rows 2 and 3
 

@@ -136,5 +136,9 @@ hipError_t launch_gemm(int type, const uint8_t *W, int64_t M, int64_t K, int64_t
 hipError_t launch_gemm_n(int type, const uint8_t *W, int64_t M, int64_t K, int32_t n,
                          const float *X, float *Y, void *ws, hipStream_t s);
 size_t gemm_n_workspace(int64_t M, int64_t K, int32_t n);
+// Y[t][i] = sum over K slices of partial[slice][t][i] (nm = n * M outputs), in
+// slice order: the second launch of K-split products.
+hipError_t launch_slice_reduce(const float *partial, int slices, int64_t nm, float *Y,
+                               hipStream_t s);
 
 }  // namespace qmv

@@ -282,10 +282,15 @@ qmv_status moe_qmv_topk(const float *x, int64_t H, const float *router, const fl
  * Q4_K, Q5_K, Q6_K.  Runs on the matrix
  * cores (bf16 MFMA on the exact integer codes, X split into bf16 hi + lo, f32
  * scales), within 1e-5 * sum_k |w_ik x_k| of the exact result like the
- * matvecs.  workspace: device, >= qmv_workspace_bytes(QMV_OP_GEMM_N, M, K, n,
- * 0) bytes (may be 0 bytes, then NULL is allowed), 16-byte aligned, no
- * initial contents needed; K is split into slices whose partial sums are
- * added in a fixed order, so results are deterministic. */
+ * matvecs.  One launch when K <= 4096: a workgroup covers all of K for its
+ * rows (its waves split K and add their partial products in a fixed order),
+ * and the workspace size is 0.  Longer K is cut into slices of at most 4096
+ * weights whose partial sums go to the workspace and are added in slice
+ * order by a second launch.  workspace: device, >=
+ * qmv_workspace_bytes(QMV_OP_GEMM_N, M, K, n, 0) bytes (NULL when that is
+ * 0), 16-byte aligned, no initial contents needed.  Results are
+ * deterministic; n <= 8 and 8 < n <= 16 use two operand layouts, so a
+ * column's bits may differ between the two ranges (both within the bound). */
 qmv_status qmv_gemm_n(qmv_type t, const void *blocks, int64_t M, int64_t K, int32_t n,
                       const float *X, float *Y, void *workspace, size_t ws_bytes,
                       hipStream_t stream);

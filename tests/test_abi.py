@@ -163,9 +163,13 @@ def test_workspace_errors():
                      A16, wc) == "QMV_EALIGN"
     assert status_of(q.qmv_short_conv, "q4_k", A16, 2048, 2048, A16, A16, 0, "q4_k", A16, A16, A16,
                      wc) == "QMV_EINVAL"
-    wg = q.qmv_workspace_bytes(q.OP_GEMM_N, 4096, 4096, 16)
-    assert wg > 0
-    assert status_of(q.qmv_gemm_n, "q4_k", A16, 4096, 4096, 16, A16, A16, A16, wg - 4) == \
+    # the verify product needs a workspace only when K is split (K > 4096)
+    assert q.qmv_workspace_bytes(q.OP_GEMM_N, 4096, 4096, 16) == 0
+    assert q.qmv_workspace_bytes(q.OP_GEMM_N, 28672, 4096, 8) == 0
+    wg = q.qmv_workspace_bytes(q.OP_GEMM_N, 4096, 14336, 16)
+    assert wg == 4 * 16 * 4096 * 4      # four slices of 14 windows
+    assert q.qmv_workspace_bytes(q.OP_GEMM_N, 100, q.MAX_K, 5) == 8 * 5 * 100 * 4
+    assert status_of(q.qmv_gemm_n, "q4_k", A16, 4096, 14336, 16, A16, A16, A16, wg - 4) == \
         "QMV_EWORKSPACE"
 
 

@@ -6,7 +6,8 @@ so the representation error is <= 2^-18 |x| per product, plus f32
 accumulation: within the matvec's 1e-5 * sum_k |w_ik X[j][k]| per output.
 Also: n = 1 matches the matvec within the bound; permuting X's rows permutes
 Y's rows bit for bit (each token is an independent MFMA row); two runs are
-identical (split-K partial sums are added in a fixed order).
+identical (the waves' and the K slices' partial sums are added in a fixed
+order).
 """
 import numpy as np
 import pytest
@@ -39,6 +40,7 @@ SHAPES = [
     ("q6_k", 200, 1536, 16), ("q6_k", 77, 4096, 3), ("q6_k", 500, 4096, 8),
     ("q8_0", 100, 576, 16), ("q8_0", 37, 224, 5), ("q8_0", 300, 4096, 16), ("q8_0", 17, 32, 2),
     ("q5_k", 300, 4096, 16), ("q5_k", 129, 2048, 7), ("q5_k", 1000, 14336, 16),
+    ("q4_k", 50, 4096, 1), ("q4_k", 333, 4096, 9), ("q6_k", 64, 1536, 1), ("q8_0", 70, 4096, 8),
 ]
 
 
@@ -67,16 +69,17 @@ def test_gemm_n_one_column_matches_matvec():
 
 @pytest.mark.parametrize("t", ["q4_k", "q5_k", "q6_k", "q8_0"])
 def test_gemm_n_token_permutation_and_determinism(t):
-    M, K, n = 333, 4096, 16
+    M, K = 333, 4096
     b = quantized(t, M, K, 820)
-    X = synth.activations(821, K, n=n)
     bd = dev(b)
-    Y = gemm_gpu(t, bd, M, K, X)
-    perm = np.random.default_rng(5).permutation(n)
-    Yp = gemm_gpu(t, bd, M, K, X[perm])
-    assert np.array_equal(Yp.view(np.uint32), Y[perm].view(np.uint32))
-    Y2 = gemm_gpu(t, bd, M, K, X)
-    assert np.array_equal(Y2.view(np.uint32), Y.view(np.uint32))
+    for n in (16, 8):             # both operand layouts
+        X = synth.activations(821 + n, K, n=n)
+        Y = gemm_gpu(t, bd, M, K, X)
+        perm = np.random.default_rng(5).permutation(n)
+        Yp = gemm_gpu(t, bd, M, K, X[perm])
+        assert np.array_equal(Yp.view(np.uint32), Y[perm].view(np.uint32)), n
+        Y2 = gemm_gpu(t, bd, M, K, X)
+        assert np.array_equal(Y2.view(np.uint32), Y.view(np.uint32)), n
 
 
 def test_gemm_n_wide_range_x():
@@ -89,13 +92,19 @@ def test_gemm_n_wide_range_x():
     assert_rel(Y.ravel(), Yr.ravel(), Ar.ravel(), what="wide-range X")
 
 
-# Shapes whose plan takes two-window slices (at least 512 (128-row group,
-# slice) pairs): whole windows, an odd window count (the last slice's second
-# window lies past the row's end), a single window, ragged row groups and a
-# Q8_0 row whose last window holds one block.  Checked on sampled rows.
-SHAPES_TWO_WINDOW = [
+# Shapes that take each part of the launch plan (windows of 256 weights;
+# waves per tile along K = the largest power of two <= the windows, at most
+# 8; one or two windows per wave; K slices only past 16 windows): one window
+# (ks = 1, eight tiles per group), 5 windows (ks = 4), 9 windows (one wave
+# with two, seven with one), 16 windows (ks = 8, many tiles per workgroup,
+# batches of four), a Q8_0 row whose last window holds one block and that
+# splits into two K slices, a Q8_0 row of 23 blocks, n = 9 (the first n of
+# the two-MFMA layout) and ragged row counts.  Checked on sampled rows, and
+# repeated runs are bit-identical.
+SHAPES_PLAN = [
     ("q4_k", 16384, 4096, 16), ("q4_k", 65536 + 77, 256, 8), ("q4_k", 16384 + 5, 2304, 3),
     ("q6_k", 8192, 4096, 8), ("q5_k", 8192 + 100, 4096, 16), ("q8_0", 8192, 4128, 16),
+    ("q4_k", 2000 + 3, 1280, 9), ("q8_0", 3000 + 1, 736, 4), ("q6_k", 1000, 6144, 12),
 ]
 
 
@@ -104,10 +113,8 @@ def sampled_rows(M, seed, n=300):
     return np.unique(np.concatenate([[0, 1, M // 2, M - 2, M - 1], g.integers(0, M, n)]))
 
 
-@pytest.mark.parametrize("t,M,K,n", SHAPES_TWO_WINDOW)
-def test_gemm_n_two_window_slices(t, M, K, n):
-    groups, windows = (M + 127) // 128, (K + 255) // 256
-    assert groups * ((windows + 1) // 2) >= 512   # the plan these shapes are chosen for
+@pytest.mark.parametrize("t,M,K,n", SHAPES_PLAN)
+def test_gemm_n_launch_plans(t, M, K, n):
     b = quantized(t, M, K, 840 + K)
     X = synth.activations(841 + K, K, n=n)
     bd = dev(b)
@@ -117,6 +124,6 @@ def test_gemm_n_two_window_slices(t, M, K, n):
     bs = b.reshape(M, rb)[rows].ravel()
     Yr, Ar = oracle.gemm_n(t, bs, len(rows), K, X)
     worst = assert_rel(Y[:, rows].ravel(), Yr.ravel(), Ar.ravel(), what=f"{t} {M}x{K} n={n}")
-    print(f"{t} {M}x{K} n={n} (two-window slices, {len(rows)} rows): worst {worst:.2e}")
+    print(f"{t} {M}x{K} n={n} ({len(rows)} sampled rows): worst {worst:.2e}")
     Y2 = gemm_gpu(t, bd, M, K, X)
     assert np.array_equal(Y2.view(np.uint32), Y.view(np.uint32))

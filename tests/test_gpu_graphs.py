@@ -63,20 +63,21 @@ def replay_check(fn, inputs, outputs, seeds, make_input, noise):
         torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("kind,t,M,K,n", [
-    ("verify", "q4_k", 1000, 14336, 16),     # 14 K slices + reduce
-    ("verify", "q6_k", 500, 4096, 8),
-    ("prefill", "q4_k", 256, 14336, 32),     # K split (small M, few tokens)
-    ("prefill", "q5_k", 129, 4096, 70),
+@pytest.mark.parametrize("kind,t,M,K,n,split", [
+    ("verify", "q4_k", 1000, 14336, 16, True),     # 4 K slices + reduce
+    ("verify", "q6_k", 500, 8192, 8, True),        # 2 K slices + reduce
+    ("verify", "q4_k", 3000, 4096, 8, False),      # one launch
+    ("prefill", "q4_k", 256, 14336, 32, True),     # K split (small M, few tokens)
+    ("prefill", "q5_k", 129, 4096, 70, True),
 ])
-def test_split_products_replay(kind, t, M, K, n):
+def test_split_products_replay(kind, t, M, K, n, split):
     b = dev(quantized(t, M, K, 1500 + M))
     X = dev(synth.activations(1501, K, n=n))
     Y = empty(n * M)
     op = q.OP_GEMM_N if kind == "verify" else q.OP_GEMM
     wsb = q.qmv_workspace_bytes(op, M, K, n)
-    assert wsb > 0                                       # a K split, so two launches
-    ws = empty(wsb, "uint8")
+    assert (wsb > 0) == split                            # a K split: two launches
+    ws = empty(max(wsb, 16), "uint8")
     other = empty(M)
     x1 = dev(synth.activations(1502, K))
 
