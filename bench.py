@@ -668,6 +668,16 @@ def summarize(dirs):
         probe = mean.get((PROBE_KERNEL, "FETCH_SIZE"))
         wcal = mean.get((CAL_WRITE_KERNEL, "WRITE_SIZE"))
         fd, wd = mean.get((dom_name, "FETCH_SIZE")), mean.get((dom_name, "WRITE_SIZE"))
+        if probe and wcal:
+            ff = PROBE_BYTES / probe
+            wf = 4096 * 4096 * 4 / wcal
+            kernels = sorted({k for k, _ in vals})
+            print("calibrated HBM bytes per dispatch: kernel, fetch, write, fetch+write")
+            for k in kernels:
+                f_, w_ = mean.get((k, "FETCH_SIZE")), mean.get((k, "WRITE_SIZE"))
+                if f_ is None or w_ is None:
+                    continue
+                print(f"  {k[:72]:72s} {f_ * ff:14.0f} {w_ * wf:12.0f} {f_ * ff + w_ * wf:14.0f}")
         if probe and wcal and fd is not None and wd is not None:
             ff = PROBE_BYTES / probe
             wf = 4096 * 4096 * 4 / wcal
@@ -850,6 +860,12 @@ def main():
             "us_per_launch": round(dom_ms * 1e3, 3),
             "us_per_launch_in_graph": round(dom_graph_us, 3),
             "frac_of_probe": round(achieved / probe_gbs, 4) if probe_gbs else None,
+            # the two shapes behind the blend, each on its own
+            "per_kind": {k: dict(us_per_launch=breakdown[k]["us_per_launch"],
+                                 algorithmic_bytes_per_launch=breakdown[k]["bytes_per_launch"],
+                                 gbs=breakdown[k]["gbs"],
+                                 frac=round(breakdown[k]["gbs"] / HBM_PEAK_GBS, 4))
+                         for k in DOMINANT_KINDS},
         },
     }
     if not args.no_extras:

@@ -119,9 +119,8 @@ struct XStagePf {
             const int pos = ((j * 4 + q) * kPfTokens + t) * F::kKpl;
             *reinterpret_cast<BFrag<F> *>(base + 2 * pos) = __builtin_bit_cast(BFrag<F>, hi);
             *reinterpret_cast<BFrag<F> *>(base + 2 * (L::kVals + pos)) = __builtin_bit_cast(BFrag<F>, lo);
-            // lane groups q = 0..3 of (j, t) are lanes tl, tl + 16, tl + 32, tl + 48
-            sum += __shfl_xor(sum, 16, kWave);
-            sum += __shfl_xor(sum, 32, kWave);
+            // lane groups q = 0..3 of (j, t) are the four 16-lane rows
+            sum = rows_sum(sum);
             if (q == 0) reinterpret_cast<float *>(base + 4 * L::kVals)[j * kPfTokens + t] = sum;
         }
     }
@@ -263,16 +262,22 @@ __global__ __launch_bounds__(kThreads, 4) void gemm_pf_kernel(GemmParams p, int 
     }
 
     float *out = p.slices == 1 ? p.Y : p.partial + (int64_t)slice * p.n * p.M;
+    // The output offsets only depend on the launch: formed here, after the
+    // loop (the empty asm keeps the compiler from computing them up front
+    // and holding them in registers through the multiply loop).
+    int row_l = row0 + r, tok_l = tok0 + 4 * q;
+    asm volatile("" : "+v"(row_l), "+v"(tok_l));
 #pragma unroll
     for (int rt = 0; rt < RT; rt++) {
-        const int row = row0 + rt * 16 + r;
+        const int row = row_l + rt * 16;
         if (row < p.M) {
+            float *yr = out + row;
 #pragma unroll
             for (int tt = 0; tt < kPfTiles; tt++)
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
-                    const int t = tok0 + tt * 16 + 4 * q + i;
-                    if (t < p.n) out[(int64_t)t * p.M + row] = acc[rt][tt][i];
+                    const int t = tok_l + tt * 16 + i;
+                    if (t < p.n) yr[(int64_t)t * p.M] = acc[rt][tt][i];
                 }
         }
     }

@@ -51,7 +51,7 @@ hipError_t launch_typed(const RowsParams &p_in, hipStream_t s, int *grid_out) {
     }
     // stacked modes: the row slots hold rows M apart (gate/up; B/C/x)
     const int64_t rows_per_tile =
-        (MODE == kModeSiluUp || MODE == kModeShortConv || one_slot ? 1
+        (MODE == kModeSiluUp || MODE == kModeShortConv || MODE == kModeMoeGateUp || one_slot ? 1
                                                                    : (int64_t)rows_per_lane<MODE>()) *
         (kWave / G);
     const int64_t ntiles = ((int64_t)p.M + rows_per_tile - 1) / rows_per_tile;

@@ -3,9 +3,10 @@
 //   1. router: logits r_e = R[e, :] . x in f32, one workgroup per expert;
 //   2. gate/up: every workgroup derives the selection (sigmoid, biased top-k,
 //      renormalised weights) from the logits, then streams the selected
-//      experts' gate and up rows into the workspace;
-//   3. down: x' = concat_s(w_s * silu(g_s) * u_s) and row i = concat_s(D_s[i])
-//      give y[i] = sum_s w_s D_s[i] . h_s in one fixed-order row sum.
+//      experts' gate and up rows, each gate row with its up row, and writes
+//      g, u and h = silu(g) * u into the workspace;
+//   3. down: x' = concat_s(w_s * h_s) and row i = concat_s(D_s[i]) give
+//      y[i] = sum_s w_s D_s[i] . h_s in one fixed-order row sum.
 // Workspace layout (bytes): [0, 256) f32 logits[E]; [256, ...) f32
 // gu[k][2I] (gate rows then up rows per slot); then f32 h[k][I].
 #include "qmv_launch.h"
@@ -57,13 +58,12 @@ hipError_t launch_moe(const float *x, int64_t H, const float *router, const floa
     m.k = k;
     m.topk_idx = topk_idx;
     m.topk_w = topk_w;
-    m.gu = gu;
     m.h = h;
     m.I = (int32_t)I;
 
     RowsParams pg{};
     pg.W = gate_up;
-    pg.M = (int32_t)(k * 2 * I);
+    pg.M = (int32_t)(k * I);  // row pairs (gate row j, up row j)
     pg.K = (int32_t)H;
     pg.row_bytes = (int64_t)row_bytes_of(gu_t, H);
     pg.x = x;

@@ -17,15 +17,18 @@
 //
 // MoE modes (BebeLM page, section "核心算子": sigmoid router, top-k experts,
 // bias used only to select, weights renormalised):
-//  - kModeMoeGateUp: rows are the gate/up rows of the k selected experts,
-//    stacked; every workgroup first derives the selection from the router
-//    logits (so no host round trip and no extra launch), workgroup 0 publishes
-//    it.  Tiles never straddle experts, so the expert of a tile is uniform.
+//  - kModeMoeGateUp: rows are the I row pairs (gate row j, up row j) of the
+//    k selected experts, stacked; a tile holds 64/G gate rows in row slot 0
+//    and the matching up rows, I further on in the expert's matrix, in slot
+//    1, and the owner lane writes g, u and h = silu(g) * u.  Every workgroup
+//    first derives the selection from the router logits (so no host round
+//    trip and no extra launch), workgroup 0 publishes it.  Tiles never
+//    straddle experts, so the expert of a tile is uniform.
 //  - kModeMoeDown: row i is the concatenation over the k selected experts of
-//    their down-projection row i, and x is the concatenation of
-//    w_s * silu(g_s) * u_s; one row sum is then the weighted expert mixture,
-//    formed in a fixed order.  G divides the units per expert, so the expert
-//    of each unit step is uniform too.
+//    their down-projection row i, and x is the concatenation of w_s * h_s;
+//    one row sum is then the weighted expert mixture, formed in a fixed
+//    order.  G divides the units per expert, so the expert of each unit step
+//    is uniform too.
 //
 // kModeShortConv (BebeLM page, section "门控短卷积": B, C, x = split(in_proj(h),
 // 3); Bx = B * x; causal depthwise conv of kernel size 3 with a 2-position
@@ -64,8 +67,7 @@ struct MoeArgs {
     int32_t E, k;
     int32_t *topk_idx;      // [k] written by the gate/up launch, read by the down launch
     float *topk_w;          // [k]
-    const float *gu;        // down launch: [k][2I] gate rows then up rows per slot
-    float *h;               // down launch: [k][I] silu(g) * u, written by workgroup 0
+    float *h;               // [k][I] silu(g) * u: written by the gate/up launch, read by the down launch
     int64_t mat_bytes;      // bytes of one expert matrix
     int32_t rows_per_mat;   // gate/up launch: 2I
     int32_t units_per_mat;  // down launch: I / unit weights
@@ -245,9 +247,11 @@ __device__ __forceinline__ void rows_body(const RowsParams &p, const int bid, co
     const int U = p.K / F::kUnitWeights;
     const int iters = (U + G - 1) / G;  // unit steps per row
     // kModeSiluUp / kModeShortConv: the row slots are rows M apart in a
-    // stack (gate and up; B, C and x)
-    constexpr bool kPair = MODE == kModeSiluUp || MODE == kModeShortConv;
+    // stack (gate and up; B, C and x); kModeMoeGateUp: I apart in an
+    // expert's matrix (gate and up)
+    constexpr bool kPair = MODE == kModeSiluUp || MODE == kModeShortConv || MODE == kModeMoeGateUp;
     static_assert(MODE != kModeSiluUp || R == 2, "gate and up slots");
+    static_assert(MODE != kModeMoeGateUp || R == 2, "gate and up slots");
     static_assert(MODE != kModeShortConv || R == 3, "B, C and x slots");
     constexpr int kRowsPerTile = kPair ? P : R * P;
     const int ntiles = (p.M + kRowsPerTile - 1) / kRowsPerTile;
@@ -263,7 +267,8 @@ __device__ __forceinline__ void rows_body(const RowsParams &p, const int bid, co
     uint32_t row_off[R];
 #pragma unroll
     for (int r = 0; r < R; r++)
-        row_off[r] = (uint32_t)(kPair ? r * p.M + sub : r * P + sub) * rb;
+        row_off[r] = (uint32_t)(kPair ? r * (MODE == kModeMoeGateUp ? p.moe.I : p.M) + sub
+                                      : r * P + sub) * rb;
     const uint32_t lane_uoff = F::unit_offset(g);
 
     float best_v = -__builtin_inff();
@@ -299,10 +304,10 @@ __device__ __forceinline__ void rows_body(const RowsParams &p, const int bid, co
         // below): past the end the view is empty and reads zeros.
         const bool live = r0 < p.M;
         if (MODE == kModeMoeGateUp) {
-            // the tile's rows belong to one selected expert
-            int slot = r0 / p.moe.rows_per_mat;
+            // the tile's row pairs belong to one selected expert
+            int slot = r0 / p.moe.I;
             slot = slot < p.moe.k ? slot : p.moe.k - 1;
-            const int rin = r0 - slot * p.moe.rows_per_mat;
+            const int rin = r0 - slot * p.moe.I;
             const int ex = __builtin_amdgcn_readfirstlane(sel[slot]);  // uniform
             base = p.W + (int64_t)ex * p.moe.mat_bytes + (int64_t)rin * rb;
             avail = live ? (uint64_t)(p.moe.rows_per_mat - rin) * rb : 0;
@@ -354,7 +359,16 @@ __device__ __forceinline__ void rows_body(const RowsParams &p, const int bid, co
             }
         }
         const int r0 = t * kRowsPerTile;
-        if constexpr (MODE == kModeSiluUp) {
+        if constexpr (MODE == kModeMoeGateUp) {
+            const int row = r0 + sub;  // row pair: slot * I + j
+            if (owner && row < p.M) {
+                const int slot = row / p.moe.I, j = row - slot * p.moe.I;
+                float *gu = p.seg.y[0] + (int64_t)slot * 2 * p.moe.I;
+                gu[j] = tot[0];
+                gu[p.moe.I + j] = tot[1];
+                p.moe.h[row] = siluf(tot[0]) * tot[1];
+            }
+        } else if constexpr (MODE == kModeSiluUp) {
             const int row = r0 + sub;
             if (owner && row < p.M) p.seg.y[0][row] = siluf(tot[0]) * tot[1];
         } else if constexpr (MODE == kModeShortConv) {
@@ -464,27 +478,24 @@ __device__ __forceinline__ void rows_body(const RowsParams &p, const int bid, co
             wsel[threadIdx.x] = p.moe.topk_w[threadIdx.x];
         }
         __syncthreads();
-        // x[s*I + j] = w_s * silu(g_s[j]) * u_s[j]; workgroup 0 keeps h.
+        // x[s*I + j] = w_s * h_s[j], h written by the gate/up launch.
         // K = k*I is a multiple of 32, so sum groups never straddle slots.
-        // The gate/up values of the first pass are loaded before the first
-        // weights are requested, as in stage_x.
+        // The first pass's h values are loaded before the first weights are
+        // requested, as in stage_x.
         const int I = p.moe.I, K = p.K;
         const int nt = blockDim.x;
-        const BufSrc gv(reinterpret_cast<const uint8_t *>(p.moe.gu), (uint64_t)p.moe.k * 2 * I * 4);
+        const BufSrc hv(reinterpret_cast<const uint8_t *>(p.moe.h), (uint64_t)K * 4);
         // kNB passes of 4 values per thread at a time: all their loads are
         // issued before any is used, so the batch pays one load latency
         constexpr int kNB = 4;
         auto batch = [&](int base0, bool first) {
-            float4 gg[kNB], uu[kNB];
+            float4 hh[kNB];
             int base[kNB], sl[kNB];
 #pragma unroll
             for (int i = 0; i < kNB; i++) {
                 base[i] = base0 + i * nt * 4 + (int)threadIdx.x * 4;
                 sl[i] = base[i] < K ? base[i] / I : 0;
-                const int j = base[i] < K ? base[i] - sl[i] * I : 0;
-                const uint32_t off = (uint32_t)(sl[i] * 2 * I + j) * 4u;
-                gg[i] = __builtin_bit_cast(float4, gv.ld16(off));
-                uu[i] = __builtin_bit_cast(float4, gv.ld16(off + (uint32_t)I * 4u));
+                hh[i] = __builtin_bit_cast(float4, hv.ld16((uint32_t)(base[i] < K ? base[i] : 0) * 4u));
             }
             if (first) {
                 issue(bufA, tA, itA);
@@ -492,12 +503,9 @@ __device__ __forceinline__ void rows_body(const RowsParams &p, const int bid, co
             }
 #pragma unroll
             for (int i = 0; i < kNB; i++) {
-                const float4 h = make_float4(siluf(gg[i].x) * uu[i].x, siluf(gg[i].y) * uu[i].y,
-                                             siluf(gg[i].z) * uu[i].z, siluf(gg[i].w) * uu[i].w);
-                if (bid == 0 && base[i] < K) *reinterpret_cast<float4 *>(p.moe.h + base[i]) = h;
                 const float w = wsel[sl[i]];
                 put_x4<F>(xs, sums, base[i], base[i] < K,
-                          make_float4(w * h.x, w * h.y, w * h.z, w * h.w));
+                          make_float4(w * hh[i].x, w * hh[i].y, w * hh[i].z, w * hh[i].w));
             }
         };
         batch(0, true);

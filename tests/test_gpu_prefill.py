@@ -49,8 +49,13 @@ SHAPES = [
     ("q4_k", 1000, 4096, 16),
     ("q5_k", 300, 4096, 100),    # Q5_K: the Q4_K policy plus fifth bits
     ("q5_k", 129, 14336, 20),    # and with K slices
-    ("q4_k", 2048, 256, 4096),   # two 16-row tiles per wave (256-row workgroups)
+    # one workgroup per compute unit with several 16-row tiles per wave:
+    ("q4_k", 2048, 256, 4096),   # four row tiles, four token tiles (512-row workgroups)
     ("q5_k", 2100, 512, 4000),   # the same with a ragged row group and token block
+    ("q4_k", 3000, 256, 1000),   # two row tiles, four token tiles
+    ("q4_k", 4000, 512, 500),    # two row tiles, two token tiles
+    ("q6_k", 1100, 1024, 1000),  # planned with four row tiles: Q6_K runs two, twice the groups
+    ("q8_0", 2100, 544, 1500),   # the same for Q8_0, ending in a partial window
 ]
 
 
