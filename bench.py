@@ -815,7 +815,7 @@ def main():
     # the same launches back to back in a HIP graph: events around the
     # replays, divided by the launch count (includes the gaps between them)
     dom_calls = [fn for (kind, t, K, b, fn) in launches if kind in DOMINANT_KINDS]
-    dom_graph_us = graph_time_us(torch, dom_calls, reps=max(2, args.steps // 5))
+    dom_graph_us = graph_time_us(torch, dom_calls, reps=max(20, args.steps))
     # the roofline's duration: these launches as the step runs them, back to
     # back in a graph (a rocprofv3 trace of the same replays agrees)
     achieved_graph = dom_bytes / (dom_graph_us * 1e-6) / 1e9
