@@ -70,26 +70,28 @@ struct Q4K {
     }
     // acc += sum over the unit's 64 weights of w * x.  Byte 32c + l of the
     // unit's nibbles holds weight l (low nibble) and weight 32 + l (high
-    // nibble) of sub-blocks 2c and 2c + 1; each pair of bytes is spread into
-    // the halves of a dword, whose low nibbles are then two f16 subnormals
-    // q * 2^-24 and whose high nibbles (masked in place) are 16 q * 2^-24.
+    // nibble) of sub-blocks 2c and 2c + 1.  A dword of four such bytes,
+    // masked in place, holds the low nibbles of bytes 0 and 2 as two f16
+    // subnormals q * 2^-24 (and their high nibbles as 16 q * 2^-24); the
+    // dword shifted right by 8 gives bytes 1 and 3 the same way.  That is
+    // one shift and four masks per eight weights.
     __device__ static __forceinline__ void dot(const Regs &r, const float *xv, const float *sums,
                                                int u, float &acc) {
         const uint32_t qw[8] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w};
         float lo0 = 0.f, lo1 = 0.f, hi0 = 0.f, hi1 = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-            const uint32_t p01 = bytes01_to_halves(qw[i]), p23 = bytes23_to_halves(qw[i]);
-            const f16x2_t a01 = as_f16x2(p01 & 0x000F000Fu), a23 = as_f16x2(p23 & 0x000F000Fu);
-            const f16x2_t b01 = as_f16x2(p01 & 0x00F000F0u), b23 = as_f16x2(p23 & 0x00F000F0u);
-            lo0 = fmaf((float)a01.x, xv[4 * i + 0], lo0);
-            lo1 = fmaf((float)a01.y, xv[4 * i + 1], lo1);
-            lo0 = fmaf((float)a23.x, xv[4 * i + 2], lo0);
-            lo1 = fmaf((float)a23.y, xv[4 * i + 3], lo1);
-            hi0 = fmaf((float)b01.x, xv[32 + 4 * i + 0], hi0);
-            hi1 = fmaf((float)b01.y, xv[32 + 4 * i + 1], hi1);
-            hi0 = fmaf((float)b23.x, xv[32 + 4 * i + 2], hi0);
-            hi1 = fmaf((float)b23.y, xv[32 + 4 * i + 3], hi1);
+            const uint32_t w = qw[i], w8 = qw[i] >> 8;
+            const f16x2_t a02 = as_f16x2(w & 0x000F000Fu), a13 = as_f16x2(w8 & 0x000F000Fu);
+            const f16x2_t b02 = as_f16x2(w & 0x00F000F0u), b13 = as_f16x2(w8 & 0x00F000F0u);
+            lo0 = fmaf((float)a02.x, xv[4 * i + 0], lo0);
+            lo1 = fmaf((float)a02.y, xv[4 * i + 2], lo1);
+            lo0 = fmaf((float)a13.x, xv[4 * i + 1], lo0);
+            lo1 = fmaf((float)a13.y, xv[4 * i + 3], lo1);
+            hi0 = fmaf((float)b02.x, xv[32 + 4 * i + 0], hi0);
+            hi1 = fmaf((float)b02.y, xv[32 + 4 * i + 2], hi1);
+            hi0 = fmaf((float)b13.x, xv[32 + 4 * i + 1], hi0);
+            hi1 = fmaf((float)b13.y, xv[32 + 4 * i + 3], hi1);
         }
         // both sums at the scale 2^-24 (the high nibbles carried 16 q)
         const float alo = lo0 + lo1, ahi = (hi0 + hi1) * 0.0625f;
@@ -577,24 +579,43 @@ struct Nib32 {
                                                int u, float &acc) {
         const uint32_t qw[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
         float lo0 = 0.f, lo1 = 0.f, hi0 = 0.f, hi1 = 0.f;
+        if constexpr (!kHigh) {
+            // four-bit codes: each dword masked in place (bytes 0 and 2) and
+            // shifted by 8 (bytes 1 and 3), as in the Q4_K dot; the high
+            // nibbles come out as 16 q
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            uint32_t a = qw[i] & 0x0F0F0F0Fu;          // weights 4i .. 4i+3
-            uint32_t b = (qw[i] >> 4) & 0x0F0F0F0Fu;   // weights 16+4i .. 16+4i+3
-            if (kHigh) {
-                a |= fifth_bits(r.hb >> (4 * i));
-                b |= fifth_bits(r.hb >> (16 + 4 * i));
+            for (int i = 0; i < 4; i++) {
+                const uint32_t w = qw[i], w8 = qw[i] >> 8;
+                const f16x2_t a02 = as_f16x2(w & 0x000F000Fu), a13 = as_f16x2(w8 & 0x000F000Fu);
+                const f16x2_t b02 = as_f16x2(w & 0x00F000F0u), b13 = as_f16x2(w8 & 0x00F000F0u);
+                lo0 = fmaf((float)a02.x, xv[4 * i + 0], lo0);
+                lo1 = fmaf((float)a02.y, xv[4 * i + 2], lo1);
+                lo0 = fmaf((float)a13.x, xv[4 * i + 1], lo0);
+                lo1 = fmaf((float)a13.y, xv[4 * i + 3], lo1);
+                hi0 = fmaf((float)b02.x, xv[16 + 4 * i + 0], hi0);
+                hi1 = fmaf((float)b02.y, xv[16 + 4 * i + 2], hi1);
+                hi0 = fmaf((float)b13.x, xv[16 + 4 * i + 1], hi0);
+                hi1 = fmaf((float)b13.y, xv[16 + 4 * i + 3], hi1);
             }
-            const f16x2_t a01 = as_f16x2(bytes01_to_halves(a)), a23 = as_f16x2(bytes23_to_halves(a));
-            const f16x2_t b01 = as_f16x2(bytes01_to_halves(b)), b23 = as_f16x2(bytes23_to_halves(b));
-            lo0 = fmaf((float)a01.x, xv[4 * i + 0], lo0);
-            lo1 = fmaf((float)a01.y, xv[4 * i + 1], lo1);
-            lo0 = fmaf((float)a23.x, xv[4 * i + 2], lo0);
-            lo1 = fmaf((float)a23.y, xv[4 * i + 3], lo1);
-            hi0 = fmaf((float)b01.x, xv[16 + 4 * i + 0], hi0);
-            hi1 = fmaf((float)b01.y, xv[16 + 4 * i + 1], hi1);
-            hi0 = fmaf((float)b23.x, xv[16 + 4 * i + 2], hi0);
-            hi1 = fmaf((float)b23.y, xv[16 + 4 * i + 3], hi1);
+            hi0 = (hi0 + hi1) * 0.0625f;  // exact: a power of two
+            hi1 = 0.f;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                // weights 4i .. 4i+3 and 16+4i .. 16+4i+3, with their fifth bits
+                const uint32_t a = (qw[i] & 0x0F0F0F0Fu) | fifth_bits(r.hb >> (4 * i));
+                const uint32_t b = ((qw[i] >> 4) & 0x0F0F0F0Fu) | fifth_bits(r.hb >> (16 + 4 * i));
+                const f16x2_t a01 = as_f16x2(bytes01_to_halves(a)), a23 = as_f16x2(bytes23_to_halves(a));
+                const f16x2_t b01 = as_f16x2(bytes01_to_halves(b)), b23 = as_f16x2(bytes23_to_halves(b));
+                lo0 = fmaf((float)a01.x, xv[4 * i + 0], lo0);
+                lo1 = fmaf((float)a01.y, xv[4 * i + 1], lo1);
+                lo0 = fmaf((float)a23.x, xv[4 * i + 2], lo0);
+                lo1 = fmaf((float)a23.y, xv[4 * i + 3], lo1);
+                hi0 = fmaf((float)b01.x, xv[16 + 4 * i + 0], hi0);
+                hi1 = fmaf((float)b01.y, xv[16 + 4 * i + 1], hi1);
+                hi0 = fmaf((float)b23.x, xv[16 + 4 * i + 2], hi0);
+                hi1 = fmaf((float)b23.y, xv[16 + 4 * i + 3], hi1);
+            }
         }
         const float qx = ((lo0 + lo1) + (hi0 + hi1)) * kTwo24;  // sum q x, exact scaling
         const float d = half_bits_to_float(r.hdr);
