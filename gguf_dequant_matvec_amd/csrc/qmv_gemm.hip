@@ -50,8 +50,13 @@ template <class F, int TT>
 struct PfLayout {
     static constexpr int kPfTokens = 16 * TT;
     static constexpr int kVals = F::kNSub * 4 * kPfTokens * F::kKpl;  // = 256 * kPfTokens
-    static constexpr int kBytes = kVals * 2 * 2 + F::kNSub * kPfTokens * 4;
+    static constexpr int kBytes = kVals * 2 * 2 + F::kNSub * kPfTokens * 4;    static_assert(kBytes % 16 == 0, "whole 16-byte chunks");
 };
+
+// Bytes of staged activations per (token block, window), the most any
+// format takes (16 sub-blocks of sums), so the workspace size does not
+// depend on the format.
+constexpr size_t pf_window_bytes_max(int tt) { return (size_t)tt * 16 * (256 * 4 + 16 * 4); }
 
 // X staging of one window for kPfTokens tokens; lane-group order as in the
 // small-batch staging (tokens fastest within 16, then the four lane groups),
@@ -126,6 +131,19 @@ struct XStagePf {
     }
 };
 
+// The staged activations of one (token block, window), written once per
+// call: every row group's workgroups copy them into LDS instead of each
+// loading and splitting X again.
+template <class F, int TT>
+__global__ __launch_bounds__(kThreads) void gemm_pf_prep(GemmParams p) {
+    using L = PfLayout<F, TT>;
+    const int tb = (int)blockIdx.x / p.windows, wi = (int)blockIdx.x % p.windows;
+    const BufSrc xview(reinterpret_cast<const uint8_t *>(p.X), (uint64_t)p.n * (uint32_t)p.K * 4u);
+    XStagePf<F, TT> xs;
+    xs.load(xview, p.K, tb * 16 * TT, wi);
+    xs.store(p.xprep + ((int64_t)tb * p.windows + wi) * L::kBytes, wi, p.K);
+}
+
 // RT 16-row tiles per wave (a workgroup owns 128 * RT rows): each X
 // fragment read from LDS feeds RT row tiles' MFMAs, and the staged X of a
 // window is shared by 128 * RT rows.
@@ -159,7 +177,6 @@ __global__ __launch_bounds__(kThreads, 4) void gemm_pf_kernel(GemmParams p, int 
     const int rows_left = p.M - row0 > 0 ? p.M - row0 : 0;
     const BufSrc src(p.W + (int64_t)row0 * p.row_bytes,
                      (uint64_t)rows_left * (uint64_t)(uint32_t)p.row_bytes);
-    const BufSrc xview(reinterpret_cast<const uint8_t *>(p.X), (uint64_t)p.n * (uint32_t)p.K * 4u);
 
     auto nvalid_of = [&](int wi) {
         if constexpr (std::is_same<F, GQ80>::value) {
@@ -248,9 +265,19 @@ __global__ __launch_bounds__(kThreads, 4) void gemm_pf_kernel(GemmParams p, int 
     for (int wi = w0; wi < wtotal; wi++) {
         const int wn = wi + 1 < wtotal ? wi + 1 : wi;
         {
-            XStagePf<F, TT> xs;
-            xs.load(xview, p.K, tok0, wi);
-            xs.store(smem, wi, p.K);
+            // the window's staged activations, copied by direct-to-LDS
+            // 16-byte loads: each wave instruction fills 1 KB of LDS and no
+            // register holds the data
+            constexpr int kChunks = L::kBytes / 16;
+            const uint8_t *g = p.xprep + ((int64_t)tb * p.windows + wi) * L::kBytes;
+            for (int base = wave * kWave; base < kChunks; base += kThreads) {  // wave-uniform
+                const int c = base + lane;
+                if (c < kChunks)
+                    __builtin_amdgcn_global_load_lds(
+                        (const __attribute__((address_space(1))) void *)(g + 16 * (int64_t)c),
+                        (__attribute__((address_space(3))) void *)(smem + 16 * base), 16, 0, 0);
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
         __syncthreads();
         Set wnext;
@@ -290,7 +317,10 @@ hipError_t launch_pf_tt(GemmParams p, const PfPlan &plan, hipStream_t s) {
     if (e != hipSuccess) return e;
     p.slices = plan.slices;
     const int64_t grid = (int64_t)plan.rg_pad * plan.token_blocks * plan.slices;
-    if (grid > 0x7FFFFFFFll) return hipErrorInvalidValue;
+    const int64_t prep_grid = (int64_t)plan.token_blocks * p.windows;
+    if (grid > 0x7FFFFFFFll || prep_grid > 0x7FFFFFFFll) return hipErrorInvalidValue;
+    e = launch_aux(gemm_pf_prep<F, TT>, dim3((unsigned)prep_grid), dim3(kThreads), 0, s, p);
+    if (e != hipSuccess) return e;
     e = launch_main(gemm_pf_kernel<F, TT, RT>, dim3((unsigned)grid), dim3(kThreads), lds, s, p,
                     plan.token_blocks, plan.wps);
     if (e != hipSuccess || plan.slices == 1) return e;
@@ -361,9 +391,17 @@ PfPlan pf_plan(int64_t M, int64_t K, int64_t n) {
     return pl;
 }
 
+// Workspace: the slices' partial sums (split K only), then the staged
+// activations of every (token block, window), 256-byte aligned.
+static size_t pf_partial_bytes(const PfPlan &pl, int64_t M, int64_t n) {
+    const size_t b = pl.slices > 1 ? (size_t)pl.slices * (size_t)n * (size_t)M * sizeof(float) : 0;
+    return (b + 255) / 256 * 256;
+}
+
 size_t gemm_workspace(int64_t M, int64_t K, int64_t n) {
     const PfPlan pl = pf_plan(M, K, n);
-    return pl.slices > 1 ? (size_t)pl.slices * (size_t)n * (size_t)M * sizeof(float) : 0;
+    const size_t windows = (size_t)((K + kWin - 1) / kWin);
+    return pf_partial_bytes(pl, M, n) + (size_t)pl.token_blocks * windows * pf_window_bytes_max(pl.tt);
 }
 
 hipError_t launch_gemm(int type, const uint8_t *W, int64_t M, int64_t K, int64_t n, const float *X,
@@ -377,6 +415,8 @@ hipError_t launch_gemm(int type, const uint8_t *W, int64_t M, int64_t K, int64_t
     p.X = X;
     p.Y = Y;
     p.partial = reinterpret_cast<float *>(ws);
+    p.windows = (int32_t)((K + kWin - 1) / kWin);
+    p.xprep = reinterpret_cast<uint8_t *>(ws) + pf_partial_bytes(pf_plan(M, K, n), M, n);
     switch (type) {
     case kQ4K: return launch_pf<GQ4K>(p, s);
     case kQ5K: return launch_pf<GQ5K>(p, s);

@@ -47,8 +47,10 @@ struct GemmParams {
     const float *X;
     float *Y;          // final output (one slice) ...
     float *partial;    // ... or [slices][n][M] partial sums
+    uint8_t *xprep;    // activations in the staged operand layout (prefill)
     int32_t row_groups;
     int32_t slices;
+    int32_t windows;   // 256-weight windows of K
 };
 
 constexpr int kThreads = 512;  // 8 waves

@@ -304,10 +304,14 @@ qmv_status qmv_gemm_n(qmv_type t, const void *blocks, int64_t M, int64_t K, int3
  * sum_k |w_ik x_k| per output.  A workgroup covers up to 64 tokens by 128
  * rows; K is split into slices only when rows and tokens alone give too few
  * workgroups (few rows, few tokens, long K), and the slices' partial sums
- * are added in a fixed order, so results are deterministic either way.
+ * are added in a fixed order, so results are deterministic either way.  A
+ * first launch splits X once into the operand layout (bf16 hi + lo and
+ * sub-block sums, 1088 bytes per 16 tokens and 256 values) in the
+ * workspace, which every workgroup then copies instead of converting X.
  * workspace: device, >= qmv_workspace_bytes(QMV_OP_GEMM, M, K, n, 0) bytes
- * (0 when K is not split; then NULL is allowed), 16-byte aligned, no initial
- * contents needed; QMV_EWORKSPACE if it is missing or too small. */
+ * (always > 0: the split activations, plus the slices' partial sums when K
+ * is split), 16-byte aligned, no initial contents needed; QMV_EWORKSPACE if
+ * it is missing or too small. */
 qmv_status qmv_gemm(qmv_type t, const void *blocks, int64_t M, int64_t K, int64_t n, const float *X,
                     float *Y, void *workspace, size_t ws_bytes, hipStream_t stream);
 

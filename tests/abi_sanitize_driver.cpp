@@ -79,9 +79,10 @@ hipError_t launch_gemm_n(int, const uint8_t *, int64_t, int64_t, int32_t, const 
     g_calls++;
     return hipSuccess;
 }
-// workspace sizes of the split products (the real plans live in the kernel
-// units): a fixed size, enough to exercise the checks
-size_t gemm_workspace(int64_t, int64_t K, int64_t) { return K > 4096 ? 4096 : 0; }
+// workspace sizes (the real plans live in the kernel units): fixed sizes,
+// enough to exercise the checks; the prefill product always takes one (its
+// staged activations), the verify product only when K is split
+size_t gemm_workspace(int64_t, int64_t, int64_t) { return 4096; }
 size_t gemm_n_workspace(int64_t, int64_t K, int32_t) { return K > 4096 ? 4096 : 0; }
 }  // namespace qmv
 
@@ -160,7 +161,8 @@ int main() {
     EXPECT(qmv_gemm_n(QMV_Q4_K, W, 100, 4096, 8, x, y, nullptr, 0, s) == QMV_OK);
     EXPECT(qmv_gemm_n(QMV_Q4_K, W, 100, 8192, 8, x, y, nullptr, 0, s) == QMV_EWORKSPACE);
     EXPECT(qmv_gemm_n(QMV_Q4_0, W, 100, 4096, 8, x, y, nullptr, 0, s) == QMV_EINVAL);
-    EXPECT(qmv_gemm(QMV_Q4_K, W, 100, 4096, 512, x, y, nullptr, 0, s) == QMV_OK);
+    EXPECT(qmv_gemm(QMV_Q4_K, W, 100, 4096, 512, x, y, nullptr, 0, s) == QMV_EWORKSPACE);
+    EXPECT(qmv_gemm(QMV_Q4_K, W, 100, 4096, 512, x, y, ws, 4096, s) == QMV_OK);
     EXPECT(qmv_gemm(QMV_Q4_K, W, 100, 4096, QMV_MAX_PREFILL_N + 1, x, y, nullptr, 0, s) ==
            QMV_ESHAPE);
     EXPECT(qmv_dequant(QMV_Q4_K, W, 4, 256, (float *)ws, s) == QMV_OK);

@@ -42,16 +42,32 @@ def test_row_bytes_and_workspace():
     assert q.qmv_row_bytes("q5_k", 512) == 352
     assert q.qmv_workspace_bytes(q.OP_ARGMAX, 128000, 4096) >= 8 * 2048
     assert q.qmv_workspace_bytes(q.OP_MOE, 2048, 1536, 32, 4) == 256 + 3 * 4 * 1536 * 4
-    # prefill product: no workspace when rows and token blocks fill the chip,
-    # else whole n x M f32 slices (2 to 16 of them)
-    assert q.qmv_workspace_bytes(q.OP_GEMM, 28672, 4096, 512) == 0
-    assert q.qmv_workspace_bytes(q.OP_GEMM, 4096, 4096, 4096) == 0
-    for M, K, n in [(4096, 14336, 64), (4096, 4096, 16), (300, 14336, 20), (256, 512, 1)]:
+    # prefill product: whole n x M f32 slices (2 to 16 of them, 256-byte
+    # rounded) when K is split, then the staged activations: 1088 bytes per
+    # 16 tokens and 256 values (bf16 or f16 hi + lo, sub-block sums) for every
+    # token block of 16 * tt tokens (tt = 1, 2 or 4) and 256-weight window
+    def staged(n, K, tt):
+        return -(-n // (16 * tt)) * -(-K // 256) * 1088 * 16 * tt
+
+    def layouts(M, K, n):
         w = q.qmv_workspace_bytes(q.OP_GEMM, M, K, n)
-        slices = w // (4 * n * M)
-        assert w % (4 * n * M) == 0 and (slices == 0 or 2 <= slices <= 16), (M, K, n, w)
-    assert q.qmv_workspace_bytes(q.OP_GEMM, 4096, 14336, 64) > 0
-    assert q.qmv_workspace_bytes(q.OP_GEMM, 256, 512, 1) == 0   # 2 windows: no split
+        out = []
+        for tt in (1, 2, 4):
+            rest = w - staged(n, K, tt)
+            for slices in [0] + list(range(2, 17)):
+                if rest == -(-(slices * 4 * n * M) // 256) * 256:
+                    out.append((tt, slices))
+        return w, out
+    # rows and token blocks fill the chip: no split
+    for M, K, n in [(28672, 4096, 512), (4096, 4096, 4096), (256, 512, 1)]:
+        w, lay = layouts(M, K, n)
+        assert any(s == 0 for _, s in lay), (M, K, n, w)
+    # few rows and tokens, long K: split
+    for M, K, n in [(4096, 14336, 64), (300, 14336, 20)]:
+        w, lay = layouts(M, K, n)
+        assert any(s >= 2 for _, s in lay), (M, K, n, w)
+    w, lay = layouts(4096, 4096, 16)
+    assert lay, w
     assert q.qmv_workspace_bytes(q.OP_GEMM, 4096, 4096, q.MAX_PREFILL_N + 1) == 0
     assert q.load().qmv_status_str(3) == b"pointer misaligned"
 
@@ -101,7 +117,11 @@ def test_pointer_and_type_errors():
     assert status_of(q.qmv_gemm, "q4_k", A16, 4, 256, 0, A16, A16) == "QMV_ESHAPE"
     assert status_of(q.qmv_gemm, "q4_k", A16, 4, 256, q.MAX_PREFILL_N + 1, A16, A16) == "QMV_ESHAPE"
     assert status_of(q.qmv_gemm, "q4_k", A16, 4, 256, 64, A16 + 2, A16) == "QMV_EALIGN"
-    # a K-split plan needs its workspace
+    # every plan needs its workspace (the staged activations)
+    need = q.qmv_workspace_bytes(q.OP_GEMM, 28672, 4096, 512)
+    assert status_of(q.qmv_gemm, "q4_k", A16, 28672, 4096, 512, A16, A16, 0, 0) == "QMV_EWORKSPACE"
+    assert status_of(q.qmv_gemm, "q4_k", A16, 28672, 4096, 512, A16, A16, A16,
+                     need - 1) == "QMV_EWORKSPACE"
     need = q.qmv_workspace_bytes(q.OP_GEMM, 256, 14336, 32)
     assert need > 0
     assert status_of(q.qmv_gemm, "q4_k", A16, 256, 14336, 32, A16, A16, 0, 0) == "QMV_EWORKSPACE"
