@@ -223,6 +223,14 @@ __global__ __launch_bounds__(kThreads, 4) void gemm_pf_kernel(GemmParams p, int 
                         acc[rt][tt] = corr_mfma<F>(w[rt], xsum, kPfTokens, tt * 16, j0, r, q,
                                                    acc[rt][tt]);
         }
+        // operand fragments of tile tt of sub-block j; each tile's are read
+        // one tile ahead, so their LDS latency overlaps the previous tile's
+        // MFMAs
+        auto frag = [&](const __bf16 *x, int j, int tt) {
+            const int fo = ((j * 4 + q) * kPfTokens + tt * 16 + r) * F::kKpl;
+            return *reinterpret_cast<const Frag<F> *>(x + fo);
+        };
+        Frag<F> ah = frag(xhi, 0, 0), al = frag(xlo, 0, 0);
 #pragma unroll
         for (int j = 0; j < F::kNSub; j++) {
             if (j >= nsub) break;
@@ -235,9 +243,14 @@ __global__ __launch_bounds__(kThreads, 4) void gemm_pf_kernel(GemmParams p, int 
             }
 #pragma unroll
             for (int tt = 0; tt < kPfTiles; tt++) {
-                const int fo = ((j * 4 + q) * kPfTokens + tt * 16 + r) * F::kKpl;
-                const Frag<F> ah = *reinterpret_cast<const Frag<F> *>(xhi + fo);
-                const Frag<F> al = *reinterpret_cast<const Frag<F> *>(xlo + fo);
+                // the next tile (past the last sub-block: none)
+                const int jn = tt + 1 < kPfTiles ? j : j + 1;
+                const int tn = tt + 1 < kPfTiles ? tt + 1 : 0;
+                Frag<F> ahn = ah, aln = al;
+                if (jn < F::kNSub) {
+                    ahn = frag(xhi, jn, tn);
+                    aln = frag(xlo, jn, tn);
+                }
 #pragma unroll
                 for (int rt = 0; rt < RT; rt++) {
                     f32x4 c = {0.f, 0.f, 0.f, 0.f};
@@ -247,7 +260,12 @@ __global__ __launch_bounds__(kThreads, 4) void gemm_pf_kernel(GemmParams p, int 
                     acc[rt][tt][1] = fmaf(scale[rt], c[1], acc[rt][tt][1]);
                     acc[rt][tt][2] = fmaf(scale[rt], c[2], acc[rt][tt][2]);
                     acc[rt][tt][3] = fmaf(scale[rt], c[3], acc[rt][tt][3]);
+                    // the sums are formed here: sunk to the next use of acc
+                    // they would hold every tile's MFMA result at once
+                    asm volatile("" : "+v"(acc[rt][tt]));
                 }
+                ah = ahn;
+                al = aln;
                 // keep each tile's operand reads and epilogue next to its
                 // MFMAs (hoisting or sinking them across tiles would need
                 // more registers than a wave has)
