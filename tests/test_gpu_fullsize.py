@@ -185,6 +185,21 @@ def test_max_k_verify(t, M, n):
         assert_rel(Yh[j], yr, ar, what=f"{t} verify {M}x{K} column {j}")
 
 
+@pytest.mark.parametrize("t,M,n", [("q4_k", 300, 40), ("q6_k", 70, 20), ("q8_0", 50, 17),
+                                   ("q5_k", 129, 70)])
+def test_max_k_prefill(t, M, n):
+    """The prefill product at the largest K: its staged activations (128
+    windows per token block) and its K slices, checked on every output."""
+    K = q.MAX_K
+    b, bd = mat(t, M, K, 970 + M)
+    X = synth.activations(971 + M, K, n=n)
+    Y = empty(n * M)
+    ws = empty(q.qmv_workspace_bytes(q.OP_GEMM, M, K, n), "uint8")
+    q.qmv_gemm(t, bd, M, K, n, dev(X), Y, ws)
+    Yr, Ar = oracle.gemm_n(t, b, M, K, X)
+    assert_rel(host(Y), Yr.ravel(), Ar.ravel(), what=f"{t} prefill {M}x{K} n={n}")
+
+
 def test_llama1b_decode_matvecs_full():
     H = C2["hidden"]
     check_fused("q4_k", C2["qkv"], H, 910)

@@ -95,6 +95,24 @@ def test_gemm_llama8b_gate_up_n512_sampled():
         assert_rel(Y[j, rows], yr, ar, what=f"token {j}")
 
 
+@pytest.mark.parametrize("t,M,K,n", [("q4_k", 300, 4096, 70), ("q6_k", 129, 1536, 40),
+                                     ("q8_0", 77, 576, 33), ("q5_k", 129, 14336, 20)])
+def test_gemm_wide_range_x(t, M, K, n):
+    """Tokens whose scales differ by up to 1e40, values within a token over
+    1e6, and an all-zero token: the bf16 hi + lo split made once per call
+    keeps every output within the bound (no overflow, no lost small token)."""
+    b = quantized(t, M, K, 840 + n)
+    g = np.random.default_rng(841 + n)
+    X = g.standard_normal((n, K)) * 10.0 ** g.integers(-3, 3, (n, K))
+    X *= 10.0 ** g.integers(-20, 20, (n, 1))
+    X[n // 2] = 0.0
+    X = X.astype(np.float32)
+    Yr, Ar = oracle.gemm_n(t, b, M, K, X)
+    Y = gemm_gpu(t, dev(b), M, K, X)
+    assert np.all(Y[n // 2] == 0.0)
+    assert_rel(Y.ravel(), Yr.ravel(), Ar.ravel(), what="wide-range X")
+
+
 def test_gemm_split_k_is_deterministic_and_within_bound():
     """A K-split call (few rows and tokens) is deterministic and agrees with
     the oracle; its workspace is a whole number of n x M f32 slices plus the
