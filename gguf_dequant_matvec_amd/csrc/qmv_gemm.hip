@@ -30,15 +30,18 @@ __global__ __launch_bounds__(256) void gemm_n_reduce(const float *partial, int s
 // Prefill-size product (n up to thousands of tokens; BebeLM page, section
 // "性能表现": prompts are processed in batches).  With many tokens there is
 // parallelism across token blocks, so K is split only when rows and token
-// blocks alone give too few workgroups: a workgroup owns 128 rows, a block
-// of 16 * TT tokens and a slice of consecutive 256-weight windows (all of K
-// unless split).  Per window it stages X for its tokens (bf16 hi/lo operand
-// fragments and per-sub-block sums) in LDS, then multiplies while the next
-// window's weights are in flight in a second register set.  Each weight sub-block's codes and scales are formed
-// once and used by the TT token tiles.  Two workgroups share a compute unit,
-// so one's X staging overlaps the other's multiply.  Every output is one fixed-order sum
-// over the windows, or over the slices' partial sums added in slice order by
-// a second kernel, so results are deterministic.
+// blocks alone give too few workgroups: a workgroup owns 128 * RT rows, a
+// block of 16 * TT tokens and a slice of consecutive 256-weight windows (all
+// of K unless split).  A first kernel splits X once per call into the
+// staged layout (bf16 hi/lo operand fragments and per-sub-block sums of
+// every token block and window) in the workspace.  Per window the main
+// kernel copies its token block's staged X into LDS, then multiplies while
+// the next window's weights are in flight in a second register set.  Each
+// weight sub-block's codes and scales are formed once and used by the TT
+// token tiles.  Two workgroups share a compute unit, so one's X copy
+// overlaps the other's multiply.  Every output is one fixed-order sum over
+// the windows, or over the slices' partial sums added in slice order by a
+// third kernel, so results are deterministic.
 // Workgroups are mapped so that those sharing rows run on the same XCD
 // (workgroups go to XCDs round-robin): their weights come from that XCD's L2.
 // ---------------------------------------------------------------------------
