@@ -376,10 +376,15 @@ hipError_t launch_pf(GemmParams p, hipStream_t s) {
 }  // namespace
 
 // Prefill launch plan.  The most tokens per workgroup (TT = 4, 2, 1) that
-// still gives two workgroups per compute unit of a 256-CU part without a K
-// split; failing that, one token tile per workgroup and K split into the
-// fewest slices (2 .. 16, at least two windows each) that reach that count.
-// The plan depends only on (M, K, n), so the workspace size does too.
+// still gives one workgroup per compute unit of a 256-CU part (half of the
+// two that fit) without a K split: more tokens per workgroup reuse each
+// code and each staged X fragment more often, which beat filling every
+// slot (32-layer passes: n = 256 13.9 -> 12.0 ms, n = 64 6.3 -> 5.3 ms
+// against a threshold of two per compute unit; a quarter per compute unit
+// was slower again).  Failing that, one token tile per workgroup and K
+// split into the fewest slices (2 .. 16, at least two windows each) that
+// give two per compute unit.  The plan depends only on (M, K, n), so the
+// workspace size does too.
 PfPlan pf_plan(int64_t M, int64_t K, int64_t n) {
     constexpr int64_t kWant = 512;
     PfPlan pl{};
@@ -401,7 +406,7 @@ PfPlan pf_plan(int64_t M, int64_t K, int64_t n) {
     for (int tt = 4; tt >= 1; tt >>= 1) {
         pl.tt = tt;
         pl.token_blocks = tblocks(tt);
-        if ((int64_t)pl.rg_pad * pl.token_blocks >= kWant) return pl;
+        if ((int64_t)pl.rg_pad * pl.token_blocks >= kWant / 2) return pl;
     }
     // tt = 1 here
     for (int ks = 2; ks <= 16 && wtotal / ks >= 2; ks *= 2) {
