@@ -47,13 +47,13 @@ __global__ __launch_bounds__(256) void gemm_n_reduce(const float *partial, int s
 // ---------------------------------------------------------------------------
 constexpr int kXcds = 8;
 
-// TT: token tiles of 16 per workgroup (1, 2 or 4, chosen per call so that
-// there are enough workgroups)
+// TT: token tiles of 16 per workgroup (4; 2 or 1 when n is at most 32 or 16)
 template <class F, int TT>
 struct PfLayout {
     static constexpr int kPfTokens = 16 * TT;
     static constexpr int kVals = F::kNSub * 4 * kPfTokens * F::kKpl;  // = 256 * kPfTokens
-    static constexpr int kBytes = kVals * 2 * 2 + F::kNSub * kPfTokens * 4;    static_assert(kBytes % 16 == 0, "whole 16-byte chunks");
+    static constexpr int kBytes = kVals * 2 * 2 + F::kNSub * kPfTokens * 4;
+    static_assert(kBytes % 16 == 0, "whole 16-byte chunks");
 };
 
 // Bytes of staged activations per (token block, window), the most any
@@ -375,44 +375,41 @@ hipError_t launch_pf(GemmParams p, hipStream_t s) {
 
 }  // namespace
 
-// Prefill launch plan.  The most tokens per workgroup (TT = 4, 2, 1) that
-// still gives one workgroup per compute unit of a 256-CU part (half of the
-// two that fit) without a K split: more tokens per workgroup reuse each
-// code and each staged X fragment more often, which beat filling every
-// slot (32-layer passes: n = 256 13.9 -> 12.0 ms, n = 64 6.3 -> 5.3 ms
-// against a threshold of two per compute unit; a quarter per compute unit
-// was slower again).  Failing that, one token tile per workgroup and K
-// split into the fewest slices (2 .. 16, at least two windows each) that
-// give two per compute unit.  The plan depends only on (M, K, n), so the
-// workspace size does too.
+// Prefill launch plan.  Tokens per workgroup: 64 (TT = 4) when n fills
+// them, else 32 or 16.  When the row groups and token blocks give fewer
+// than 384 workgroups (1.5 per compute unit of a 256-CU part; two fit),
+// K is split into the fewest slices (2 .. 16, at least two windows each)
+// that reach 384, rather than taking fewer tokens per workgroup: at
+// n = 64 / 256 / 512 the 4096 x 14336 down projection took 51 -> 38,
+// 130 -> 93 and 193 -> 172 us per call, the 4096 x 4096 one 23 -> 23,
+// 42 -> 38 and 62 -> 59 us.  A stack with enough rows for 384 workgroups of
+// two row tiles each takes those and no split (gate+up 28672 x 4096 at
+// n = 256: 149 us, 169 us with two slices).  The plan depends only on
+// (M, K, n), so the workspace size does too.
 PfPlan pf_plan(int64_t M, int64_t K, int64_t n) {
-    constexpr int64_t kWant = 512;
+    constexpr int64_t kEnough = 384;
     PfPlan pl{};
     const int wtotal = (int)((K + kWin - 1) / kWin);
     auto tblocks = [&](int tt) { return (int)((n + 16 * tt - 1) / (16 * tt)); };
     pl.slices = 1;
     pl.wps = wtotal;
-    // two row tiles per wave (256-row workgroups) when that still gives 1.5
-    // workgroups per compute unit with 64 tokens each (n = 256 over the 32
-    // layers: 17.8 ms with a threshold of 2 per compute unit, 16.8 with 1.5)
+    // two row tiles per wave (256-row workgroups) with 64 tokens each
     pl.rt = 2;
     pl.tt = 4;
     pl.token_blocks = tblocks(4);
     pl.rg_pad = (int)(((M + 2 * kRowsPerWG - 1) / (2 * kRowsPerWG) + kXcds - 1) / kXcds * kXcds);
-    if ((int64_t)pl.rg_pad * pl.token_blocks >= kWant * 3 / 4) return pl;
+    if ((int64_t)pl.rg_pad * pl.token_blocks >= kEnough) return pl;
     pl.rt = 1;
     const int64_t row_groups = (M + kRowsPerWG - 1) / kRowsPerWG;
     pl.rg_pad = (int)((row_groups + kXcds - 1) / kXcds * kXcds);
-    for (int tt = 4; tt >= 1; tt >>= 1) {
-        pl.tt = tt;
-        pl.token_blocks = tblocks(tt);
-        if ((int64_t)pl.rg_pad * pl.token_blocks >= kWant / 2) return pl;
-    }
-    // tt = 1 here
+    pl.tt = n > 32 ? 4 : n > 16 ? 2 : 1;
+    pl.token_blocks = tblocks(pl.tt);
+    const int64_t grid = (int64_t)pl.rg_pad * pl.token_blocks;
+    if (grid >= kEnough) return pl;
     for (int ks = 2; ks <= 16 && wtotal / ks >= 2; ks *= 2) {
         pl.wps = (wtotal + ks - 1) / ks;
         pl.slices = (wtotal + pl.wps - 1) / pl.wps;  // no empty slice
-        if ((int64_t)pl.rg_pad * pl.token_blocks * pl.slices >= kWant) break;
+        if (grid * pl.slices >= kEnough) break;
     }
     return pl;
 }

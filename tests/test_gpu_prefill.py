@@ -116,8 +116,8 @@ def test_gemm_wide_range_x(t, M, K, n):
 def test_gemm_split_k_is_deterministic_and_within_bound():
     """A K-split call (few rows and tokens) is deterministic and agrees with
     the oracle; its workspace is a whole number of n x M f32 slices plus the
-    staged activations (1088 bytes per 16 tokens and 256 values; one 16-token
-    tile per token block in a split plan)."""
+    staged activations (1088 bytes per 16 tokens and 256 values; n = 32
+    fills its token blocks exactly)."""
     t, M, K, n = "q4_k", 256, 14336, 32
     wsb = q.qmv_workspace_bytes(q.OP_GEMM, M, K, n)
     rest = wsb - (-(-n // 16)) * (-(-K // 256)) * 1088 * 16
