@@ -376,42 +376,61 @@ hipError_t launch_pf(GemmParams p, hipStream_t s) {
 }  // namespace
 
 // Prefill launch plan.  Tokens per workgroup: 64 (TT = 4) when n fills
-// them, else 32 or 16.  When the row groups and token blocks give fewer
-// than 384 workgroups (1.5 per compute unit of a 256-CU part; two fit),
-// K is split into the fewest slices (2 .. 16, at least two windows each)
-// that reach 384, rather than taking fewer tokens per workgroup: at
-// n = 64 / 256 / 512 the 4096 x 14336 down projection took 51 -> 38,
-// 130 -> 93 and 193 -> 172 us per call, the 4096 x 4096 one 23 -> 23,
-// 42 -> 38 and 62 -> 59 us.  A stack with enough rows for 384 workgroups of
-// two row tiles each takes those and no split (gate+up 28672 x 4096 at
-// n = 256: 149 us, 169 us with two slices).  The plan depends only on
-// (M, K, n), so the workspace size does too.
+// them, else 32 or 16.  Enough workgroups means 384 (1.5 per compute unit
+// of a 256-CU part; two fit).  In order of preference:
+//  1. two row tiles per wave (256-row workgroups, 64 tokens), no K split;
+//  2. one row tile per wave (128 rows), no split;
+//  3. two row tiles and K split into the fewest slices (powers of two up to
+//     16) that give enough workgroups, if each slice keeps at least eight
+//     256-weight windows;
+//  4. one row tile and the fewest slices (at least two windows each) that
+//     give enough, or the most there can be.
+// Splitting K beat taking fewer tokens per workgroup, and long slices paid
+// for the two-tile waves' shared X reads (us per call, old plan of fewer
+// tokens -> this one; the 4096 x 14336 down projection at n = 64 / 256 /
+// 512: 51 -> 38, 130 -> 93, 193 -> 163; the 4096 x 4096 one at n = 256 /
+// 512: 42 -> 38, 62 -> 59).  Short slices did not pay for two tiles (4096 x
+// 4096 at n = 512 with four slices of four windows: 62.6 against 58.8 us),
+// and a split did not pay where there were enough workgroups (gate+up
+// 28672 x 4096 at n = 256: 149 us, 169 with two slices).  The plan depends
+// only on (M, K, n), so the workspace size does too.
 PfPlan pf_plan(int64_t M, int64_t K, int64_t n) {
     constexpr int64_t kEnough = 384;
-    PfPlan pl{};
+    constexpr int kLongSlice = 8;
     const int wtotal = (int)((K + kWin - 1) / kWin);
-    auto tblocks = [&](int tt) { return (int)((n + 16 * tt - 1) / (16 * tt)); };
+    const int tt = n > 32 ? 4 : n > 16 ? 2 : 1;
+    const int tb = (int)((n + 16 * tt - 1) / (16 * tt));
+    auto groups = [&](int rows) {
+        const int64_t g = (M + rows - 1) / rows;
+        return (int)((g + kXcds - 1) / kXcds * kXcds);
+    };
+    const int rg2 = groups(2 * kRowsPerWG), rg1 = groups(kRowsPerWG);
+    PfPlan pl{};
+    pl.tt = tt;
+    pl.token_blocks = tb;
     pl.slices = 1;
     pl.wps = wtotal;
-    // two row tiles per wave (256-row workgroups) with 64 tokens each
-    pl.rt = 2;
-    pl.tt = 4;
-    pl.token_blocks = tblocks(4);
-    pl.rg_pad = (int)(((M + 2 * kRowsPerWG - 1) / (2 * kRowsPerWG) + kXcds - 1) / kXcds * kXcds);
-    if ((int64_t)pl.rg_pad * pl.token_blocks >= kEnough) return pl;
-    pl.rt = 1;
-    const int64_t row_groups = (M + kRowsPerWG - 1) / kRowsPerWG;
-    pl.rg_pad = (int)((row_groups + kXcds - 1) / kXcds * kXcds);
-    pl.tt = n > 32 ? 4 : n > 16 ? 2 : 1;
-    pl.token_blocks = tblocks(pl.tt);
-    const int64_t grid = (int64_t)pl.rg_pad * pl.token_blocks;
-    if (grid >= kEnough) return pl;
-    for (int ks = 2; ks <= 16 && wtotal / ks >= 2; ks *= 2) {
-        pl.wps = (wtotal + ks - 1) / ks;
-        pl.slices = (wtotal + pl.wps - 1) / pl.wps;  // no empty slice
-        if (grid * pl.slices >= kEnough) break;
-    }
-    return pl;
+    auto with = [&](int rt, int rg) {
+        pl.rt = rt;
+        pl.rg_pad = rg;
+        return pl;
+    };
+    if (tt == 4 && (int64_t)rg2 * tb >= kEnough) return with(2, rg2);
+    if ((int64_t)rg1 * tb >= kEnough) return with(1, rg1);
+    // the fewest slices that give g workgroups enough (or the most allowed)
+    auto split = [&](int64_t g) {
+        for (int ks = 2; ks <= 16 && wtotal / ks >= 2; ks *= 2) {
+            pl.wps = (wtotal + ks - 1) / ks;
+            pl.slices = (wtotal + pl.wps - 1) / pl.wps;  // no empty slice
+            if (g * pl.slices >= kEnough) return true;
+        }
+        return false;
+    };
+    if (tt == 4 && split((int64_t)rg2 * tb) && pl.wps >= kLongSlice) return with(2, rg2);
+    pl.slices = 1;
+    pl.wps = wtotal;
+    split((int64_t)rg1 * tb);
+    return with(1, rg1);
 }
 
 // Workspace: the slices' partial sums (split K only), then the staged

@@ -95,6 +95,43 @@ def test_gemm_llama8b_gate_up_n512_sampled():
         assert_rel(Y[j, rows], yr, ar, what=f"token {j}")
 
 
+@pytest.mark.parametrize("n", [256, 512])
+def test_gemm_llama8b_down_sampled(n):
+    """The 4096 x 14336 down projection as the 32-layer prefill pass runs it:
+    K split into four slices, with one row tile per wave at n = 256 and two
+    at n = 512 (long slices), checked on sampled rows of sampled tokens."""
+    t, (M, K) = "q4_k", synth.CONFIG4["down"]
+    wsb = q.qmv_workspace_bytes(q.OP_GEMM, M, K, n)
+    assert wsb - (n // 16) * (K // 256) * 1088 * 16 == 4 * 4 * n * M
+    b = quantized(t, M, K, 903)
+    X = synth.activations(1125 + n, K, n=n)
+    Y = gemm_gpu(t, dev(b), M, K, X)
+    g = np.random.default_rng(11)
+    rows = np.unique(np.concatenate([[0, M - 1], g.integers(0, M, 40)])).astype(np.int64)
+    for j in [0, 1, 63, 64, 129, n - 1]:
+        yr, ar = oracle.qmv_rows(t, b, M, K, X[j], rows)
+        assert_rel(Y[j, rows], yr, ar, what=f"down n={n} token {j}")
+
+
+@pytest.mark.parametrize("t", ["q4_k", "q5_k"])
+def test_gemm_two_tiles_with_k_slices(t):
+    """Few 256-row groups, six 64-token blocks and long K: two row tiles per
+    wave with K in eight slices of eight windows (a ragged last row group
+    and token block), every token on sampled rows."""
+    M, K, n = 1100, 16384, 330
+    wsb = q.qmv_workspace_bytes(q.OP_GEMM, M, K, n)
+    assert wsb - 6 * 64 * (K // 256) * 1088 == -(-(8 * 4 * n * M) // 256) * 256
+    b = quantized(t, M, K, 1140)
+    X = synth.activations(1141, K, n=n)
+    Y = gemm_gpu(t, dev(b), M, K, X)
+    g = np.random.default_rng(12)
+    rows = np.unique(np.concatenate([[0, 255, 256, 1023, 1024, M - 1],
+                                     g.integers(0, M, 24)])).astype(np.int64)
+    for j in range(n):
+        yr, ar = oracle.qmv_rows(t, b, M, K, X[j], rows)
+        assert_rel(Y[j, rows], yr, ar, what=f"{t} token {j}")
+
+
 @pytest.mark.parametrize("t,M,K,n", [("q4_k", 300, 4096, 70), ("q6_k", 129, 1536, 40),
                                      ("q8_0", 77, 576, 33), ("q5_k", 129, 14336, 20)])
 def test_gemm_wide_range_x(t, M, K, n):
