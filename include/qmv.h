@@ -302,9 +302,10 @@ qmv_status qmv_gemm_n(qmv_type t, const void *blocks, int64_t M, int64_t K, int3
  * Q8_0, Q4_K, Q5_K, Q6_K.  Same arithmetic as qmv_gemm_n (bf16 MFMA on the exact
  * codes, X as bf16 hi + lo, f32 scales per sub-block), so within 1e-5 *
  * sum_k |w_ik x_k| per output.  A workgroup covers up to 64 tokens by 128
- * rows; K is split into slices only when rows and tokens alone give too few
- * workgroups (few rows, few tokens, long K), and the slices' partial sums
- * are added in a fixed order, so results are deterministic either way.  A
+ * or 256 rows; K is split into slices when rows and tokens alone give
+ * fewer than 384 workgroups (1.5 per compute unit of a 256-CU part), and
+ * the slices' partial sums are added in a fixed order, so results are
+ * deterministic either way (the plan depends only on M, K and n).  A
  * first launch splits X once into the operand layout (bf16 hi + lo and
  * sub-block sums, 1088 bytes per 16 tokens and 256 values) in the
  * workspace, which every workgroup then copies instead of converting X.
