@@ -379,24 +379,26 @@ hipError_t launch_pf(GemmParams p, hipStream_t s) {
 // them, else 32 or 16.  Enough workgroups means 384 (1.5 per compute unit
 // of a 256-CU part; two fit).  In order of preference:
 //  1. two row tiles per wave (256-row workgroups, 64 tokens), no K split;
-//  2. one row tile per wave (128 rows), no split;
-//  3. two row tiles and K split into the fewest slices (powers of two up to
-//     16) that give enough workgroups, if each slice keeps at least eight
+//  2. two row tiles and K split into the fewest slices (powers of two up to
+//     16) that give enough workgroups, if each slice keeps at least twelve
 //     256-weight windows;
+//  3. one row tile per wave (128 rows), no split;
 //  4. one row tile and the fewest slices (at least two windows each) that
 //     give enough, or the most there can be.
 // Splitting K beat taking fewer tokens per workgroup, and long slices paid
 // for the two-tile waves' shared X reads (us per call, old plan of fewer
 // tokens -> this one; the 4096 x 14336 down projection at n = 64 / 256 /
-// 512: 51 -> 38, 130 -> 93, 193 -> 163; the 4096 x 4096 one at n = 256 /
-// 512: 42 -> 38, 62 -> 59).  Short slices did not pay for two tiles (4096 x
-// 4096 at n = 512 with four slices of four windows: 62.6 against 58.8 us),
-// and a split did not pay where there were enough workgroups (gate+up
-// 28672 x 4096 at n = 256: 149 us, 169 with two slices).  The plan depends
-// only on (M, K, n), so the workspace size does too.
+// 512: 51 -> 38, 130 -> 93, 193 -> 163, and at n = 1024 one tile without a
+// split 329 against two tiles with two slices 311; the 4096 x 4096 one at
+// n = 256 / 512: 42 -> 38, 62 -> 59).  Short slices did not pay for two
+// tiles (4096 x 4096 at n = 512 with four slices of four windows: 62.6
+// against 58.8 us; at n = 1024 with two of eight: 102.9 against 97.0), and
+// a split did not pay where there were enough workgroups (gate+up 28672 x
+// 4096 at n = 256: 149 us, 169 with two slices).  The plan depends only on
+// (M, K, n), so the workspace size does too.
 PfPlan pf_plan(int64_t M, int64_t K, int64_t n) {
     constexpr int64_t kEnough = 384;
-    constexpr int kLongSlice = 8;
+    constexpr int kLongSlice = 12;
     const int wtotal = (int)((K + kWin - 1) / kWin);
     const int tt = n > 32 ? 4 : n > 16 ? 2 : 1;
     const int tb = (int)((n + 16 * tt - 1) / (16 * tt));
@@ -408,17 +410,16 @@ PfPlan pf_plan(int64_t M, int64_t K, int64_t n) {
     PfPlan pl{};
     pl.tt = tt;
     pl.token_blocks = tb;
-    pl.slices = 1;
-    pl.wps = wtotal;
     auto with = [&](int rt, int rg) {
         pl.rt = rt;
         pl.rg_pad = rg;
         return pl;
     };
-    if (tt == 4 && (int64_t)rg2 * tb >= kEnough) return with(2, rg2);
-    if ((int64_t)rg1 * tb >= kEnough) return with(1, rg1);
     // the fewest slices that give g workgroups enough (or the most allowed)
     auto split = [&](int64_t g) {
+        pl.slices = 1;
+        pl.wps = wtotal;
+        if (g >= kEnough) return true;
         for (int ks = 2; ks <= 16 && wtotal / ks >= 2; ks *= 2) {
             pl.wps = (wtotal + ks - 1) / ks;
             pl.slices = (wtotal + pl.wps - 1) / pl.wps;  // no empty slice
@@ -426,9 +427,8 @@ PfPlan pf_plan(int64_t M, int64_t K, int64_t n) {
         }
         return false;
     };
-    if (tt == 4 && split((int64_t)rg2 * tb) && pl.wps >= kLongSlice) return with(2, rg2);
-    pl.slices = 1;
-    pl.wps = wtotal;
+    if (tt == 4 && split((int64_t)rg2 * tb) && (pl.slices == 1 || pl.wps >= kLongSlice))
+        return with(2, rg2);
     split((int64_t)rg1 * tb);
     return with(1, rg1);
 }

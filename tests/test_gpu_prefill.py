@@ -116,9 +116,9 @@ def test_gemm_llama8b_down_sampled(n):
 @pytest.mark.parametrize("t", ["q4_k", "q5_k"])
 def test_gemm_two_tiles_with_k_slices(t):
     """Few 256-row groups, six 64-token blocks and long K: two row tiles per
-    wave with K in eight slices of eight windows (a ragged last row group
+    wave with K in eight slices of twelve windows (a ragged last row group
     and token block), every token on sampled rows."""
-    M, K, n = 1100, 16384, 330
+    M, K, n = 1100, 24576, 330
     wsb = q.qmv_workspace_bytes(q.OP_GEMM, M, K, n)
     assert wsb - 6 * 64 * (K // 256) * 1088 == -(-(8 * 4 * n * M) // 256) * 256
     b = quantized(t, M, K, 1140)
