@@ -200,6 +200,26 @@ def test_max_k_prefill(t, M, n):
     assert_rel(host(Y), Yr.ravel(), Ar.ravel(), what=f"{t} prefill {M}x{K} n={n}")
 
 
+def test_max_n_and_k_prefill():
+    """The prefill product at the most tokens and the largest K together: X
+    is 2^31 bytes, so the 32-bit byte offsets into X (and the staged
+    activations of 256 token blocks x 128 windows) run up to their limit.
+    X is drawn on the device; sampled tokens (both ends, token-block and
+    half-way edges) are checked on every row."""
+    t, M, K, n = "q4_k", 40, q.MAX_K, q.MAX_PREFILL_N
+    b, bd = mat(t, M, K, 980)
+    Xd = synth.normal_device(981, synth.T_X, (n, K), synth.X_STD, "cuda")
+    Y = empty(n * M)
+    ws = empty(q.qmv_workspace_bytes(q.OP_GEMM, M, K, n), "uint8")
+    q.qmv_gemm(t, bd, M, K, n, Xd, Y, ws)
+    Yh = host(Y).reshape(n, M)
+    for j in [0, 1, 63, 64, 8191, 8192, n - 65, n - 1]:
+        xj = host(Xd[j])
+        yr, ar = oracle.qmv(t, b, M, K, xj)
+        assert_rel(Yh[j], yr, ar, what=f"max n and K, token {j}")
+    del Xd, ws
+
+
 def test_llama1b_decode_matvecs_full():
     H = C2["hidden"]
     check_fused("q4_k", C2["qkv"], H, 910)
