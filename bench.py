@@ -427,29 +427,35 @@ def extras(torch, q, synth, step, progress, probe_gbs=None, only=None):
         progress("extras: gated gate+up done")
 
     if want("formats"):
-        # the further block formats at a gate-sized matrix, 14336 x 4096, cold:
-        # random code bytes with every block's fp16 scale fields set to 2^-7
-        # (and its min to -2^-6) -- the rate does not depend on the values
-        M, K = 14336, 4096
+        # the further block formats, cold, at a gate-sized matrix (14336 x
+        # 4096, where the per-launch fixed cost is a large part) and at a
+        # vocabulary-sized one (128000 x 4096, which shows the streaming
+        # rate): random code bytes with every block's fp16 scale fields set
+        # to 2^-7 (and its min to -2^-6) -- the rate does not depend on the
+        # values
         fields = {"q5_k": (0, 2), "q4_0": (0,), "q4_1": (0, 2), "q5_0": (0,), "q5_1": (0, 2),
                   "q8_1": (0, 2), "q2_k": (80, 82), "q3_k": (108,)}
+        K = 4096
         xk = synth.normal_device(7, synth.T_X, (K,), 1.0, dev)
-        yk = torch.empty(M, device=dev)
-        for t, offs in fields.items():
-            rb = q.row_bytes(t, K)
-            bb = q.BLOCK_BYTES[q.TYPES[t]]
-            g = torch.Generator(device=dev)
-            g.manual_seed(8)
-            b = torch.randint(0, 256, (M * rb,), dtype=torch.uint8, device=dev, generator=g)
-            bv = b.view(-1, bb)
-            for j, o in enumerate(offs):
-                bv[:, o] = 0x00
-                bv[:, o + 1] = 0x20 if j == 0 else 0xA4      # 2^-7, then -2^-6
-            n = GiB // b.numel() + 1
-            reps = replicas(b, n)
-            us = graph_time_us(torch, [lambda r=r, t=t: q.qmv(t, r, M, K, xk, yk) for r in reps], reps=5)
-            out[f"{t}_14336x4096_cold"] = rec(us, b.numel() + 4 * K + 4 * M, replicas=n)
-            del reps, b, bv
+        for M in (14336, 128000):
+            yk = torch.empty(M, device=dev)
+            for t, offs in fields.items():
+                rb = q.row_bytes(t, K)
+                bb = q.BLOCK_BYTES[q.TYPES[t]]
+                g = torch.Generator(device=dev)
+                g.manual_seed(8)
+                b = torch.randint(0, 256, (M * rb,), dtype=torch.uint8, device=dev, generator=g)
+                bv = b.view(-1, bb)
+                for j, o in enumerate(offs):
+                    bv[:, o] = 0x00
+                    bv[:, o + 1] = 0x20 if j == 0 else 0xA4      # 2^-7, then -2^-6
+                n = max(2, GiB // b.numel() + 1)
+                reps = replicas(b, n)
+                us = graph_time_us(torch, [lambda r=r, t=t: q.qmv(t, r, M, K, xk, yk) for r in reps],
+                                   reps=5 if M < 100000 else 3)
+                out[f"{t}_{M}x{K}_cold"] = rec(us, b.numel() + 4 * K + 4 * M, replicas=n)
+                del reps, b, bv
+            del yk
         progress("extras: further formats done")
 
     if want("cold"):

@@ -545,6 +545,8 @@ struct Nib32 {
     static constexpr int kUnitWeights = 32;
     static constexpr int kSumGroup = 32;
     static constexpr int kPadEvery = 32;
+    static constexpr int kHighOff = kHigh, kCodesOff = kCodes;
+    static constexpr bool kHasMin = kMin;
     struct Regs {
         uint4 q;
         uint32_t hdr;  // d (and m in the high half)
@@ -575,9 +577,10 @@ struct Nib32 {
     __device__ static __forceinline__ uint32_t fifth_bits(uint32_t t) {
         return (((t & 15u) * 0x00204081u) & 0x01010101u) << 4;
     }
-    __device__ static __forceinline__ void dot(const Regs &r, const float *xv, const float *sums,
-                                               int u, float &acc) {
-        const uint32_t qw[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
+    // One block: code dwords qw, header hdr (d, and m in the high half),
+    // fifth bits hb, its 32 activations xv and their sum.
+    __device__ static __forceinline__ void block(const uint32_t (&qw)[4], uint32_t hdr, uint32_t hb,
+                                                 const float *xv, float xsum, float &acc) {
         float lo0 = 0.f, lo1 = 0.f, hi0 = 0.f, hi1 = 0.f;
         if constexpr (!kHigh) {
             // four-bit codes: each dword masked in place (bytes 0 and 2) and
@@ -603,8 +606,8 @@ struct Nib32 {
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 // weights 4i .. 4i+3 and 16+4i .. 16+4i+3, with their fifth bits
-                const uint32_t a = (qw[i] & 0x0F0F0F0Fu) | fifth_bits(r.hb >> (4 * i));
-                const uint32_t b = ((qw[i] >> 4) & 0x0F0F0F0Fu) | fifth_bits(r.hb >> (16 + 4 * i));
+                const uint32_t a = (qw[i] & 0x0F0F0F0Fu) | fifth_bits(hb >> (4 * i));
+                const uint32_t b = ((qw[i] >> 4) & 0x0F0F0F0Fu) | fifth_bits(hb >> (16 + 4 * i));
                 const f16x2_t a01 = as_f16x2(bytes01_to_halves(a)), a23 = as_f16x2(bytes23_to_halves(a));
                 const f16x2_t b01 = as_f16x2(bytes01_to_halves(b)), b23 = as_f16x2(bytes23_to_halves(b));
                 lo0 = fmaf((float)a01.x, xv[4 * i + 0], lo0);
@@ -618,18 +621,83 @@ struct Nib32 {
             }
         }
         const float qx = ((lo0 + lo1) + (hi0 + hi1)) * kTwo24;  // sum q x, exact scaling
-        const float d = half_bits_to_float(r.hdr);
+        const float d = half_bits_to_float(hdr);
         if constexpr (kMin) {
-            acc = fmaf(d, qx, fmaf(half_bits_to_float(r.hdr >> 16), sums[u], acc));
+            acc = fmaf(d, qx, fmaf(half_bits_to_float(hdr >> 16), xsum, acc));
         } else {
-            acc = fmaf(d, fmaf(-(float)kOff, sums[u], qx), acc);
+            acc = fmaf(d, fmaf(-(float)kOff, xsum, qx), acc);
         }
+    }
+    __device__ static __forceinline__ void dot(const Regs &r, const float *xv, const float *sums,
+                                               int u, float &acc) {
+        const uint32_t qw[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
+        block(qw, r.hdr, r.hb, xv, sums[u], acc);
     }
 };
 using Q40 = Nib32<18, false, 0, 2, 8>;
 using Q41 = Nib32<20, true, 0, 4, 0>;
 using Q50 = Nib32<22, false, 2, 6, 16>;
 using Q51 = Nib32<24, true, 4, 8, 0>;
+
+// ---------------------------------------------------------------------------
+// Q4_0 and Q5_0, two blocks per unit (rows with an even number of blocks):
+// their 18- and 22-byte blocks leave one-block loads only 2-byte aligned,
+// while two blocks (36 and 44 bytes) start 4-byte aligned.  Block 1's
+// fields then sit on whole dwords; block 0's are the dwords funnel-shifted
+// by 16 bits.  Each block is computed exactly as in the one-block unit.
+// ---------------------------------------------------------------------------
+template <class B>
+struct Nib32x2 {
+    static constexpr int kBlockWeights = 32;
+    static constexpr int kBlockBytes = B::kBlockBytes;
+    static constexpr int kUnitWeights = 64;
+    static constexpr int kSumGroup = 32;
+    static constexpr int kPadEvery = 64;
+    static constexpr int kHigh = B::kHighOff, kCodes = B::kCodesOff;
+    static_assert(kBlockBytes % 4 == 2 && kCodes % 4 == 2 && (kHigh == 0 || kHigh % 4 == 2) && !B::kHasMin,
+                  "2-byte-aligned blocks without a min field");
+    struct Regs {
+        uint4 a, b, c;  // bytes 0 .. 48 of the unit (Q4_0 uses 36, Q5_0 44)
+    };
+    __device__ static __forceinline__ uint32_t unit_offset(int u) {
+        return (uint32_t)u * (2 * kBlockBytes);
+    }
+    __device__ static __forceinline__ Regs load(const BufSrc &src, uint32_t off, int) {
+        Regs r;
+        r.a = src.ld16(off);
+        r.b = src.ld16(off + 16);
+        if constexpr (2 * kBlockBytes > 36) {
+            r.c = src.ld16(off + 32);  // the last dword belongs to the next unit
+        } else {
+            r.c = make_uint4(src.ld4(off + 32), 0u, 0u, 0u);
+        }
+        return r;
+    }
+    __device__ static __forceinline__ void load_x(const float *xs, int u, float *xv) {
+        Q4K::load_x(xs, u, xv);
+    }
+    __device__ static __forceinline__ void dot(const Regs &r, const float *xv, const float *sums,
+                                               int u, float &acc) {
+        const uint32_t D[12] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y,
+                                r.b.z, r.b.w, r.c.x, r.c.y, r.c.z, r.c.w};
+        // block 0: fields at bytes 0 (d), kHigh, kCodes
+        constexpr int c0 = kCodes / 4;  // codes start 2 bytes into D[c0]
+        const uint32_t q0[4] = {__builtin_amdgcn_alignbit(D[c0 + 1], D[c0], 16),
+                                __builtin_amdgcn_alignbit(D[c0 + 2], D[c0 + 1], 16),
+                                __builtin_amdgcn_alignbit(D[c0 + 3], D[c0 + 2], 16),
+                                __builtin_amdgcn_alignbit(D[c0 + 4], D[c0 + 3], 16)};
+        const uint32_t hb0 = kHigh ? __builtin_amdgcn_alignbit(D[kHigh / 4 + 1], D[kHigh / 4], 16) : 0u;
+        B::block(q0, D[0], hb0, xv, sums[2 * u], acc);
+        // block 1: fields at kBlockBytes (d, the high half of a dword) and
+        // kBlockBytes + kHigh / kCodes (whole dwords)
+        constexpr int c1 = (kBlockBytes + kCodes) / 4;
+        const uint32_t q1[4] = {D[c1], D[c1 + 1], D[c1 + 2], D[c1 + 3]};
+        const uint32_t hb1 = kHigh ? D[(kBlockBytes + kHigh) / 4] : 0u;
+        B::block(q1, D[kBlockBytes / 4] >> 16, hb1, xv + 32, sums[2 * u + 1], acc);
+    }
+};
+using Q40x2 = Nib32x2<Q40>;
+using Q50x2 = Nib32x2<Q50>;
 
 // ---------------------------------------------------------------------------
 // Q8_1 as weights: Q8_0 plus an fp16 field s (the scaled code sum, meant for

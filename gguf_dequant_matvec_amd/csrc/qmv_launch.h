@@ -68,17 +68,23 @@ hipError_t launch_fmt(int type, const RowsParams &p, hipStream_t s, int *grid_ou
     case kQ4K: return launch_typed<Q4K, MODE>(p, s, grid_out);
     case kQ5K: return launch_typed<Q5K, MODE>(p, s, grid_out);
     case kQ6K: return launch_typed<Q6K, MODE>(p, s, grid_out);
-    case kQ40: case kQ41: case kQ50: case kQ51: case kQ81:
+    case kQ40: case kQ41: case kQ50: case kQ51: case kQ81: {
         // one 32-weight block per unit; in the MoE down launch the units per
         // expert (I / 32) must be a multiple of the narrowest lane group (4)
         if (MODE == kModeMoeDown && (p.moe.I / 32) % 4 != 0) return hipErrorInvalidValue;
+        // Q4_0 and Q5_0 take two blocks per unit (4-byte aligned) when a
+        // row, or in the MoE down launch an expert, holds an even number of
+        // blocks (there: a multiple of four two-block units)
+        const bool pair = MODE == kModeMoeDown ? p.moe.I % 64 == 0 && (p.moe.I / 64) % 4 == 0
+                                               : (p.K / 32) % 2 == 0;
         switch (type) {
-        case kQ40: return launch_typed<Q40, MODE>(p, s, grid_out);
+        case kQ40: return pair ? launch_typed<Q40x2, MODE>(p, s, grid_out) : launch_typed<Q40, MODE>(p, s, grid_out);
         case kQ41: return launch_typed<Q41, MODE>(p, s, grid_out);
-        case kQ50: return launch_typed<Q50, MODE>(p, s, grid_out);
+        case kQ50: return pair ? launch_typed<Q50x2, MODE>(p, s, grid_out) : launch_typed<Q50, MODE>(p, s, grid_out);
         case kQ51: return launch_typed<Q51, MODE>(p, s, grid_out);
         default: return launch_typed<Q81x1, MODE>(p, s, grid_out);
         }
+    }
     case kQ80:
         if (MODE == kModeMoeDown) {
             // unit steps must not straddle experts: the units per expert must
