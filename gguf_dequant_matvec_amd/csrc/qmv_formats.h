@@ -656,20 +656,24 @@ struct Nib32x2 {
     static constexpr int kHigh = B::kHighOff, kCodes = B::kCodesOff;
     static_assert(kBlockBytes % 4 == 2 && kCodes % 4 == 2 && (kHigh == 0 || kHigh % 4 == 2) && !B::kHasMin,
                   "2-byte-aligned blocks without a min field");
+    static_assert(2 * kBlockBytes == 36 || 2 * kBlockBytes == 44, "Q4_0 or Q5_0");
     struct Regs {
-        uint4 a, b, c;  // bytes 0 .. 48 of the unit (Q4_0 uses 36, Q5_0 44)
+        uint4 a, b;  // unit dwords 0 .. 7
+        uint4 c;     // dwords 7 .. 10 (Q5_0), or dword 8 in .y (Q4_0)
     };
     __device__ static __forceinline__ uint32_t unit_offset(int u) {
         return (uint32_t)u * (2 * kBlockBytes);
     }
+    // Every load stays inside the unit: Q5_0's last 16 bytes start at byte
+    // 28, overlapping the second load by one dword.
     __device__ static __forceinline__ Regs load(const BufSrc &src, uint32_t off, int) {
         Regs r;
         r.a = src.ld16(off);
         r.b = src.ld16(off + 16);
-        if constexpr (2 * kBlockBytes > 36) {
-            r.c = src.ld16(off + 32);  // the last dword belongs to the next unit
+        if constexpr (2 * kBlockBytes == 44) {
+            r.c = src.ld16(off + 28);
         } else {
-            r.c = make_uint4(src.ld4(off + 32), 0u, 0u, 0u);
+            r.c = make_uint4(0u, src.ld4(off + 32), 0u, 0u);
         }
         return r;
     }
@@ -678,8 +682,8 @@ struct Nib32x2 {
     }
     __device__ static __forceinline__ void dot(const Regs &r, const float *xv, const float *sums,
                                                int u, float &acc) {
-        const uint32_t D[12] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y,
-                                r.b.z, r.b.w, r.c.x, r.c.y, r.c.z, r.c.w};
+        const uint32_t D[11] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y,
+                                r.b.z, r.b.w, r.c.y, r.c.z, r.c.w};
         // block 0: fields at bytes 0 (d), kHigh, kCodes
         constexpr int c0 = kCodes / 4;  // codes start 2 bytes into D[c0]
         const uint32_t q0[4] = {__builtin_amdgcn_alignbit(D[c0 + 1], D[c0], 16),
