@@ -173,9 +173,13 @@ class DecodeStep:
         return out
 
 
-def graph_time_us(torch, fn_list, reps=10):
+def graph_time_us(torch, fn_list, reps=10, min_calls=1):
     """Per-call average (us) of a list of library calls captured once as a HIP
-    graph and replayed `reps` times (warm-up replays first)."""
+    graph and replayed `reps` times (warm-up replays first).  The list is
+    repeated until the graph holds at least `min_calls` calls, so that the
+    cost of launching the graph itself is spread over many calls, as in a
+    decode step's graph."""
+    fn_list = list(fn_list) * max(1, -(-min_calls // len(fn_list)))
     stream = torch.cuda.current_stream()
     side = torch.cuda.Stream()
     side.wait_stream(stream)
@@ -452,7 +456,7 @@ def extras(torch, q, synth, step, progress, probe_gbs=None, only=None):
                 n = max(2, GiB // b.numel() + 1)
                 reps = replicas(b, n)
                 us = graph_time_us(torch, [lambda r=r, t=t: q.qmv(t, r, M, K, xk, yk) for r in reps],
-                                   reps=5 if M < 100000 else 3)
+                                   reps=5 if M < 100000 else 3, min_calls=32)
                 out[f"{t}_{M}x{K}_cold"] = rec(us, b.numel() + 4 * K + 4 * M, replicas=n)
                 del reps, b, bv
             del yk
@@ -463,14 +467,18 @@ def extras(torch, q, synth, step, progress, probe_gbs=None, only=None):
         # supplementary cold Q8_0 stream at the decode-step scale
         V = step.vocab
         yv = torch.empty(V, device=dev)
-        us = graph_time_us(torch, [lambda: q.qmv_q6_k(step.out, V, Hs, step.x_h, yv)], reps=10)
-        out["q6_k_128000x4096_logits"] = rec(us, step.out.numel() + 4 * Hs + 4 * V)
+        outs = [step.out, step.out.clone()]   # two copies, 861 MB: beyond the 256 MB MALL
+        us = graph_time_us(torch, [lambda r=r: q.qmv_q6_k(r, V, Hs, step.x_h, yv) for r in outs],
+                           reps=3, min_calls=32)
+        del outs
+        out["q6_k_128000x4096_logits"] = rec(us, step.out.numel() + 4 * Hs + 4 * V, replicas=2)
         M, K = 28672, 4096
         b = make("q8_0", M, K, synth.T_W, 6)
         n = GiB // b.numel() + 1
         reps = replicas(b, n)
         y = torch.empty(M, device=dev)
-        us = graph_time_us(torch, [lambda r=r: q.qmv_q8_0(r, M, K, step.x_h, y) for r in reps], reps=5)
+        us = graph_time_us(torch, [lambda r=r: q.qmv_q8_0(r, M, K, step.x_h, y) for r in reps], reps=5,
+                           min_calls=32)
         out["q8_0_28672x4096_cold"] = rec(us, b.numel() + 4 * K + 4 * M, replicas=n)
         del reps, b
         # vocabulary-sized Q8_0 and Q4_K matrices (557 and 295 MB): the per-launch
@@ -482,7 +490,7 @@ def extras(torch, q, synth, step, progress, probe_gbs=None, only=None):
             n = max(2, GiB // b.numel() + 1)
             reps = replicas(b, n)
             us = graph_time_us(torch, [lambda r=r, t=t: q.qmv(t, r, M, K, step.x_h, y) for r in reps],
-                               reps=3)
+                               reps=3, min_calls=32)
             out[f"{t}_{M}x{K}_cold"] = rec(us, b.numel() + 4 * K + 4 * M, replicas=n)
             del reps, b
         progress("extras: cold streams done")

@@ -51,6 +51,7 @@
 namespace qmv {
 
 constexpr int kMaxSegments = 8;
+constexpr int kXcds = 8;  // XCDs of an MI355X, each with its own L2
 constexpr int kMaxExperts = 64;
 
 // Row counts are below 2^31 (checked on the host), so every row and tile
@@ -104,6 +105,31 @@ __device__ __forceinline__ uint64_t argmax_key(float v, int32_t idx) {
 
 // Items whose weight loads a wave keeps in flight (register sets in its ring).
 constexpr int kPipeDepth = 2;
+
+// Formats whose row kernel streams faster with the next item requested only
+// once the current item's first load has returned (measured: Q8_0 in
+// two-block units, 128000 x 4096 96.3 against 99.2 us, 28672 x 4096 22.4
+// against 23.7 us).  wait_first makes the first-issued load's register an
+// operand of an empty asm, so the compiler waits for that load there.
+template <class F>
+struct Throttle {
+    static constexpr bool kOn = false;
+    __device__ static void wait_first(const typename F::Regs &) {}
+};
+template <>
+struct Throttle<Q80x2> {
+    static constexpr bool kOn = true;
+    __device__ static __forceinline__ void wait_first(const Q80x2::Regs &r) {
+        asm volatile("" ::"v"(r.a.x));
+    }
+};
+template <>
+struct Throttle<Q80x1> {
+    static constexpr bool kOn = true;
+    __device__ static __forceinline__ void wait_first(const Q80x1::Regs &r) {
+        asm volatile("" ::"v"(r.c));
+    }
+};
 
 // Floats of the padded LDS copy of x.
 template <class F>
@@ -430,26 +456,57 @@ __device__ __forceinline__ void rows_body(const RowsParams &p, const int bid, co
         t = __builtin_amdgcn_readfirstlane(t);
         it = __builtin_amdgcn_readfirstlane(it);
         const int u = g + G * it;
-        if (u < U) {
-            if constexpr (XR) {
+        // Lanes whose unit lies past the row's end compute on unit 0 (in
+        // bounds of x and its sums) and keep their old sum: a select, not a
+        // branch, so every path uses the set's registers and none leaves its
+        // loads pending across the loop's back edge (with such a path the
+        // compiler's waits before a refill also count the result stores
+        // issued in between, and the ring ran one item deep).
+        const bool valid = u < U;
+        const int uc = valid ? u : 0;
+        float part[R];
+        if constexpr (XR) {
 #pragma unroll
-                for (int r = 0; r < R; r++) F::dot(src[r], xr, sums, u, acc[r]);
-            } else {
-                float xv[F::kUnitWeights];
-                F::load_x(xs, u, xv);
-                // u indexes the (concatenated) x and its sums; the block-internal
-                // position only depends on u mod 4, the same inside each expert
+            for (int r = 0; r < R; r++) {
+                part[r] = acc[r];
+                F::dot(src[r], xr, sums, uc, part[r]);
+            }
+        } else {
+            float xv[F::kUnitWeights];
+            F::load_x(xs, uc, xv);
+            // u indexes the (concatenated) x and its sums; the block-internal
+            // position only depends on u mod 4, the same inside each expert
 #pragma unroll
-                for (int r = 0; r < R; r++) F::dot(src[r], xv, sums, u, acc[r]);
+            for (int r = 0; r < R; r++) {
+                part[r] = acc[r];
+                F::dot(src[r], xv, sums, uc, part[r]);
             }
         }
+#pragma unroll
+        for (int r = 0; r < R; r++) acc[r] = valid ? part[r] : acc[r];
         if (it + KS >= iters) finish_tile(t);  // this wave's last step of the tile
     };
 
     // Items of this wave: tiles t_first, t_first + stride, ..., each with
-    // `iters` unit steps.
-    const int t_first = __builtin_amdgcn_readfirstlane(
-        KS == 1 ? bid * waves_per_block + wave : bid);
+    // `iters` unit steps.  A round of tiles gives each wave one.  With many
+    // rounds (long matrices) the wave's place in a round is chosen so that
+    // the tiles covering one 128-byte line of y (kLineTiles consecutive
+    // tiles) go to waves of one XCD (workgroup b runs on XCD b % 8): each
+    // XCD then reads runs of consecutive rows and completes its lines of y
+    // in its own L2, while the lines of a round still spread over all XCDs.
+    // Measured (MI355X, cold): Q8_0 128000 x 4096 94.4 -> 90.7 us, 28672 x
+    // 4096 22.5 -> 22.0 us, Q6_K 128000 x 4096 75.7 -> 73.2 us; with a few
+    // rounds (the 4096 x 14336 and 28672 x 4096 Q4_K launches) it was
+    // slower, so it applies from eight rounds on.  Any order of the tiles
+    // gives the same results.
+    constexpr int kLineTiles = kRowsPerTile >= 32 ? 1 : 32 / kRowsPerTile;
+    int slot = KS == 1 ? bid * waves_per_block + wave : bid;
+    if (KS == 1 && MODE != kModeArgmax && nblk % kXcds == 0 &&
+        ntiles >= 8 * tile_stride && (nblk / kXcds * waves_per_block) % kLineTiles == 0) {
+        const int j = (bid / kXcds) * waves_per_block + wave;  // place among the XCD's waves
+        slot = ((j / kLineTiles) * kXcds + bid % kXcds) * kLineTiles + j % kLineTiles;
+    }
+    const int t_first = __builtin_amdgcn_readfirstlane(slot);
     const int my_tiles = t_first < ntiles ? (ntiles - 1 - t_first) / tile_stride + 1 : 0;
     const int steps = (iters - it0 + KS - 1) / KS;  // this wave's steps per tile
     const int n_items = my_tiles * steps;
@@ -541,19 +598,35 @@ __device__ __forceinline__ void rows_body(const RowsParams &p, const int bid, co
         ring_it[j] = it_last;
         issue(buf[j], t_last, it_last);
     }
-    if (n_items > 0) {
-        for (int k = 0; k < n_items; k += D) {
+    // Whole rounds of D items, each consume unconditional: no path around
+    // the loop's back edge skips a consume, so no register set's loads can
+    // still be pending when it is refilled.  (With a skippable consume the
+    // compiler has to assume they might be, and with a result store between
+    // the two sets' loads its wait before each refill then also waited for
+    // the newest set's first load: the ring ran one item deep in the modes
+    // that store.)
+    int k = 0;
+    for (; k + D <= n_items; k += D) {
 #pragma unroll
-            for (int j = 0; j < D; j++) {
-                const int jn = (j + D - 1) % D;  // the set consumed one step ago
-                next_item();
-                ring_t[jn] = t_last;
-                ring_it[jn] = it_last;
-                issue(buf[jn], t_last, it_last);
-                if (k + j < n_items) consume(buf[j], ring_t[j], ring_it[j]);
-            }
+        for (int j = 0; j < D; j++) {
+            const int jn = (j + D - 1) % D;  // the set consumed one step ago
+            next_item();
+            ring_t[jn] = t_last;
+            ring_it[jn] = it_last;
+            // formats whose loads stream better with fewer in flight request
+            // the next item only once the current one's first load is back
+            if constexpr (Throttle<F>::kOn) Throttle<F>::wait_first(buf[j][0]);
+            issue(buf[jn], t_last, it_last);
+            // keep the multiply below the refill: hoisted above it, its
+            // waits would hold the next loads back
+            __builtin_amdgcn_sched_barrier(0);
+            consume(buf[j], ring_t[j], ring_it[j]);
         }
     }
+    // the last n_items - k (< D) items are already in flight in sets 0..
+#pragma unroll
+    for (int j = 0; j < D - 1; j++)
+        if (k + j < n_items) consume(buf[j], ring_t[j], ring_it[j]);
 
     if (MODE == kModeArgmax) {
         __shared__ uint64_t wave_best[kMaxBlockThreads / kWave];

@@ -77,6 +77,22 @@ def test_qmv_parity(t, M, K):
     assert_rel(host(y), y_ref, a_ref, what=f"{t} {M}x{K}")
 
 
+# Long matrices: from eight rounds of tiles per wave on, a launch numbers its
+# workgroups XCD by XCD (a different tile order); every row is checked.
+# Shapes cover one and two row slots and lane groups of 4, 8 and 64.
+MANY_ROUNDS = [("q8_0", 20000, 4096), ("q4_k", 40000, 4096), ("q4_k", 600000, 256),
+               ("q6_k", 140000, 512)]
+
+
+@pytest.mark.parametrize("t,M,K", MANY_ROUNDS)
+def test_qmv_parity_many_rounds(t, M, K):
+    b, x = _case(t, M, K, 250)
+    y_ref, a_ref = oracle.qmv(t, b, M, K, x)
+    y = empty(M)
+    q.qmv(t, dev(b), M, K, dev(x), y)
+    assert_rel(host(y), y_ref, a_ref, what=f"{t} {M}x{K}")
+
+
 @pytest.mark.parametrize("t,M,K", [("q4_k", 40, 4096), ("q6_k", 40, 1536), ("q8_0", 40, 576),
                                    ("q8_0", 9, 224), ("q4_k", 33, 14336), ("q5_k", 40, 4096),
                                    ("q4_0", 40, 576), ("q4_1", 40, 576), ("q5_0", 40, 576),
@@ -134,6 +150,10 @@ def test_x_extremes():
     ("q2_k", (300, 5), 4096),
     # the stack takes two row slots per lane, each segment alone one
     ("q4_k", (4096, 4096), 4096),
+    # long stacks (eight or more rounds of tiles: workgroups numbered XCD by
+    # XCD) against segments that stay below that
+    ("q4_k", (20000, 13001, 7000), 4096),
+    ("q8_0", (9000, 8000, 3001), 4096),
 ])
 def test_fused_rows(t, segs, K):
     M = sum(segs)

@@ -72,6 +72,7 @@ SHAPES = [
     ("q5_1", 45, 224),
     ("q3_k", 150, 2048),
     ("q2_k", 64, 4096),
+    ("q4_k", 17000, 4096),  # eight or more rounds of tiles (workgroups numbered XCD by XCD)
 ]
 
 
