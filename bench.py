@@ -173,12 +173,14 @@ class DecodeStep:
         return out
 
 
-def graph_time_us(torch, fn_list, reps=10, min_calls=1):
+def graph_time_us(torch, fn_list, reps=10, min_calls=1, warm_ms=0.0):
     """Per-call average (us) of a list of library calls captured once as a HIP
     graph and replayed `reps` times (warm-up replays first).  The list is
     repeated until the graph holds at least `min_calls` calls, so that the
     cost of launching the graph itself is spread over many calls, as in a
-    decode step's graph."""
+    decode step's graph.  With `warm_ms`, the warm-up replays run for about
+    that much GPU time (long HBM streams right after host-side set-up ran up
+    to 10% slower for the first few ms, while the clocks settle)."""
     fn_list = list(fn_list) * max(1, -(-min_calls // len(fn_list)))
     stream = torch.cuda.current_stream()
     side = torch.cuda.Stream()
@@ -192,10 +194,15 @@ def graph_time_us(torch, fn_list, reps=10, min_calls=1):
     with torch.cuda.graph(g):
         for fn in fn_list:
             fn()
-    for _ in range(2):
+    a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    g.replay()
+    z.record(stream)
+    torch.cuda.synchronize()
+    n_warm = int(warm_ms / max(a.elapsed_time(z), 1e-3)) if warm_ms > 0 else 1
+    for _ in range(max(1, min(200, n_warm))):
         g.replay()
     torch.cuda.synchronize()
-    a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record(stream)
     for _ in range(reps):
         g.replay()
@@ -456,7 +463,8 @@ def extras(torch, q, synth, step, progress, probe_gbs=None, only=None):
                 n = max(2, GiB // b.numel() + 1)
                 reps = replicas(b, n)
                 us = graph_time_us(torch, [lambda r=r, t=t: q.qmv(t, r, M, K, xk, yk) for r in reps],
-                                   reps=5 if M < 100000 else 3, min_calls=32)
+                                   reps=5 if M < 100000 else 3, min_calls=32,
+                                   warm_ms=30.0 if M >= 100000 else 0.0)
                 out[f"{t}_{M}x{K}_cold"] = rec(us, b.numel() + 4 * K + 4 * M, replicas=n)
                 del reps, b, bv
             del yk
@@ -469,7 +477,7 @@ def extras(torch, q, synth, step, progress, probe_gbs=None, only=None):
         yv = torch.empty(V, device=dev)
         outs = [step.out, step.out.clone()]   # two copies, 861 MB: beyond the 256 MB MALL
         us = graph_time_us(torch, [lambda r=r: q.qmv_q6_k(r, V, Hs, step.x_h, yv) for r in outs],
-                           reps=3, min_calls=32)
+                           reps=3, min_calls=32, warm_ms=30.0)
         del outs
         out["q6_k_128000x4096_logits"] = rec(us, step.out.numel() + 4 * Hs + 4 * V, replicas=2)
         M, K = 28672, 4096
@@ -478,7 +486,7 @@ def extras(torch, q, synth, step, progress, probe_gbs=None, only=None):
         reps = replicas(b, n)
         y = torch.empty(M, device=dev)
         us = graph_time_us(torch, [lambda r=r: q.qmv_q8_0(r, M, K, step.x_h, y) for r in reps], reps=5,
-                           min_calls=32)
+                           min_calls=32, warm_ms=30.0)
         out["q8_0_28672x4096_cold"] = rec(us, b.numel() + 4 * K + 4 * M, replicas=n)
         del reps, b
         # vocabulary-sized Q8_0 and Q4_K matrices (557 and 295 MB): the per-launch
@@ -490,7 +498,7 @@ def extras(torch, q, synth, step, progress, probe_gbs=None, only=None):
             n = max(2, GiB // b.numel() + 1)
             reps = replicas(b, n)
             us = graph_time_us(torch, [lambda r=r, t=t: q.qmv(t, r, M, K, step.x_h, y) for r in reps],
-                               reps=3, min_calls=32)
+                               reps=3, min_calls=32, warm_ms=30.0)
             out[f"{t}_{M}x{K}_cold"] = rec(us, b.numel() + 4 * K + 4 * M, replicas=n)
             del reps, b
         progress("extras: cold streams done")
