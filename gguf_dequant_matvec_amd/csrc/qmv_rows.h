@@ -210,7 +210,12 @@ __device__ __forceinline__ void stage_x(const float *__restrict__ x, int K, floa
 }
 
 __device__ __forceinline__ float sigmoidf(float v) { return 1.0f / (1.0f + expf(-v)); }
-__device__ __forceinline__ float siluf(float v) { return v / (1.0f + expf(-v)); }
+// silu(v) = v / (1 + e^-v), with the quotient as v times the hardware
+// reciprocal (1 ulp) instead of the IEEE division sequence: a dozen fewer
+// VALU instructions per row, which the gated launches pay once per tile.
+__device__ __forceinline__ float siluf(float v) {
+    return v * __builtin_amdgcn_rcpf(1.0f + expf(-v));
+}
 
 // MoE selection from the router logits, done by every wave (each writes the
 // same values into the workgroup's LDS slots, so it can use them without a
