@@ -16,6 +16,17 @@ constexpr int kMaxBlocksPerCU = 2;  // persistent workgroups per compute unit
 // G lanes; pick the G (a power of two, >= 4) that maximises it, preferring
 // wider groups on ties (fewer rows per wave, better coalescing).
 inline int pick_group(int U) {
+    // Rows of 9-32 units take one step of 16 or 32 lanes (a wave's item
+    // chain is then one item per tile and x stays in registers), even
+    // though up to 44% of the lanes idle: matrices of such short rows are
+    // small and latency-bound.  Measured (MI355X, cold, us): Q8_0 1536x576
+    // 4.10 -> 3.02 (groups of 4, three steps, before), Q4_K 8192x768 4.10 ->
+    // 3.56, Q4_K 1536x1536 4.0 -> 3.17 and 8960x1536 5.28 -> 5.13, Q6_K
+    // 8960x1536 6.53 -> 5.80, Q8_0 8960x1536 6.2 -> 5.61, and 32768x576 no
+    // slower (7.0 -> 6.8).  Longer rows keep the rule below: with 40 units
+    // one 64-lane step made 20000x2560 slower (9.5 -> 10.1) though 2048x2560
+    // faster (5.18 -> 3.82).
+    if (U > 8 && U <= 32) return U <= 16 ? 16 : 32;
     int best = 64;
     double best_eff = -1.0;
     for (int G = 64; G >= 4; G >>= 1) {
