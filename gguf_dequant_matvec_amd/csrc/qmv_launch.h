@@ -65,6 +65,17 @@ constexpr bool prefers_one_slot() {
     return std::is_same<F, Q6K>::value || std::is_same<F, Q80x2>::value;
 }
 
+// Formats whose plain launches with long rows keep two 4-wave workgroups per
+// compute unit instead of one 8-wave one (measured for Q6_K, us: 14336 x
+// 14336 36.8 -> 32.8, 4096 x 8192 8.79 -> 8.42, 2048 x 8192 6.65 -> 6.19,
+// 4096 x 14336 13.0 either way; Q4_K was slower with two: 2048 x 8192 5.06
+// -> 5.39, 4096 x 8192 7.1 -> 7.4; Q8_0 mixed: 14336 x 14336 39.1 -> 38.3,
+// 4096 x 14336 13.4 -> 13.8).
+template <class F>
+constexpr bool keeps_two_workgroups() {
+    return std::is_same<F, Q6K>::value;
+}
+
 // The launcher of the row kernel for one (format, mode).  Its definition
 // lives in qmv_launch_impl.h and is instantiated once per (format, mode) in
 // qmv_rows_inst.hip, so the kernels compile in parallel units.

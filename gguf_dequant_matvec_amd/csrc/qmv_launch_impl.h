@@ -32,8 +32,9 @@ hipError_t launch_typed(const RowsParams &p_in, hipStream_t s, int *grid_out) {
     // ones, so each compute unit stages x once, not twice (4096 x 14336
     // Q4_K: 11.4 -> 9.9 us).  Shorter rows keep two 4-wave workgroups
     // (gate+up 28672 x 4096 was slower with one 8-wave, and Q8_0 1536 x 576
-    // went from 4.2 to 5.7 us with half as many workgroups).
-    const bool wide = MODE == kModeStore && iters > 1 && p.K >= 8192;
+    // went from 4.2 to 5.7 us with half as many workgroups); so do the
+    // formats that keep two (keeps_two_workgroups).
+    const bool wide = MODE == kModeStore && iters > 1 && p.K >= 8192 && !keeps_two_workgroups<F>();
     const int bt = wide ? kWideBlockThreads : kBlockThreads;
     const int waves = bt / kWave;
     const int64_t total_waves =
