@@ -425,11 +425,14 @@ def extras(torch, q, synth, step, progress, probe_gbs=None, only=None):
         hg = torch.empty(Ig, device=dev)
         ygu = [torch.empty(m, device=dev) for m in step.gu_rows]
         per = {}
-        for name, fn in (("silu", lambda lay: q.qmv_gate_up_silu("q4_k", lay["gu"], Ig, Hs, step.x_h, hg)),
-                         ("fused", lambda lay: q.qmv_fused_rows("q4_k", lay["gu"], Hs, step.x_h,
-                                                                step.gu_rows, ygu))):
-            calls = [lambda lay=lay, fn=fn: fn(lay) for lay in step.layers]
-            per[name] = graph_time_us(torch, calls, reps=5)
+        # the two alternate twice, after a short warm-up each, so that neither
+        # always runs first (the clocks settle over the first few ms)
+        for _ in range(2):
+            for name, fn in (("silu", lambda lay: q.qmv_gate_up_silu("q4_k", lay["gu"], Ig, Hs, step.x_h, hg)),
+                             ("fused", lambda lay: q.qmv_fused_rows("q4_k", lay["gu"], Hs, step.x_h,
+                                                                    step.gu_rows, ygu))):
+                calls = [lambda lay=lay, fn=fn: fn(lay) for lay in step.layers]
+                per[name] = per.get(name, 0.0) + graph_time_us(torch, calls, reps=5, warm_ms=10.0) / 2
         gbytes = step.layers[0]["gu"].numel()
         r = rec(per["silu"], gbytes + 4 * Hs + 4 * Ig, per="call (32 stacks in turn)")
         r["fused_rows_same_stacks_us"] = round(per["fused"], 3)
