@@ -40,6 +40,10 @@ SHAPES = [
     # 2- and 3-bit K-quants
     ("q2_k", 1, 256), ("q2_k", 77, 2048), ("q2_k", 1000, 4096), ("q2_k", 97, 14336),
     ("q3_k", 1, 256), ("q3_k", 50, 768), ("q3_k", 1000, 4096), ("q3_k", 97, 14336),
+    # short rows of 9-32 units take one step of 16 or 32 lanes: the edges of
+    # that rule (10, 16, 17, 20 and 32 units; 36 falls back to the fewest-idle group)
+    ("q4_k", 300, 1024), ("q4_k", 300, 1280), ("q6_k", 129, 1280), ("q4_k", 77, 2304),
+    ("q4_0", 300, 640), ("q5_1", 129, 1024), ("q8_0", 300, 1088),
 ]
 
 
@@ -150,6 +154,8 @@ def test_x_extremes():
     ("q2_k", (300, 5), 4096),
     # the stack takes two row slots per lane, each segment alone one
     ("q4_k", (4096, 4096), 4096),
+    ("q4_k", (600, 300, 129), 1280),           # 20 units: one 32-lane step per row
+    ("q8_0", (1000, 536), 576),                # 9 units: one 16-lane step per row
     # long stacks (eight or more rounds of tiles: workgroups numbered XCD by
     # XCD) against segments that stay below that
     ("q4_k", (20000, 13001, 7000), 4096),
