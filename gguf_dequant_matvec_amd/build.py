@@ -27,7 +27,7 @@ ARCH = os.environ.get("QMV_OFFLOAD_ARCH", "gfx950")
 
 # row-kernel formats (format structs of qmv_formats.h) and modes (qmv_rows.h)
 ROW_FORMATS = ["Q2K", "Q3K", "Q4K", "Q5K", "Q6K", "Q40", "Q41", "Q50", "Q51", "Q81x1",
-               "Q80x1", "Q80x2", "Q40x2", "Q50x2"]
+               "Q80x1", "Q80x2", "Q40x2", "Q50x2", "Q41x2", "Q51x2"]
 ROW_MODES = ["kModeStore", "kModeArgmax", "kModeMoeGateUp", "kModeMoeDown", "kModeSiluUp",
              "kModeShortConv"]
 INST_SRC = "qmv_rows_inst.hip"

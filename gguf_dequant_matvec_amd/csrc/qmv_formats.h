@@ -704,6 +704,66 @@ using Q40x2 = Nib32x2<Q40>;
 using Q50x2 = Nib32x2<Q50>;
 
 // ---------------------------------------------------------------------------
+// Q4_1 and Q5_1, two blocks per unit (rows with an even number of blocks):
+// their 20- and 24-byte blocks are 4-byte aligned, so every field of both
+// blocks sits on whole dwords (d and m in one dword, then Q5_1's fifth bits,
+// then the 16 code bytes).  With 64 weights per unit a 4096-weight row is one
+// unit step of 64 lanes, which keeps x in registers.  Each block is computed
+// exactly as in the one-block unit.
+// ---------------------------------------------------------------------------
+template <class B>
+struct Nib32x2m {
+    static constexpr int kBlockWeights = 32;
+    static constexpr int kBlockBytes = B::kBlockBytes;
+    static constexpr int kUnitWeights = 64;
+    static constexpr int kSumGroup = 32;
+    static constexpr int kPadEvery = 64;
+    static constexpr int kHigh = B::kHighOff, kCodes = B::kCodesOff;
+    static_assert(kBlockBytes % 4 == 0 && kCodes % 4 == 0 && kHigh % 4 == 0 && B::kHasMin,
+                  "4-byte-aligned blocks with a min field");
+    static_assert(2 * kBlockBytes == 40 || 2 * kBlockBytes == 48, "Q4_1 or Q5_1");
+    struct Regs {
+        uint4 a, b, c;  // unit dwords 0 .. 11 (Q5_1); Q4_1: c holds dwords 6 .. 9
+    };
+    __device__ static __forceinline__ uint32_t unit_offset(int u) {
+        return (uint32_t)u * (2 * kBlockBytes);
+    }
+    // Every load stays inside the unit: Q4_1's last 16 bytes start at byte
+    // 24, overlapping the second load by two dwords.
+    __device__ static __forceinline__ Regs load(const BufSrc &src, uint32_t off, int) {
+        Regs r;
+        r.a = src.ld16(off);
+        r.b = src.ld16(off + 16);
+        r.c = src.ld16(off + (2 * kBlockBytes == 48 ? 32 : 24));
+        return r;
+    }
+    __device__ static __forceinline__ void load_x(const float *xs, int u, float *xv) {
+        Q4K::load_x(xs, u, xv);
+    }
+    __device__ static __forceinline__ void dot(const Regs &r, const float *xv, const float *sums,
+                                               int u, float &acc) {
+        // D[i] is dword i of the unit
+        uint32_t D[12];
+        D[0] = r.a.x; D[1] = r.a.y; D[2] = r.a.z; D[3] = r.a.w;
+        D[4] = r.b.x; D[5] = r.b.y; D[6] = r.b.z; D[7] = r.b.w;
+        if constexpr (2 * kBlockBytes == 48) {
+            D[8] = r.c.x; D[9] = r.c.y; D[10] = r.c.z; D[11] = r.c.w;
+        } else {
+            D[8] = r.c.z; D[9] = r.c.w; D[10] = 0u; D[11] = 0u;
+        }
+        constexpr int c0 = kCodes / 4, c1 = (kBlockBytes + kCodes) / 4;
+        const uint32_t q0[4] = {D[c0], D[c0 + 1], D[c0 + 2], D[c0 + 3]};
+        const uint32_t q1[4] = {D[c1], D[c1 + 1], D[c1 + 2], D[c1 + 3]};
+        const uint32_t hb0 = kHigh ? D[kHigh / 4] : 0u;
+        const uint32_t hb1 = kHigh ? D[(kBlockBytes + kHigh) / 4] : 0u;
+        B::block(q0, D[0], hb0, xv, sums[2 * u], acc);
+        B::block(q1, D[kBlockBytes / 4], hb1, xv + 32, sums[2 * u + 1], acc);
+    }
+};
+using Q41x2 = Nib32x2m<Q41>;
+using Q51x2 = Nib32x2m<Q51>;
+
+// ---------------------------------------------------------------------------
 // Q8_1 as weights: Q8_0 plus an fp16 field s (the scaled code sum, meant for
 // activations, not used here); one 36-byte block per unit.
 // ---------------------------------------------------------------------------

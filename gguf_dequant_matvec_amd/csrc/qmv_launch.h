@@ -94,16 +94,16 @@ hipError_t launch_fmt(int type, const RowsParams &p, hipStream_t s, int *grid_ou
         // one 32-weight block per unit; in the MoE down launch the units per
         // expert (I / 32) must be a multiple of the narrowest lane group (4)
         if (MODE == kModeMoeDown && (p.moe.I / 32) % 4 != 0) return hipErrorInvalidValue;
-        // Q4_0 and Q5_0 take two blocks per unit (4-byte aligned) when a
-        // row, or in the MoE down launch an expert, holds an even number of
-        // blocks (there: a multiple of four two-block units)
+        // Q4_0, Q5_0, Q4_1 and Q5_1 take two blocks per unit when a row, or
+        // in the MoE down launch an expert, holds an even number of blocks
+        // (there: a multiple of four two-block units)
         const bool pair = MODE == kModeMoeDown ? p.moe.I % 64 == 0 && (p.moe.I / 64) % 4 == 0
                                                : (p.K / 32) % 2 == 0;
         switch (type) {
         case kQ40: return pair ? launch_typed<Q40x2, MODE>(p, s, grid_out) : launch_typed<Q40, MODE>(p, s, grid_out);
-        case kQ41: return launch_typed<Q41, MODE>(p, s, grid_out);
+        case kQ41: return pair ? launch_typed<Q41x2, MODE>(p, s, grid_out) : launch_typed<Q41, MODE>(p, s, grid_out);
         case kQ50: return pair ? launch_typed<Q50x2, MODE>(p, s, grid_out) : launch_typed<Q50, MODE>(p, s, grid_out);
-        case kQ51: return launch_typed<Q51, MODE>(p, s, grid_out);
+        case kQ51: return pair ? launch_typed<Q51x2, MODE>(p, s, grid_out) : launch_typed<Q51, MODE>(p, s, grid_out);
         default: return launch_typed<Q81x1, MODE>(p, s, grid_out);
         }
     }

@@ -44,6 +44,10 @@ SHAPES = [
     # that rule (10, 16, 17, 20 and 32 units; 36 falls back to the fewest-idle group)
     ("q4_k", 300, 1024), ("q4_k", 300, 1280), ("q6_k", 129, 1280), ("q4_k", 77, 2304),
     ("q4_0", 300, 640), ("q5_1", 129, 1024), ("q8_0", 300, 1088),
+    # Q4_1 and Q5_1 in two-block units: one 64-lane step (x in registers),
+    # several steps, and an odd block count (one-block units)
+    ("q4_1", 300, 4096), ("q5_1", 300, 4096), ("q4_1", 97, 14336), ("q5_1", 97, 14336),
+    ("q4_1", 50, 4064),
 ]
 
 
@@ -150,6 +154,8 @@ def test_x_extremes():
     ("q5_k", (512, 128, 128), 2048),
     ("q4_0", (64, 16, 16), 4096),
     ("q5_1", (33, 7), 224),
+    ("q4_1", (300, 77), 4096),                 # two-block units
+    ("q5_1", (129, 64, 3), 2048),
     ("q3_k", (512, 128, 128), 2048),
     ("q2_k", (300, 5), 4096),
     # the stack takes two row slots per lane, each segment alone one

@@ -169,6 +169,8 @@ def test_moe_k1_and_tie_to_lower_expert():
     (8, 512, 256, 4, "q5_k", "q4_0"),     # further formats: Q5_K gate/up, Q4_0 down
     (6, 256, 128, 2, "q5_0", "q5_1"),
     (4, 256, 256, 2, "q4_1", "q8_1"),
+    (4, 512, 256, 2, "q5_1", "q4_1"),     # Q4_1 down in two-block units (I = 4 units of 64)
+    (4, 256, 512, 2, "q4_1", "q5_1"),     # Q5_1 down in two-block units
     (8, 512, 256, 4, "q3_k", "q2_k"),     # 3- and 2-bit K-quants
 ])
 def test_moe_small_shapes(E, H, I, k, gu_t, dn_t):
